@@ -1,0 +1,81 @@
+"""Pins of the oracle's scale and quantise steps: exact rational arithmetic
+for the float32 quotient, exact round trips, and the pages' size claim."""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+from oracle import e4m3, quant
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_kv_capacity.json")
+
+
+def _round_f32(fr: Fraction) -> np.float32:
+    """Correctly rounded (ties-to-even) float32 of an exact rational, for
+    normal-range values: pick between the two float32 neighbours."""
+    f = np.float32(float(fr))  # within an ulp
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    best = None
+    for c in cands:
+        d = abs(Fraction(float(c)) - fr)
+        if best is None or d < best[0] or (d == best[0] and (int(c.view(np.uint32)) & 1) == 0):
+            best = (d, c)
+    return best[1]
+
+
+def test_scale_from_amax_exact_cases():
+    assert quant.scale_from_amax(448.0) == np.float32(1.0)
+    assert quant.scale_from_amax(896.0) == np.float32(2.0)
+    assert quant.scale_from_amax(0.0) == np.float32(1.0)
+    assert quant.scale_from_amax(4.90625) == _round_f32(Fraction(4.90625) / 448)
+    for a in [1.0, 3.0, 80.5, 1e-3, 7.25]:
+        assert quant.scale_from_amax(a) == _round_f32(Fraction(a) / 448)
+
+
+def test_quotient_is_correctly_rounded_float32_division():
+    rng = np.random.default_rng(3)
+    bits = (rng.integers(0, 65536, size=3000, dtype=np.uint32) << 16)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) > 1e-30) & (np.abs(x) < 1e30)]
+    for s in [np.float32(4.90625 / 448), np.float32(3.0), np.float32(1.0 / 3.0)]:
+        q = quant.quotient(x, s)
+        for xi, qi in zip(x[:1500], q[:1500]):
+            assert qi == _round_f32(Fraction(float(xi)) / Fraction(float(s)))
+
+
+def test_quantize_dequantize_round_trip_on_grid():
+    """fl32(code value * s) lies within a float32 ulp of a grid point, far
+    inside half a code step, so it quantises back to the same code."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    for s in [np.float32(5.0 / 448), np.float32(1.0), np.float32(0.37)]:
+        x = (e4m3.DECODE[codes] * np.float64(s)).astype(np.float32)
+        assert np.array_equal(quant.quantize(x, s), codes)
+
+
+def test_quantization_error_bound():
+    """Within range, |dequant(quant(x)) - x| <= half a code step times s."""
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(100_000).astype(np.float32)
+    s = quant.scale_from_amax(float(np.abs(x).max()))
+    c = quant.quantize(x, s)
+    xr = quant.dequantize(c, s)
+    a = np.abs(x.astype(np.float64)) / np.float64(s)
+    ex = np.floor(np.log2(np.maximum(a, 2.0**-6)))
+    ulp = 2.0 ** (ex - 3)
+    assert np.all(np.abs(xr - x) <= 0.5 * ulp * np.float64(s) * (1 + 1e-12))
+
+
+def test_fp8_pool_is_half_the_bf16_pool():
+    """'halves its size' / 'twice as much' context at equal memory."""
+    g = json.load(open(GOLDEN))
+    per_token = lambda e: 2 * 8 * 128 * e  # K and V, 8 kv heads, head dim 128
+    b16 = per_token(g["bytes_per_element"]["bf16"])
+    f8 = per_token(g["bytes_per_element"]["fp8_e4m3"])
+    assert b16 == 2 * f8
+    budget = 686_000 * b16
+    tokens_fp8 = budget // f8
+    assert tokens_fp8 == 2 * 686_000
+    # the pages' own rounded figures agree with an exact doubling to 0.2%
+    r = g["tokens_held"]["fp8_e4m3"] / g["tokens_held"]["bf16"]
+    assert abs(r - g["stated_ratio"]) < 0.005

@@ -1,0 +1,10 @@
+"""Seeded synthetic inputs shared by the tests, the oracle checks and the bench.
+
+Holds no attention or quantisation arithmetic: only draws of lengths, page
+placements, tags, reallocations and bf16 K/V/Q values.
+"""
+from .configs import (SWEEP_BATCHES, Workload, custom, gqa, in_use_pages, integrity_cost,
+                      long_context, mla, sweep, tiny)
+
+__all__ = ["SWEEP_BATCHES", "Workload", "custom", "gqa", "in_use_pages", "integrity_cost",
+           "long_context", "mla", "sweep", "tiny"]
