@@ -1,0 +1,248 @@
+"""Throughput of the FP8 paged decode step on one MI355X.
+
+A step is one pass of the whole hot path over a batch of decode requests,
+issued on torch's current stream:
+    pkv_verify -> pkv_append (one new token per request) -> pkv_decode_attn
+    -> pkv_combine
+Default workload: the concurrency-sweep point at batch 64 (contexts uniform
+on [2048, 32768], 64 query / 8 KV heads, head dim 128, page 16, per-head
+e4m3 scales, tag check on). Inputs are built on the GPU before timing.
+
+Printed: one JSON line. ``value`` is KV GB/s of the step (e4m3 cache bytes
+read by the step / step time); also sequence-steps/s, the BF16-cache step for
+comparison, the decode kernel's roofline (its algorithmic bytes over its
+average duration, timed with events on the launching stream) and the oracle
+on the host as a CPU baseline.
+
+    python bench.py [--steps K] [--warmup W] [--batch B] [--no-bf16]
+                    [--no-cpu-baseline] [--sweep] [--integrity]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--batch", type=int, default=64)
+    ap.add_argument("--split", type=int, default=0, help="split tokens (0 = library's suggestion)")
+    ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="also time batch 1/8/16/32")
+    ap.add_argument("--integrity", action="store_true",
+                    help="also time verify on/off at batch 1/2/4/8, context 8692")
+    return ap.parse_args()
+
+
+def kv_bytes(w, elem_bytes: int) -> int:
+    per_token = w.num_kv_heads * (w.head_dim_k if w.latent else w.head_dim_k + w.head_dim_v)
+    return int(w.seq_lens.astype("int64").sum()) * per_token * elem_bytes
+
+
+class Runner:
+    """Device state of one workload and its timed step."""
+
+    def __init__(self, w, kv_dtype: str, split: int | None, verify: bool = True):
+        import numpy as np
+        import torch
+
+        import decode_attention_fp8_amd as pkv
+        self.torch, self.pkv, self.w = torch, pkv, w
+        dev = "cuda"
+        c = pkv.allocate_cache(w.num_pages, w.num_kv_heads, w.page_size, w.head_dim_k,
+                               w.head_dim_v, kv_dtype, w.latent, dev)
+        k = w.k_all(dev)
+        v = None if w.latent else w.v_all(dev)
+        if kv_dtype == "fp8":
+            pkv.pkv_scales_from_amax(k, w.per_head_scales, c.k_scale)
+            if w.latent:
+                c.v_scale = c.k_scale
+            else:
+                pkv.pkv_scales_from_amax(v, w.per_head_scales, c.v_scale)
+        slot = torch.from_numpy(w.slots()).to(dev)
+        pkv.pkv_append(c, k, v, slot)
+        off = w.token_offsets()
+        last = torch.from_numpy(off[1:] - 1).to(dev)
+        self.new_k = k[last].contiguous()
+        self.new_v = None if v is None else v[last].contiguous()
+        self.new_slot = slot[last].contiguous()
+        del k, v, slot
+        self.new_req = torch.arange(w.batch, dtype=torch.int32, device=dev)
+        c.page_tags = torch.from_numpy(w.page_tags.view(np.int32).copy()).to(dev)
+        self.bt = torch.from_numpy(w.block_table).to(dev)
+        self.exp = torch.from_numpy(w.expected_tags.view(np.int32).copy()).to(dev)
+        self.lens = torch.from_numpy(w.seq_lens).to(dev)
+        self.q = w.q_values(dev)
+        self.cache = c
+        self.step = pkv.DecodeStep(c, w.num_q_heads, w.batch, int(w.seq_lens.max()),
+                                   split or w.split_tokens, verify, dev)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+    def one(self, ev=None):
+        pkv, s = self.pkv, self.step
+        abort = None
+        if s.verify:
+            pkv.pkv_verify(self.cache, self.bt, self.exp, self.lens, s.abort)
+            abort = s.abort
+        pkv.pkv_append(self.cache, self.new_k, self.new_v, self.new_slot, self.new_req, abort)
+        if ev is not None:
+            ev[0].record()
+        pkv.pkv_decode_attn(self.cache, self.q, self.bt, self.lens, s.max_seq_len, abort,
+                            self.w.sm_scale, s.split_tokens, s.o_part, s.lse_part)
+        if ev is not None:
+            ev[1].record()
+        pkv.pkv_combine(s.o_part, s.lse_part, self.lens, s.split_tokens, s.max_seq_len, abort,
+                        s.out, s.lse)
+
+    def time(self, steps: int, warmup: int):
+        torch = self.torch
+        for _ in range(warmup):
+            self.one()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e in evs:
+            self.one(e)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        dec_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+        return (t1 - t0) * 1e3 / steps, dec_ms
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The oracle (quantise + tag check + attention) on a bounded sample of the
+    same workload: whole requests in order, until the time budget is spent."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from oracle import attention, quant, step
+
+    ks, vs = step.scales(w, "fp8")
+    qall = w.q_values().double().numpy()
+    G = w.group
+    t_total, tokens, reqs = 0.0, 0, 0
+    with threadpool_limits(1):
+        t = time.perf_counter()
+        flags = oracle.verify.verify(w.page_tags, w.block_table, w.expected_tags, w.seq_lens,
+                                     w.page_size)
+        t_total += time.perf_counter() - t
+        for b in range(w.batch):
+            for h in range(w.num_kv_heads):
+                x = w.k_values(b, heads=[h]).double().numpy()[:, 0, :]
+                y = w.v_values(b, heads=[h]).double().numpy()[:, 0, :]
+                t = time.perf_counter()
+                kk = quant.dequantize(quant.quantize(x, ks[h]), ks[h])[:, None, :]
+                vv = quant.dequantize(quant.quantize(y, vs[h]), vs[h])[:, None, :]
+                if not flags[b]:
+                    attention.attend(qall[b, h * G:(h + 1) * G], kk, vv, w.sm_scale)
+                t_total += time.perf_counter() - t
+            tokens += int(w.seq_lens[b])
+            reqs += 1
+            if t_total > budget_s:
+                break
+    sample_bytes = tokens * w.num_kv_heads * (w.head_dim_k + w.head_dim_v)
+    return {"value": round(sample_bytes / t_total / 1e9, 6), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"first {reqs} of {w.batch} requests ({tokens} context tokens, all "
+                      f"{w.num_kv_heads} kv heads): quantise K/V, tag check of the batch, "
+                      f"float64 attention; {t_total:.2f} s on one thread",
+            "seq_steps_per_s": round(reqs / t_total, 4)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import torch
+
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+
+    w = W.sweep(args.batch)
+    run = Runner(w, "fp8", args.split or None)
+    ms, dec_ms = run.time(args.steps, args.warmup)
+    split = run.step.split_tokens
+    fp8_bytes = kv_bytes(w, 1)
+    gbs = fp8_bytes / (ms * 1e-3) / 1e9
+    dec_gbs = fp8_bytes / (dec_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "FP8 paged decode-attn KV GB/s (% HBM peak) and seq-steps/s at B=1..64",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "e4m3-kv/f32",
+        "data": "synthetic (seeded counter-based bf16 N(0,1); lengths U[2048,32768])",
+        "config": {"workload": f"concurrency sweep B={w.batch}: contexts U[2048,32768], 64 q / 8 kv "
+                               "heads, head dim 128, page 16, e4m3 KV per-head scales, tag check on",
+                   "batch": w.batch, "total_context_tokens": w.total_tokens,
+                   "split_tokens": split, "kv_bytes": fp8_bytes},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "seq_steps_per_s": round(w.batch / (ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pkv_decode_attn (e4m3)", "avg_ms": round(dec_ms, 5)},
+    }
+    del run
+    torch.cuda.empty_cache()
+    if not args.no_bf16:
+        rb = Runner(w, "bf16", split)
+        ms_b, dec_b = rb.time(args.steps, args.warmup)
+        del rb
+        torch.cuda.empty_cache()
+        rec["bf16"] = {"ms_per_step": round(ms_b, 5),
+                       "kv_gbs": round(kv_bytes(w, 2) / (ms_b * 1e-3) / 1e9, 2),
+                       "decode_ms": round(dec_b, 5),
+                       "seq_steps_per_s": round(w.batch / (ms_b * 1e-3), 1)}
+        rec["fp8_speedup_over_bf16"] = round(ms_b / ms, 4)
+    if args.sweep:
+        rows = []
+        for B in W.SWEEP_BATCHES:
+            ws = W.sweep(B)
+            row = {"batch": B}
+            for kv, e in (("fp8", 1), ("bf16", 2)):
+                r = Runner(ws, kv, None)
+                m, d = r.time(max(10, args.steps // 2), 5)
+                del r
+                torch.cuda.empty_cache()
+                row[kv] = {"ms_per_step": round(m, 5), "kv_gbs": round(kv_bytes(ws, e) / (m * 1e-3) / 1e9, 2),
+                           "hbm_frac": round(kv_bytes(ws, e) / (m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "seq_steps_per_s": round(B / (m * 1e-3), 1), "decode_ms": round(d, 5)}
+            row["fp8_speedup_over_bf16"] = round(row["bf16"]["ms_per_step"] / row["fp8"]["ms_per_step"], 4)
+            rows.append(row)
+        rec["sweep"] = rows
+    if args.integrity:
+        rows = []
+        for B in (1, 2, 4, 8):
+            wi = W.integrity_cost(B)
+            on = Runner(wi, "fp8", None, verify=True)
+            m_on, _ = on.time(max(20, args.steps), 10)
+            del on
+            off = Runner(wi, "fp8", None, verify=False)
+            m_off, _ = off.time(max(20, args.steps), 10)
+            del off
+            torch.cuda.empty_cache()
+            rows.append({"batch": B, "ms_verify_on": round(m_on, 5), "ms_noop": round(m_off, 5),
+                         "overhead": round((m_on - m_off) / m_off, 4)})
+        rec["integrity_cost"] = rows
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

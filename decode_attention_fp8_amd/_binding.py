@@ -1,0 +1,231 @@
+"""ctypes marshalling for libpkv.so (the C ABI declared in include/pkv.h).
+
+Every function here only converts torch tensors to device pointers, reads
+torch's current HIP stream, calls the library and raises on a bad status.
+No step of the computation runs in Python: without the built library the
+import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP = 0, -1, -2, -3
+PKV_KV_E4M3, PKV_KV_BF16 = 1, 2
+
+EXPORTS = ("pkv_scales_from_amax", "pkv_append", "pkv_verify", "pkv_decode_attn",
+           "pkv_combine", "pkv_suggest_split", "pkv_strerror", "pkv_version")
+
+
+class PkvError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({pkv_strerror(status)})")
+        self.status = status
+
+
+class PkvCacheStruct(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("dtype", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("page_tags", ctypes.c_void_p)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m decode_attention_fp8_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    CP = ctypes.POINTER(PkvCacheStruct)
+    sig = {
+        "pkv_scales_from_amax": (I32, [P, I64, I32, I32, I32, P, P]),
+        "pkv_append": (I32, [CP, P, P, P, P, P, I64, P]),
+        "pkv_verify": (I32, [CP, P, P, P, I32, I32, P, P]),
+        "pkv_decode_attn": (I32, [CP, P, I32, P, P, I32, I32, I32, P, F, I32, I32, P, P, P]),
+        "pkv_combine": (I32, [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P]),
+        "pkv_suggest_split": (I32, [I32, I32, I32, I32]),
+        "pkv_strerror": (ctypes.c_char_p, [I32]),
+        "pkv_version": (I32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def pkv_strerror(status: int) -> str:
+    return _lib.pkv_strerror(int(status)).decode()
+
+
+def pkv_version() -> int:
+    return int(_lib.pkv_version())
+
+
+def pkv_suggest_split(batch: int, max_seq_len: int, num_kv_heads: int, page_size: int) -> int:
+    r = int(_lib.pkv_suggest_split(batch, max_seq_len, num_kv_heads, page_size))
+    if r < 0:
+        raise PkvError("pkv_suggest_split", r)
+    return r
+
+
+def _check(fn: str, status: int) -> None:
+    if status != PKV_OK:
+        raise PkvError(fn, status)
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libpkv takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libpkv takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+@dataclass
+class Cache:
+    """A paged cache held in torch device tensors.
+
+    k_pool: uint8 (e4m3 codes) or bfloat16, [num_pages, Hkv, P, Dk]
+    v_pool: same dtype, [num_pages, Hkv, P, Dv]; None = latent layout
+            (V is the first ``latent_dim_v`` values of each K row)
+    k_scale, v_scale: float32 [Hkv] (e4m3 only)
+    page_tags: int32 or uint32 [num_pages]
+    """
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor | None = None
+    k_scale: torch.Tensor | None = None
+    v_scale: torch.Tensor | None = None
+    page_tags: torch.Tensor | None = None
+    latent_dim_v: int | None = None
+
+    @property
+    def dtype(self) -> int:
+        return PKV_KV_E4M3 if self.k_pool.dtype == torch.uint8 else PKV_KV_BF16
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    @property
+    def num_kv_heads(self) -> int:
+        return int(self.k_pool.shape[1])
+
+    @property
+    def page_size(self) -> int:
+        return int(self.k_pool.shape[2])
+
+    @property
+    def head_dim_k(self) -> int:
+        return int(self.k_pool.shape[3])
+
+    @property
+    def head_dim_v(self) -> int:
+        return int(self.v_pool.shape[3]) if self.v_pool is not None else int(self.latent_dim_v)
+
+    def struct(self) -> PkvCacheStruct:
+        if self.k_pool.dtype not in (torch.uint8, torch.bfloat16):
+            raise ValueError("pool dtype must be uint8 (e4m3) or bfloat16")
+        if self.v_pool is not None and self.v_pool.dtype != self.k_pool.dtype:
+            raise ValueError("K and V pools differ in dtype")
+        if self.v_pool is None and self.latent_dim_v is None:
+            raise ValueError("latent layout needs latent_dim_v")
+        for t in (self.k_scale, self.v_scale):
+            if t is not None and t.dtype != torch.float32:
+                raise ValueError("scales are float32")
+        if self.page_tags is not None and self.page_tags.element_size() != 4:
+            raise ValueError("page tags are 32-bit")
+        return PkvCacheStruct(_ptr(self.k_pool), _ptr(self.v_pool), self.dtype, self.num_pages,
+                              self.page_size, self.num_kv_heads, self.head_dim_k,
+                              self.head_dim_v, _ptr(self.k_scale), _ptr(self.v_scale),
+                              _ptr(self.page_tags))
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def pkv_scales_from_amax(x: torch.Tensor, per_head: bool, scale_out: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    """x: bf16 [n_rows, H, D] -> float32 [H] scales (written into scale_out)."""
+    _need(x, torch.bfloat16, "x")
+    n, H, D = x.shape
+    if scale_out is None:
+        scale_out = torch.empty(H, dtype=torch.float32, device=x.device)
+    _check("pkv_scales_from_amax", _lib.pkv_scales_from_amax(
+        _ptr(x), n, H, D, 1 if per_head else 0, _ptr(scale_out), _stream(stream)))
+    return scale_out
+
+
+def pkv_append(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor | None,
+               slot: torch.Tensor, token_req: torch.Tensor | None = None,
+               abort_flags: torch.Tensor | None = None, stream=None) -> None:
+    _need(k_new, torch.bfloat16, "k_new")
+    if v_new is not None:
+        _need(v_new, torch.bfloat16, "v_new")
+    _need(slot, torch.int32, "slot")
+    cs = cache.struct()
+    _check("pkv_append", _lib.pkv_append(
+        ctypes.byref(cs), _ptr(k_new), _ptr(v_new), _ptr(slot), _ptr(token_req),
+        _ptr(abort_flags), int(slot.numel()), _stream(stream)))
+
+
+def pkv_verify(cache: Cache, block_table: torch.Tensor, expected_tags: torch.Tensor,
+               seq_lens: torch.Tensor, abort_out: torch.Tensor, stream=None) -> None:
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    _need(abort_out, torch.uint8, "abort_out")
+    if expected_tags.element_size() != 4:
+        raise ValueError("expected_tags are 32-bit")
+    B, max_pages = block_table.shape
+    cs = cache.struct()
+    _check("pkv_verify", _lib.pkv_verify(
+        ctypes.byref(cs), _ptr(block_table), _ptr(expected_tags), _ptr(seq_lens), B, max_pages,
+        _ptr(abort_out), _stream(stream)))
+
+
+def pkv_decode_attn(cache: Cache, q: torch.Tensor, block_table: torch.Tensor,
+                    seq_lens: torch.Tensor, max_seq_len: int, abort_flags: torch.Tensor | None,
+                    sm_scale: float, split_tokens: int, o_part: torch.Tensor,
+                    lse_part: torch.Tensor, stream=None) -> None:
+    """q bf16 [B, Hq, Dk]; o_part f32 [B, Hq, max_splits, Dv]; lse_part f32 [B, Hq, max_splits]."""
+    _need(q, torch.bfloat16, "q")
+    _need(o_part, torch.float32, "o_part")
+    _need(lse_part, torch.float32, "lse_part")
+    B, Hq, _ = q.shape
+    max_splits = int(lse_part.shape[2])
+    cs = cache.struct()
+    _check("pkv_decode_attn", _lib.pkv_decode_attn(
+        ctypes.byref(cs), _ptr(q), Hq, _ptr(block_table), _ptr(seq_lens), B,
+        int(block_table.shape[1]), int(max_seq_len), _ptr(abort_flags), float(sm_scale),
+        int(split_tokens), max_splits, _ptr(o_part), _ptr(lse_part), _stream(stream)))
+
+
+def pkv_combine(o_part: torch.Tensor, lse_part: torch.Tensor, seq_lens: torch.Tensor,
+                split_tokens: int, max_seq_len: int, abort_flags: torch.Tensor | None,
+                out: torch.Tensor, lse_out: torch.Tensor | None = None, stream=None) -> None:
+    """out bf16 [B, Hq, Dv]; lse_out f32 [B, Hq] or None."""
+    _need(out, torch.bfloat16, "out")
+    B, Hq, max_splits, Dv = o_part.shape
+    _check("pkv_combine", _lib.pkv_combine(
+        _ptr(o_part), _ptr(lse_part), _ptr(seq_lens), B, Hq, Dv, int(split_tokens), max_splits,
+        int(max_seq_len), _ptr(abort_flags), _ptr(out), _ptr(lse_out), _stream(stream)))

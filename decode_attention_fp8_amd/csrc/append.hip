@@ -1,0 +1,134 @@
+// pkv_append: quantise-on-append of new K/V rows into cache pages.
+//
+// "Smaller, faster, safer", section "Quantizing the KV cache": the cache is
+// held as e4m3 instead of BF16. Each value x of kv head h becomes
+// RNE_SAT(fl32(x / scale[h])): a correctly rounded float32 division, then
+// round-to-nearest-even onto the OCP E4M3 grid, saturating at +-448.
+//
+// One thread owns 16 consecutive values of one (token, kv head) row: it
+// reads 32 bytes of bf16 and writes one 16-byte chunk of codes (32 bytes for
+// a bf16 cache), so a wave writes whole rows with 16-byte stores.
+#include "common.h"
+
+namespace {
+
+// float32 -> e4m3 code, round to nearest even, saturating, from the IEEE
+// bit layout: 4-bit exponent with bias 7 and 3 mantissa bits; below 2^-6
+// the grid is the multiples of 2^-9.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;   // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;  // |y| >= 448 or infinite
+  if (a < 0x3C800000u) {                      // |y| < 2^-6: count of 2^-9 steps
+    return sign | static_cast<uint32_t>(rintf(__uint_as_float(a) * 512.0f));
+  }
+  uint32_t code = (((a >> 23) - 120u) << 3) | ((a >> 20) & 7u);
+  const uint32_t rem = a & 0xFFFFFu;
+  code += (rem > 0x80000u) || (rem == 0x80000u && (code & 1u));
+  return sign | code;
+}
+
+struct AppendArgs {
+  const uint16_t* src;  // bf16 [n][heads][dim]
+  uint8_t* pool;        // [pages][heads][P][dim] elements of elem_bytes
+  const float* scale;   // [heads] (e4m3 only)
+  int dim;              // elements per row
+  int pool_dim;         // row length in the pool (>= dim; latent rows)
+};
+
+template <bool kE4M3>
+__global__ void __launch_bounds__(256) append_kernel(AppendArgs a, const int32_t* __restrict__ slot,
+                                                     const int32_t* __restrict__ token_req,
+                                                     const uint8_t* __restrict__ abort_flags,
+                                                     int64_t n_tokens, int heads, int page_size,
+                                                     int64_t n_slots) {
+  const int chunks = a.dim / 16;
+  const int64_t per_token = static_cast<int64_t>(heads) * chunks;
+  const int64_t total = n_tokens * per_token;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t tok = i / per_token;
+    const int rem = static_cast<int>(i - tok * per_token);
+    const int h = rem / chunks;
+    const int c = rem - h * chunks;
+    const int32_t s = slot[tok];
+    if (s < 0 || s >= n_slots) continue;
+    if (token_req && abort_flags && abort_flags[token_req[tok]]) continue;
+    const int64_t page = s / page_size;
+    const int row = s - static_cast<int>(page) * page_size;
+    const uint16_t* src = a.src + (tok * heads + h) * a.dim + c * 16;
+    const uint4 w0 = *reinterpret_cast<const uint4*>(src);
+    const uint4 w1 = *reinterpret_cast<const uint4*>(src + 8);
+    const int64_t dst_elem = ((page * heads + h) * page_size + row) * a.pool_dim + c * 16;
+    if constexpr (kE4M3) {
+      const float s_h = a.scale[h];
+      const uint32_t in[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      uint32_t out[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t pair = in[2 * k + j];
+          const float lo = __uint_as_float(pair << 16);
+          const float hi = __uint_as_float(pair & 0xFFFF0000u);
+          const uint32_t c0 = e4m3_rne_sat(__fdiv_rn(lo, s_h));
+          const uint32_t c1 = e4m3_rne_sat(__fdiv_rn(hi, s_h));
+          word |= (c0 | (c1 << 8)) << (16 * j);
+        }
+        out[k] = word;
+      }
+      *reinterpret_cast<uint4*>(a.pool + dst_elem) = make_uint4(out[0], out[1], out[2], out[3]);
+    } else {
+      uint4* dst = reinterpret_cast<uint4*>(a.pool + dst_elem * 2);
+      dst[0] = w0;
+      dst[1] = w1;
+    }
+  }
+}
+
+template <bool kE4M3>
+int launch(const AppendArgs& a, const int32_t* slot, const int32_t* token_req,
+           const uint8_t* abort_flags, int64_t n, int heads, int page_size, int64_t n_slots,
+           hipStream_t stream) {
+  const int64_t total = n * heads * (a.dim / 16);
+  if (total == 0) return PKV_OK;
+  const int blocks = static_cast<int>(std::min<int64_t>(pkv::cdiv(total, 256), 65536));
+  append_kernel<kE4M3><<<blocks, 256, 0, stream>>>(a, slot, token_req, abort_flags, n, heads,
+                                                   page_size, n_slots);
+  return pkv::launch_status();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" int pkv_append(const pkv_cache* cache, const void* k_new, const void* v_new,
+                          const int32_t* slot, const int32_t* token_req,
+                          const uint8_t* abort_flags, int64_t n_tokens, hipStream_t stream) {
+  int st = pkv::check_cache(cache);
+  if (st) return st;
+  const bool latent = cache->v_pool == nullptr;
+  if (!k_new || !slot || n_tokens < 0 || (latent && v_new) || (!latent && !v_new))
+    return PKV_EINVAL;
+  if (!aligned16(k_new) || (v_new && !aligned16(v_new)) || !aligned16(cache->k_pool) ||
+      (cache->v_pool && !aligned16(cache->v_pool)))
+    return PKV_EINVAL;
+  const bool e4m3 = cache->dtype == PKV_KV_E4M3;
+  const int64_t n_slots = static_cast<int64_t>(cache->num_pages) * cache->page_size;
+  AppendArgs k{static_cast<const uint16_t*>(k_new), static_cast<uint8_t*>(cache->k_pool),
+               cache->k_scale, cache->head_dim_k, cache->head_dim_k};
+  st = e4m3 ? launch<true>(k, slot, token_req, abort_flags, n_tokens, cache->num_kv_heads,
+                           cache->page_size, n_slots, stream)
+            : launch<false>(k, slot, token_req, abort_flags, n_tokens, cache->num_kv_heads,
+                            cache->page_size, n_slots, stream);
+  if (st || latent) return st;
+  AppendArgs v{static_cast<const uint16_t*>(v_new), static_cast<uint8_t*>(cache->v_pool),
+               cache->v_scale, cache->head_dim_v, cache->head_dim_v};
+  return e4m3 ? launch<true>(v, slot, token_req, abort_flags, n_tokens, cache->num_kv_heads,
+                             cache->page_size, n_slots, stream)
+              : launch<false>(v, slot, token_req, abort_flags, n_tokens, cache->num_kv_heads,
+                              cache->page_size, n_slots, stream);
+}

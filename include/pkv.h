@@ -1,0 +1,242 @@
+/*
+ * pkv — FP8 (OCP E4M3) paged KV cache and single-token decode attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Smaller, faster, safer: running Kimi and GLM at scale"
+ * (Cloudflare blog).
+ *   - Section "Quantizing the KV cache": keys and values are cached as
+ *     8-bit floats (e4m3) instead of BF16, which halves the cache; the
+ *     attention kernel converts the cached values as it reads them.
+ *   - Section "Protecting a shared KV cache": every physical page has a
+ *     tag that changes when the page is reallocated; the server records
+ *     the pages and tags each request expects; before decode reads the
+ *     cache the mapping is checked in a separate batch pass, and any
+ *     request with a mismatch is aborted; with checking off, a no-op
+ *     tracker costs nothing.
+ *
+ * A decode step is four calls on one stream, in this order:
+ *   pkv_verify -> pkv_append -> pkv_decode_attn -> pkv_combine
+ * The abort flags written by pkv_verify reach the later calls through
+ * device memory, ordered by the stream; passing abort_flags == NULL to a
+ * call is the no-op tracker (nothing is checked, nothing is skipped).
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller; the
+ *     library keeps no reference after the call returns.
+ *   - The library allocates no memory, never synchronises the host, throws
+ *     nothing across this interface and keeps no state between calls.
+ *   - Work is enqueued on `stream` (NULL = the null stream) and runs
+ *     asynchronously; results are valid once the stream reaches them.
+ *   - Return value: PKV_OK, or a negative pkv_status. Argument errors are
+ *     detected on the host before anything is enqueued. PKV_EHIP means a
+ *     launch failed (hipGetLastError); the stream's earlier work is intact.
+ *   - A tag mismatch is data, not an error: it appears only in the flags.
+ *   - bf16 means IEEE-754 binary32 truncated to its upper 16 bits (brain
+ *     float), stored as uint16; e4m3 means OCP 8-bit float E4M3 (bias 7,
+ *     max 448, NaN S.1111.111, no infinity) stored as uint8.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,        /* a pointer, size or layout argument is invalid */
+  PKV_EUNSUPPORTED = -2,  /* valid arguments, but no kernel for that shape */
+  PKV_EHIP = -3           /* a HIP launch or runtime call failed */
+} pkv_status;
+
+typedef enum pkv_kv_dtype {
+  PKV_KV_E4M3 = 1,  /* one byte per element, dequantised with a scale */
+  PKV_KV_BF16 = 2   /* two bytes per element, used as stored */
+} pkv_kv_dtype;
+
+/*
+ * The paged cache (caller-owned device memory).
+ *
+ * Layout ("pages of the same physical KV cache", section "Protecting a
+ * shared KV cache"; the pages give no layout, this one is chosen so a
+ * (page, kv head) block is one contiguous run of page_size rows):
+ *   k_pool: [num_pages][num_kv_heads][page_size][head_dim_k]
+ *   v_pool: [num_pages][num_kv_heads][page_size][head_dim_v]
+ * Token t of a request is in page block_table[t / page_size], row
+ * t % page_size; one tag per page id covers K and V of every kv head.
+ *
+ * Latent layout (v_pool == NULL): one row of head_dim_k values per token
+ * and kv head, and V is the first head_dim_v values of the same row (read
+ * once, dequantised with k_scale).
+ *
+ * k_scale, v_scale: float32 [num_kv_heads], the dequantisation scale of
+ *   each kv head (equal entries = one scale per tensor); an e4m3 code c
+ *   stands for decode(c) * scale. Ignored for PKV_KV_BF16 (may be NULL).
+ * page_tags: uint32 [num_pages], the current tag of each physical page;
+ *   read only by pkv_verify (may be NULL otherwise).
+ */
+typedef struct pkv_cache {
+  void* k_pool;
+  void* v_pool;
+  int32_t dtype;        /* pkv_kv_dtype */
+  int32_t num_pages;    /* >= 1 */
+  int32_t page_size;    /* tokens per page: 16, 32 or 64 */
+  int32_t num_kv_heads; /* >= 1 */
+  int32_t head_dim_k;   /* multiple of 16 */
+  int32_t head_dim_v;   /* multiple of 16; <= head_dim_k when latent */
+  const float* k_scale;
+  const float* v_scale;
+  const uint32_t* page_tags;
+} pkv_cache;
+
+/*
+ * Per-head (or per-tensor) e4m3 scales from the largest magnitude.
+ * Section "Quantizing the KV cache" gives no scale rule; this library's is
+ * a static scale s = fl32(amax / 448) (a correctly rounded float32
+ * division; s = 1 when amax = 0), 448 being the largest e4m3 magnitude.
+ *
+ *   x:         bf16 [n_rows][num_heads][head_dim], e.g. all K rows.
+ *   per_head:  nonzero -> scale_out[h] from head h's values only;
+ *              zero    -> every scale_out[h] from the whole tensor.
+ *   scale_out: float32 [num_heads]; also used as scratch during the call.
+ * NaN inputs give a NaN scale. EINVAL: NULL pointer, n_rows < 1,
+ * num_heads < 1, head_dim not a multiple of 8.
+ */
+int pkv_scales_from_amax(const void* x, int64_t n_rows, int32_t num_heads,
+                         int32_t head_dim, int32_t per_head, float* scale_out,
+                         hipStream_t stream);
+
+/*
+ * Quantise-on-append (section "Quantizing the KV cache": the cache is held
+ * in e4m3).
+ *
+ * For every token i < n_tokens with slot[i] >= 0, every kv head h and
+ * dimension d:
+ *   e4m3: pool[slot/P][h][slot%P][d] = RNE_SAT(fl32(x / scale[h]))
+ *         (round to nearest, ties to even; |y| >= 448 and infinities become
+ *          +-448; NaN becomes the NaN code of its sign; -0 stays -0)
+ *   bf16: the value is copied unchanged.
+ *   k_new: bf16 [n_tokens][num_kv_heads][head_dim_k]
+ *   v_new: bf16 [n_tokens][num_kv_heads][head_dim_v]; must be NULL for the
+ *          latent layout (V lives inside the K row).
+ *   slot:  int32 [n_tokens], page * page_size + row; < 0 = skip the token;
+ *          slots past the pool (>= num_pages * page_size) are skipped too.
+ *   token_req, abort_flags: when both are non-NULL, token i is skipped if
+ *          abort_flags[token_req[i]] != 0 (an aborted request writes
+ *          nothing). token_req: int32 [n_tokens]; abort_flags: uint8 [B].
+ * Two tokens with the same slot in one call race (either may win).
+ * EINVAL: NULL pool/scale/k_new/slot, v_new given for latent or missing
+ * otherwise, n_tokens < 0, invalid cache geometry.
+ */
+int pkv_append(const pkv_cache* cache, const void* k_new, const void* v_new,
+               const int32_t* slot, const int32_t* token_req,
+               const uint8_t* abort_flags, int64_t n_tokens, hipStream_t stream);
+
+/*
+ * Integrity check (section "Protecting a shared KV cache"): for each
+ * request b with n = ceil(seq_lens[b] / page_size) pages,
+ *   abort_out[b] = 1 if some j < n has block_table[b][j] outside
+ *                  [0, num_pages), or page_tags[block_table[b][j]] !=
+ *                  expected_tags[b][j], or j >= max_pages; else 0.
+ * Entries past n are ignored. A separate launch: the decode kernel reads
+ * the flags after it, never alongside it.
+ *
+ *   block_table:   int32  [batch][max_pages]
+ *   expected_tags: uint32 [batch][max_pages], the tags recorded by the caller
+ *   seq_lens:      int32  [batch], tokens of each request including the one
+ *                  appended this step (<= 0 = empty request, never aborted)
+ *   abort_out:     uint8  [batch], fully overwritten.
+ * EINVAL: NULL pointers (cache->page_tags included), batch < 0,
+ * max_pages < 1.
+ */
+int pkv_verify(const pkv_cache* cache, const int32_t* block_table,
+               const uint32_t* expected_tags, const int32_t* seq_lens,
+               int32_t batch, int32_t max_pages, uint8_t* abort_out,
+               hipStream_t stream);
+
+/*
+ * Split-KV paged decode attention (section "Quantizing the KV cache": the
+ * FP8 kernel converts values as it reads them; section "Protecting a shared
+ * KV cache": paged attention over a shared physical cache).
+ *
+ * For request b (skipped entirely when abort_flags != NULL and
+ * abort_flags[b] != 0), split c < ceil(L / split_tokens) covering tokens
+ * [c*S, min((c+1)*S, L)), and query head h reading kv head
+ * g = h / (num_q_heads / num_kv_heads):
+ *   s_t        = sm_scale * sum_d q[b][h][d] * K[t][g][d]
+ *   o_part     = sum_t exp(s_t - m) * V[t][g][:] / sum_t exp(s_t - m)
+ *   lse_part   = m + ln sum_t exp(s_t - m)        (natural log)
+ * where K, V are the dequantised cached values (code * scale for e4m3).
+ *
+ *   q:        bf16 [batch][num_q_heads][head_dim_k]
+ *   block_table, seq_lens, max_pages: as for pkv_verify.
+ *   max_seq_len: an upper bound on every seq_lens[b], used to size the
+ *            launch; must satisfy max_seq_len <= max_pages * page_size and
+ *            ceil(max_seq_len / split_tokens) <= max_splits. A request with
+ *            seq_lens[b] > max_seq_len gets NaN outputs from pkv_combine.
+ *   split_tokens: S, a positive multiple of page_size.
+ *   o_part:   float32 [batch][num_q_heads][max_splits][head_dim_v]
+ *   lse_part: float32 [batch][num_q_heads][max_splits]
+ * Only the splits a request has are written; aborted requests write
+ * nothing. A block-table entry outside [0, num_pages) is never read: its
+ * tokens are left out (pkv_verify turns such requests into aborts).
+ * EINVAL: NULL pointers, num_q_heads not a multiple of num_kv_heads,
+ * split_tokens invalid, max_seq_len or max_splits inconsistent.
+ * EUNSUPPORTED: a shape with no kernel; supported are
+ *   grouped-query: head_dim_k == head_dim_v in {64, 128},
+ *                  num_q_heads / num_kv_heads in {1, 2, 4, 8, 16};
+ *   latent:        head_dim_k == 576, head_dim_v == 512, one kv head,
+ *                  num_q_heads a multiple of 16.
+ */
+int pkv_decode_attn(const pkv_cache* cache, const void* q, int32_t num_q_heads,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    int32_t batch, int32_t max_pages, int32_t max_seq_len,
+                    const uint8_t* abort_flags, float sm_scale,
+                    int32_t split_tokens, int32_t max_splits, float* o_part,
+                    float* lse_part, hipStream_t stream);
+
+/*
+ * Log-sum-exp merge of the split partials (not on the pages; a reordering
+ * of the same softmax sum). For request b with n = ceil(L / split_tokens)
+ * splits:
+ *   M = max_c lse_c, w_c = exp(lse_c - M),
+ *   out[b][h] = bf16_RNE( sum_c w_c * o_c / sum_c w_c ),
+ *   lse_out[b][h] = M + ln sum_c w_c.
+ * Aborted (abort_flags[b] != 0) or empty (L <= 0) requests get out = 0 and
+ * lse_out = -inf; a request with L > max_seq_len gets NaN.
+ *   o_part, lse_part, split_tokens, max_splits, max_seq_len: as passed to
+ *            pkv_decode_attn.
+ *   out:     bf16 [batch][num_q_heads][head_dim_v]
+ *   lse_out: float32 [batch][num_q_heads], or NULL.
+ * EINVAL: NULL pointers, non-positive sizes, head_dim_v not a multiple of 8,
+ * ceil(max_seq_len / split_tokens) > max_splits.
+ */
+int pkv_combine(const float* o_part, const float* lse_part,
+                const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                int32_t head_dim_v, int32_t split_tokens, int32_t max_splits,
+                int32_t max_seq_len, const uint8_t* abort_flags, void* out,
+                float* lse_out, hipStream_t stream);
+
+/*
+ * Host helper: a split size (multiple of page_size) giving enough
+ * independent work units to fill the GPU for this batch and context,
+ * without cutting splits so short that the merge traffic matters.
+ * Returns a positive token count, or PKV_EINVAL.
+ */
+int32_t pkv_suggest_split(int32_t batch, int32_t max_seq_len,
+                          int32_t num_kv_heads, int32_t page_size);
+
+/* Host helper: a static string naming a status code. */
+const char* pkv_strerror(int32_t status);
+
+/* Host helper: library version, major * 10000 + minor * 100 + patch. */
+int32_t pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

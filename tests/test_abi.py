@@ -1,0 +1,100 @@
+"""CPU checks of the C-ABI boundary: the library loads, exports every
+function include/pkv.h declares, and rejects bad arguments on the host
+before anything reaches a GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import decode_attention_fp8_amd as pkv
+from decode_attention_fp8_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_four_hot_path_calls():
+    d = declared()
+    for name in ("pkv_append", "pkv_verify", "pkv_decode_attn", "pkv_combine"):
+        assert name in d
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for name in declared():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (pkv_\w+)", nm))
+    assert set(declared()) <= exported
+    assert set(B.EXPORTS) == set(declared())
+
+
+def test_host_helpers():
+    assert pkv.pkv_version() >= 100
+    assert pkv.pkv_strerror(0) == "ok"
+    assert pkv.pkv_strerror(-1) == "invalid argument"
+    s = pkv.pkv_suggest_split(64, 32768, 8, 16)
+    assert s > 0 and s % 16 == 0
+    assert pkv.pkv_suggest_split(1, 10, 8, 64) == 64
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_suggest_split(1, 10, 8, 17)
+
+
+def _cache(**kw):
+    base = dict(k_pool=16, v_pool=32, dtype=1, num_pages=4, page_size=16, num_kv_heads=1,
+                head_dim_k=64, head_dim_v=64, k_scale=48, v_scale=64, page_tags=80)
+    base.update(kw)
+    return B.PkvCacheStruct(**base)
+
+
+def test_invalid_arguments_rejected_on_host():
+    lib = B._lib
+    E = B.PKV_EINVAL
+    P = 4096  # a fake, aligned, never-dereferenced address
+    # scales
+    assert lib.pkv_scales_from_amax(None, 1, 1, 64, 0, P, None) == E
+    assert lib.pkv_scales_from_amax(P, 1, 1, 60, 0, P, None) == E
+    assert lib.pkv_scales_from_amax(P + 2, 1, 1, 64, 0, P, None) == E
+    # append
+    assert lib.pkv_append(None, P, P, P, None, None, 1, None) == E
+    assert lib.pkv_append(ctypes.byref(_cache(page_size=24)), P, P, P, None, None, 1, None) == E
+    assert lib.pkv_append(ctypes.byref(_cache(head_dim_k=72)), P, P, P, None, None, 1, None) == E
+    assert lib.pkv_append(ctypes.byref(_cache(v_pool=None)), P, P, P, None, None, 1, None) == E
+    assert lib.pkv_append(ctypes.byref(_cache()), P, None, P, None, None, 1, None) == E
+    assert lib.pkv_append(ctypes.byref(_cache(k_scale=None)), P, P, P, None, None, 1, None) == E
+    # verify
+    assert lib.pkv_verify(ctypes.byref(_cache(page_tags=None)), P, P, P, 1, 1, P, None) == E
+    assert lib.pkv_verify(ctypes.byref(_cache()), P, P, P, -1, 1, P, None) == E
+    assert lib.pkv_verify(ctypes.byref(_cache()), P, P, P, 1, 0, P, None) == E
+    # decode: split not a page multiple, q heads not a kv multiple, bounds inconsistent
+    c = ctypes.byref(_cache(num_kv_heads=2))
+    assert lib.pkv_decode_attn(c, P, 8, P, P, 1, 4, 64, None, 0.1, 24, 8, P, P, None) == E
+    assert lib.pkv_decode_attn(c, P, 7, P, P, 1, 4, 64, None, 0.1, 16, 8, P, P, None) == E
+    assert lib.pkv_decode_attn(c, P, 8, P, P, 1, 4, 65, None, 0.1, 16, 8, P, P, None) == E
+    assert lib.pkv_decode_attn(c, P, 8, P, P, 1, 4, 64, None, 0.1, 16, 3, P, P, None) == E
+    assert lib.pkv_decode_attn(c, None, 8, P, P, 1, 4, 64, None, 0.1, 16, 8, P, P, None) == E
+    # decode: unsupported shapes
+    U = B.PKV_EUNSUPPORTED
+    assert lib.pkv_decode_attn(ctypes.byref(_cache(head_dim_k=96, head_dim_v=96)), P, 1, P, P, 1,
+                               4, 64, None, 0.1, 16, 8, P, P, None) == U
+    assert lib.pkv_decode_attn(ctypes.byref(_cache(num_kv_heads=1)), P, 3, P, P, 1, 4, 64, None,
+                               0.1, 16, 8, P, P, None) == U
+    # combine
+    assert lib.pkv_combine(None, P, P, 1, 1, 64, 16, 4, 64, None, P, None, None) == E
+    assert lib.pkv_combine(P, P, P, 1, 1, 64, 16, 3, 64, None, P, None, None) == E
+    assert lib.pkv_combine(P, P, P, 1, 1, 60, 16, 4, 64, None, P, None, None) == E
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros((1, 1, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pkv.pkv_scales_from_amax(x, False, torch.zeros(1))
