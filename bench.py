@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true", help="also time batch 1/8/16/32")
     ap.add_argument("--integrity", action="store_true",
                     help="also time verify on/off at batch 1/2/4/8, context 8692")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
 
 
@@ -173,6 +176,15 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return
 
     w = W.sweep(args.batch)
     run = Runner(w, "fp8", args.split or None)

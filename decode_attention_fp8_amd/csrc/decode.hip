@@ -6,12 +6,17 @@
 // shared by many requests (paged attention), and a request flagged by the
 // separate tag check is never read.
 //
+// This file holds the entry point and the generic kernel used for shapes
+// without a specialised one (decode_gqa.hip covers head dim 128 with 8 query
+// heads per kv head).
+//
 // Work unit = (request b, kv head g, group of NH query heads, split c).
 // A workgroup of four waves takes one work unit; wave w handles tokens
 // c*S + w, c*S + w + 4, ...; lane l owns dimensions l, l + 64, ... of the
 // head. Scores are reduced across the wave, each wave keeps its own online
 // softmax state, and the four states are merged through LDS at the end.
 #include "common.h"
+#include "decode_params.h"
 
 namespace {
 
@@ -36,22 +41,7 @@ __device__ __forceinline__ float load_kv(const void* base, int64_t idx) {
   }
 }
 
-struct Params {
-  const void* k_pool;
-  const void* v_pool;     // == k_pool for the latent layout
-  const float* k_scale;
-  const float* v_scale;
-  const uint16_t* q;
-  const int32_t* block_table;
-  const int32_t* seq_lens;
-  const uint8_t* abort_flags;
-  float* o_part;
-  float* lse_part;
-  int num_pages, page_size, num_kv_heads, num_q_heads, max_pages, max_seq_len;
-  int split_tokens, max_splits, head_groups;
-  int v_row;              // elements per V row in v_pool
-  float sm_scale_log2;    // sm_scale * log2(e)
-};
+using Params = DecodeParams;
 
 template <bool kE4M3, int DK, int DV, int NH>
 __global__ void __launch_bounds__(256) decode_kernel(Params p) {
@@ -250,6 +240,8 @@ extern "C" int pkv_decode_attn(const pkv_cache* cache, const void* q, int32_t nu
   p.v_row = latent ? dk : dv;
   p.sm_scale_log2 = sm_scale * kLog2e;
   const bool e4m3 = cache->dtype == PKV_KV_E4M3;
+  if (gqa_fast_path_supported(dk, dv, G, latent, split_tokens, cache->page_size))
+    return launch_decode_gqa(p, e4m3, static_cast<int>(n_split_blocks), batch, stream);
   return e4m3 ? dispatch<true>(p, latent, dk, G, static_cast<int>(n_split_blocks), batch, stream)
               : dispatch<false>(p, latent, dk, G, static_cast<int>(n_split_blocks), batch, stream);
 }

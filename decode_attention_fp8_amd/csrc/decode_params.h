@@ -1,0 +1,28 @@
+// Launch parameters shared by the decode kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+struct DecodeParams {
+  const void* k_pool;
+  const void* v_pool;  // == k_pool for the latent layout
+  const float* k_scale;
+  const float* v_scale;
+  const uint16_t* q;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const uint8_t* abort_flags;
+  float* o_part;
+  float* lse_part;
+  int num_pages, page_size, num_kv_heads, num_q_heads, max_pages, max_seq_len;
+  int split_tokens, max_splits, head_groups;
+  int v_row;            // elements per V row in v_pool
+  float sm_scale_log2;  // sm_scale * log2(e)
+};
+
+// grouped-query kernel for head dim 128, 8 query heads per kv head
+bool gqa_fast_path_supported(int dk, int dv, int group, bool latent, int split_tokens,
+                             int page_size);
+int launch_decode_gqa(const DecodeParams& p, bool e4m3, int n_split_blocks, int batch,
+                      hipStream_t stream);

@@ -213,6 +213,7 @@ int pkv_decode_attn(const pkv_cache* cache, const void* q, int32_t num_q_heads,
  *   lse_out: float32 [batch][num_q_heads], or NULL.
  * EINVAL: NULL pointers, non-positive sizes, head_dim_v not a multiple of 8,
  * ceil(max_seq_len / split_tokens) > max_splits.
+ * EUNSUPPORTED: head_dim_v not in {64, 128, 256, 512}.
  */
 int pkv_combine(const float* o_part, const float* lse_part,
                 const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
