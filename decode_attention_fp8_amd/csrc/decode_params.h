@@ -26,3 +26,9 @@ bool gqa_fast_path_supported(int dk, int dv, int group, bool latent, int split_t
                              int page_size);
 int launch_decode_gqa(const DecodeParams& p, bool e4m3, int n_split_blocks, int batch,
                       hipStream_t stream);
+
+// wide-head kernel for one latent kv head (576 / 512), page size 64
+bool mla_fast_path_supported(int dk, int dv, int num_kv_heads, int num_q_heads, int page_size,
+                             int split_tokens);
+int launch_decode_mla(const DecodeParams& p, bool e4m3, int n_split_blocks, int batch,
+                      hipStream_t stream);

@@ -86,6 +86,16 @@ def test_mla_sampled_including_aborted(kv):
     _check_requests(st, sorted(set(aborted + shortest + longest)))
 
 
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+@pytest.mark.parametrize("hq,lens,split", [(64, [1, 63, 64, 65, 700], 64), (128, [129, 2000], 512),
+                                           (128, [4100, 33], 1024)])
+def test_mla_shapes_ragged(kv, hq, lens, split):
+    w = W.custom(f"mla{hq}", 81, lens, hq=hq, hkv=1, dk=576, dv=512, page=64, latent=True,
+                 split=split, sm_scale=1 / math.sqrt(576))
+    st = State(w, kv)
+    _check_requests(st, range(w.batch))
+
+
 # ------------------------------------------------------------- edge cases
 @pytest.mark.parametrize("lens,P,split", [([1], 16, 16), ([16, 17, 15], 16, 16), ([1, 2, 3, 4], 64, 64),
                                           ([300, 1, 257], 32, 96), ([5000, 33], 16, 256)])
