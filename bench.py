@@ -26,6 +26,7 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK = 2500.0  # TFLOP/s, dense
 
 
 def parse():
@@ -34,6 +35,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--batch", type=int, default=64)
+    ap.add_argument("--workload", default="sweep", choices=["sweep", "gqa", "long", "mla"],
+                    help="sweep: concurrency-sweep point (--batch); gqa: batch 8 x 4096; "
+                         "long: batch 4 x 131072, 256-token splits; mla: wide latent head")
     ap.add_argument("--split", type=int, default=0, help="split tokens (0 = library's suggestion)")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -186,7 +190,8 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
         return
 
-    w = W.sweep(args.batch)
+    w = {"sweep": lambda: W.sweep(args.batch), "gqa": W.gqa, "long": W.long_context,
+         "mla": W.mla}[args.workload]()
     run = Runner(w, "fp8", args.split or None)
     ms, dec_ms = run.time(args.steps, args.warmup)
     split = run.step.split_tokens
@@ -199,16 +204,27 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "e4m3-kv/f32",
         "data": "synthetic (seeded counter-based bf16 N(0,1); lengths U[2048,32768])",
-        "config": {"workload": f"concurrency sweep B={w.batch}: contexts U[2048,32768], 64 q / 8 kv "
-                               "heads, head dim 128, page 16, e4m3 KV per-head scales, tag check on",
-                   "batch": w.batch, "total_context_tokens": w.total_tokens,
-                   "split_tokens": split, "kv_bytes": fp8_bytes},
+        "config": {"workload": f"{w.name}: {w.description}", "batch": w.batch,
+                   "total_context_tokens": w.total_tokens, "split_tokens": split,
+                   "kv_dtype": "e4m3", "kv_bytes": fp8_bytes},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "seq_steps_per_s": round(w.batch / (ms * 1e-3), 1),
-        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "pkv_decode_attn (e4m3)", "avg_ms": round(dec_ms, 5)},
     }
+    if w.latent:
+        # the dense contraction bounds this kernel: QK^T over 576 dims and PV
+        # over 512 for every (token, query head)
+        flop = 2 * w.num_q_heads * (w.head_dim_k + w.head_dim_v) * w.total_tokens
+        tflops = flop / (dec_ms * 1e-3) / 1e12
+        rec["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK,
+                           "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK, 4),
+                           "traffic": None, "kernel": "pkv_decode_attn (latent, bf16 MFMA)",
+                           "avg_ms": round(dec_ms, 5), "hbm_gbs": round(dec_gbs, 2),
+                           "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        rec["roofline"] = {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                           "traffic": None, "kernel": "pkv_decode_attn (e4m3)",
+                           "avg_ms": round(dec_ms, 5)}
     del run
     torch.cuda.empty_cache()
     if not args.no_bf16:
@@ -251,7 +267,7 @@ def main():
             rows.append({"batch": B, "ms_verify_on": round(m_on, 5), "ms_noop": round(m_off, 5),
                          "overhead": round((m_on - m_off) / m_off, 4)})
         rec["integrity_cost"] = rows
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not w.latent:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)
 
