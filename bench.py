@@ -170,7 +170,7 @@ def cpu_baseline(w, budget_s: float = 12.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "pkv measures one GPU; --gpus must be 1 (sharding is described, not run)"}))
         sys.exit(2)
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import torch

@@ -60,8 +60,8 @@ typedef enum pkv_kv_dtype {
 /*
  * The paged cache (caller-owned device memory).
  *
- * Layout ("pages of the same physical KV cache", section "Protecting a
- * shared KV cache"; the pages give no layout, this one is chosen so a
+ * Layout (section "Protecting a shared KV cache" has requests share pages
+ * of one physical cache; the pages give no layout, this one is chosen so a
  * (page, kv head) block is one contiguous run of page_size rows):
  *   k_pool: [num_pages][num_kv_heads][page_size][head_dim_k]
  *   v_pool: [num_pages][num_kv_heads][page_size][head_dim_v]
