@@ -28,6 +28,17 @@ import time
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK = 2500.0  # TFLOP/s, dense
 
+# HBM traffic of the decode kernel from rocprofv3 --pmc runs of this same
+# command (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, mean over the
+# dispatches), keyed by (workload, split, sha256 prefix of the kernel source
+# the counters were taken on). A plain 1 GiB device copy reads as 524,300 KiB
+# FETCH_SIZE and 1,048,576 KiB WRITE_SIZE, so FETCH_SIZE counts in units of 2 KiB
+# here and WRITE_SIZE in KiB. Entries stop matching once the kernel changes.
+FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
+TRAFFIC_KIB = {
+    ("sweep_b64", 512, "decode_gqa.hip", "ae4dd4fb49899969"): (1199578.1, 81311.7),
+}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -48,6 +59,20 @@ def parse():
                     help="only run a plain 1 GiB device-to-device copy (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def measured_traffic(w, split: int):
+    """Scaled HBM bytes per decode launch, or None if no counters match."""
+    import hashlib
+    src = "decode_mla.hip" if w.latent else "decode_gqa.hip"
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "decode_attention_fp8_amd",
+                        "csrc", src)
+    with open(path, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()[:16]
+    kib = TRAFFIC_KIB.get((w.name, split, src, digest))
+    if kib is None:
+        return None
+    return int(round((kib[0] * FETCH_FACTOR + kib[1] * WRITE_FACTOR) * 1024))
 
 
 def kv_bytes(w, elem_bytes: int) -> int:
@@ -217,13 +242,14 @@ def main():
         tflops = flop / (dec_ms * 1e-3) / 1e12
         rec["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK,
                            "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK, 4),
-                           "traffic": None, "kernel": "pkv_decode_attn (latent, bf16 MFMA)",
+                           "traffic": measured_traffic(w, split),
+                           "kernel": "pkv_decode_attn (latent, bf16 MFMA)",
                            "avg_ms": round(dec_ms, 5), "hbm_gbs": round(dec_gbs, 2),
                            "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4)}
     else:
         rec["roofline"] = {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                           "traffic": None, "kernel": "pkv_decode_attn (e4m3)",
+                           "traffic": measured_traffic(w, split), "kernel": "pkv_decode_attn (e4m3)",
                            "avg_ms": round(dec_ms, 5)}
     del run
     torch.cuda.empty_cache()
