@@ -48,7 +48,7 @@ constexpr float kTau = 8.0f;      // log2 headroom before a rescale
 constexpr float kMInit = -1e30f;  // running max before any token
 constexpr int kD = 128;
 constexpr int kG = 8;
-constexpr int kMaxUnitPages = 256;  // page ids staged per work unit
+constexpr int kMaxUnitPages = 64;  // pages per work unit (one per lane)
 
 __device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
 __device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
@@ -102,17 +102,17 @@ struct Ring<false> {
 };
 
 struct __attribute__((aligned(16))) WaveLds {
-  int32_t pages[kMaxUnitPages];  // physical page of each page of the unit
-  uint32_t ppair[8][kG];         // (p[t], p[t+4]) halves, t = 8*(pi>>2) + (pi&3)
-  float score[16][kG];           // scores of one group, for the rare max update
-  float m[kG];                   // running max per head (log2 domain)
-  float alpha[kG];               // rescale factor of the last max update
-  float l[kG];                   // final denominators
+  uint32_t ppair[2][8][kG];  // per group parity: (p[t], p[t+4]) halves, t = 8*(pi>>2) + (pi&3)
+  float score[16][kG];       // scores of one group, for the rare max update
+  float m[kG];               // running max per head (log2 domain)
+  float alpha[kG];           // rescale factor of the last max update
+  float l[kG];               // final denominators
 };
 
 template <bool kE4M3>
-__global__ void __launch_bounds__(64) decode_gqa_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) decode_gqa_kernel(DecodeParams p) {
   using R = Ring<kE4M3>;
+  constexpr int kVw = kE4M3 ? 2 : 4;  // V words per token row slice of a lane
   __shared__ WaveLds lds;
   __shared__ __attribute__((aligned(16))) uint8_t ring[R::kSlots * R::kGroupBytes];
   const int c = blockIdx.x;
@@ -165,11 +165,18 @@ __global__ void __launch_bounds__(64) decode_gqa_kernel(DecodeParams p) {
   const float qk_scale = (kE4M3 ? p.k_scale[g] : 1.0f) * p.sm_scale_log2;
   const float o_scale = kE4M3 ? p.v_scale[g] : 1.0f;
 
-  // page ids of the unit, staged in LDS
+  // The unit's pages (at most 64): lane j holds the byte offset of the
+  // (page j, kv head g) block, read back per group with readlane; bit j of
+  // valid says whether page id j is inside the pool (an invalid page is
+  // replaced by page 0 for the loads and its tokens are masked).
+  constexpr int64_t kElem = kE4M3 ? 1 : 2;
+  constexpr int kRow = kD * kElem;  // bytes per cache row
+  const int64_t head_stride = static_cast<int64_t>(P) * kRow;  // bytes of one (page, head) block
   const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_pages;
   const int first_page = t_begin >> log2P;
   const int n_unit_pages = (t_end - t_begin + P - 1) >> log2P;
-  for (int j = lane; j < n_unit_pages; j += 64) lds.pages[j] = bt[first_page + j];
+  int pg = -1;
+  if (lane < n_unit_pages) pg = bt[first_page + lane];
   if (lane < kG) lds.m[lane] = kMInit;
   // Every compiler-issued load must be complete before the first DMA, or its
   // own wait for them would also wait for the ring.
@@ -179,8 +186,13 @@ __global__ void __launch_bounds__(64) decode_gqa_kernel(DecodeParams p) {
     for (int k = 0; k < 16; k += 8)
       asm volatile("" : : "v"(qr[h][k]), "v"(qr[h][k + 1]), "v"(qr[h][k + 2]), "v"(qr[h][k + 3]),
                    "v"(qr[h][k + 4]), "v"(qr[h][k + 5]), "v"(qr[h][k + 6]), "v"(qr[h][k + 7]));
-  asm volatile("" : : "v"(qk_scale), "v"(o_scale));
+  asm volatile("" : : "v"(qk_scale), "v"(o_scale), "v"(pg));
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" : : : "memory");
+  const bool pg_ok = pg >= 0 && pg < p.num_pages;
+  const uint64_t valid = __ballot(pg_ok);
+  const int64_t blk_off = (static_cast<int64_t>(pg_ok ? pg : 0) * p.num_kv_heads + g) * head_stride;
+  const int off_lo = static_cast<int>(static_cast<uint32_t>(blk_off));
+  const int off_hi = static_cast<int>(static_cast<uint32_t>(static_cast<uint64_t>(blk_off) >> 32));
 
   float o[kG][8];
 #pragma unroll
@@ -190,9 +202,6 @@ __global__ void __launch_bounds__(64) decode_gqa_kernel(DecodeParams p) {
   float mq[2] = {kMInit, kMInit};
   float l[2] = {0.0f, 0.0f};
 
-  constexpr int64_t kElem = kE4M3 ? 1 : 2;
-  constexpr int kRow = kD * kElem;  // bytes per cache row
-  const int64_t head_stride = static_cast<int64_t>(P) * kRow;  // bytes of one (page, head) block
   const uint8_t* kpool = static_cast<const uint8_t*>(p.k_pool);
   const uint8_t* vpool = static_cast<const uint8_t*>(p.v_pool);
   const uint32_t ring0 = lds_addr(ring);
@@ -208,19 +217,18 @@ __global__ void __launch_bounds__(64) decode_gqa_kernel(DecodeParams p) {
   }
   const uint32_t voff = lane << 4;
 
-  auto page_valid = [&](int page) __attribute__((always_inline)) {
-    return page >= 0 && page < p.num_pages;
+  auto group_valid = [&](int gi) __attribute__((always_inline)) {
+    return ((valid >> ((gi << 4) >> log2P)) & 1u) != 0;
   };
-  // DMA of group gi into its ring slot; an invalid page reads page 0 instead
-  // (the group is skipped later) so every group costs the same loads.
+  // DMA of group gi into its ring slot.
   auto issue = [&](int gi) __attribute__((always_inline)) {
-    int page = __builtin_amdgcn_readfirstlane(lds.pages[(gi << 4) >> log2P]);
-    if (!page_valid(page)) page = 0;
-    const int row0 = (t_begin + (gi << 4)) & (P - 1);
-    const int64_t off = (static_cast<int64_t>(page) * p.num_kv_heads + g) * head_stride +
-                        static_cast<int64_t>(row0) * kRow;
-    const uint8_t* kb = kpool + off;
-    const uint8_t* vb = vpool + off;
+    const int j = (gi << 4) >> log2P;
+    const uint64_t off =
+        (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(off_hi, j))) << 32) |
+        static_cast<uint32_t>(__builtin_amdgcn_readlane(off_lo, j));
+    const uint32_t row_off = static_cast<uint32_t>(((gi << 4) & (P - 1)) * kRow);
+    const uint8_t* kb = kpool + off + row_off;
+    const uint8_t* vb = vpool + off + row_off;
     const uint32_t slot = ring0 + (gi % R::kSlots) * R::kGroupBytes;
     if constexpr (kE4M3) {
       dma16(slot, koff0, kb);
@@ -239,14 +247,10 @@ __global__ void __launch_bounds__(64) decode_gqa_kernel(DecodeParams p) {
     }
   };
 
-  auto compute = [&](int gi) __attribute__((always_inline)) {
-    const uint8_t* sk = ring + (gi % R::kSlots) * R::kGroupBytes;
-    const uint8_t* sv = sk + R::kGroupBytes / 2;
-    const int nv = min(16, t_end - (t_begin + (gi << 4)));
-    const bool full = nv == 16;
-
-    // ---- V rows tg + 4j, dims [8dg, 8dg+8) (issued first, used last)
-    uint32_t vw[4][kE4M3 ? 2 : 4];
+  // V rows tg + 4j, dims [8dg, 8dg+8) of group gi; rows past the context
+  // (last group) or of an invalid page are zeroed.
+  auto read_v = [&](int gi, uint32_t (&vw)[4][kVw]) __attribute__((always_inline)) {
+    const uint8_t* sv = ring + (gi % R::kSlots) * R::kGroupBytes + R::kGroupBytes / 2;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (kE4M3) {
@@ -257,8 +261,22 @@ __global__ void __launch_bounds__(64) decode_gqa_kernel(DecodeParams p) {
         vw[j][0] = x.x; vw[j][1] = x.y; vw[j][2] = x.z; vw[j][3] = x.w;
       }
     }
+    const int nv = group_valid(gi) ? min(16, t_end - (t_begin + (gi << 4))) : 0;
+    if (nv < 16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (tg + 4 * j >= nv)
+#pragma unroll
+          for (int k = 0; k < kVw; ++k) vw[j][k] = 0u;
+    }
+  };
 
-    // ---- partial scores of row tq over dims [32cq, 32cq+32), 8 heads
+  // QK^T and the softmax numerators of group gi (into ppair[gi & 1]); returns
+  // whether the running max moved (then alpha is in lds.alpha and o must be
+  // rescaled once the previous group's PV is done).
+  auto qk = [&](int gi) __attribute__((always_inline)) {
+    const uint8_t* sk = ring + (gi % R::kSlots) * R::kGroupBytes;
+    const int nv = group_valid(gi) ? min(16, t_end - (t_begin + (gi << 4))) : 0;
     float a[kG];
     {
       uint32_t kw[kE4M3 ? 8 : 16];
@@ -296,7 +314,7 @@ __global__ void __launch_bounds__(64) decode_gqa_kernel(DecodeParams p) {
       }
     }
 
-    // ---- reduce-scatter over the 4 chunk lanes
+    // reduce-scatter over the 4 chunk lanes
     float u[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -308,12 +326,13 @@ __global__ void __launch_bounds__(64) decode_gqa_kernel(DecodeParams p) {
     for (int j = 0; j < 2; ++j) {
       const auto r = __builtin_amdgcn_permlane16_swap(f2u(u[j]), f2u(u[j + 2]), false, false);
       const float sc = (u2f(r[0]) + u2f(r[1])) * qk_scale;
-      x[j] = full ? sc : ((my_tok < nv) ? sc : -INFINITY);
+      x[j] = (my_tok < nv) ? sc : -INFINITY;
     }
 
-    // ---- rare running-max update
+    // rare running-max update
     const bool over = (x[0] > mq[0] + kTau) || (x[1] > mq[1] + kTau);
-    if (__any(over)) {
+    const bool moved = __any(over);
+    if (moved) {
       lds.score[my_tok][my_h0] = x[0];
       lds.score[my_tok][my_h0 + 1] = x[1];
       __builtin_amdgcn_wave_barrier();
@@ -332,19 +351,13 @@ __global__ void __launch_bounds__(64) decode_gqa_kernel(DecodeParams p) {
         mq[j] = lds.m[my_h0 + j];
         l[j] *= lds.alpha[my_h0 + j];
       }
-#pragma unroll
-      for (int h = 0; h < kG; ++h) {
-        const float a = lds.alpha[h];
-#pragma unroll
-        for (int d = 0; d < 8; ++d) o[h][d] *= a;
-      }
     }
 
-    // ---- probabilities to LDS, pairs (t, t+4)
+    // probabilities to LDS, pairs (t, t+4)
     {
       const int pi = ((my_tok >> 3) << 2) | (my_tok & 3);
       const int half = (my_tok >> 2) & 1;
-      uint16_t* pp = reinterpret_cast<uint16_t*>(&lds.ppair[pi][0]);
+      uint16_t* pp = reinterpret_cast<uint16_t*>(&lds.ppair[gi & 1][pi][0]);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const float pr = __builtin_amdgcn_exp2f(x[j] - mq[j]);
@@ -364,21 +377,15 @@ __global__ void __launch_bounds__(64) decode_gqa_kernel(DecodeParams p) {
       }
     }
     __builtin_amdgcn_wave_barrier();
+    return moved;
+  };
 
-    // rows past the context in the last group hold stale bytes: zero them
-    if (!full) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (tg + 4 * j >= nv)
-#pragma unroll
-          for (int k = 0; k < (kE4M3 ? 2 : 4); ++k) vw[j][k] = 0u;
-    }
-
-    // ---- PV
+  // o += P V for group gi, from ppair[gi & 1] and its V words.
+  auto pv = [&](int gi, const uint32_t (&vw)[4][kVw]) __attribute__((always_inline)) {
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
-      const uint4 pa = *reinterpret_cast<const uint4*>(&lds.ppair[pr * 4 + tg][0]);
-      const uint4 pb = *reinterpret_cast<const uint4*>(&lds.ppair[pr * 4 + tg][4]);
+      const uint4 pa = *reinterpret_cast<const uint4*>(&lds.ppair[gi & 1][pr * 4 + tg][0]);
+      const uint4 pb = *reinterpret_cast<const uint4*>(&lds.ppair[gi & 1][pr * 4 + tg][4]);
       const uint32_t ph[kG] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
       uint32_t vp[8];
       const uint32_t* A = vw[2 * pr];      // token t
@@ -414,30 +421,51 @@ __global__ void __launch_bounds__(64) decode_gqa_kernel(DecodeParams p) {
                                                       false);
       }
     }
-    __builtin_amdgcn_wave_barrier();
   };
 
-  // ---- main loop: kSlots - 1 groups in flight while one is computed
-  constexpr int kAhead = R::kSlots - 1;
+  auto rescale_o = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int k = 0; k < kAhead; ++k)
-    if (k < n_groups) issue(k);
-  for (int gi = 0; gi < n_groups; ++gi) {
-    if (gi + kAhead < n_groups) issue(gi + kAhead);
-    // groups issued after gi decide how many loads may still be in flight
-    const int after = min(kAhead, n_groups - 1 - gi);
-    if constexpr (kAhead == 3) {
-      if (after == 3) wait_vm<3 * R::kDma>();
-      else if (after == 2) wait_vm<2 * R::kDma>();
-      else if (after == 1) wait_vm<R::kDma>();
-      else wait_vm<0>();
-    } else {
-      if (after == 2) wait_vm<2 * R::kDma>();
-      else if (after == 1) wait_vm<R::kDma>();
-      else wait_vm<0>();
+    for (int h = 0; h < kG; ++h) {
+      const float a = lds.alpha[h];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) o[h][d] *= a;
     }
-    const int page = __builtin_amdgcn_readfirstlane(lds.pages[(gi << 4) >> log2P]);
-    if (page_valid(page)) compute(gi);
+  };
+
+  // ---- main loop. Iteration gi computes QK^T of group gi, then P V of
+  // group gi - 1 (its probabilities went to LDS one iteration earlier), so no
+  // LDS round trip sits between the two halves. The ring starts full
+  // (groups 0 .. kSlots-1); iteration gi >= 1 refills the slot of group
+  // gi - 1 with group gi - 1 + kSlots once that group's V words are in
+  // registers. So before group gi is used, the loads of groups up to
+  // gi + kSlots - 1 (gi = 0) or gi + kSlots - 2 (gi >= 1) have been issued.
+#pragma unroll
+  for (int k = 0; k < R::kSlots; ++k)
+    if (k < n_groups) issue(k);
+  for (int gi = 0; gi <= n_groups; ++gi) {
+    const int after = min(gi == 0 ? R::kSlots - 1 : R::kSlots - 2, n_groups - 1 - gi);
+    if (after >= 3) wait_vm<3 * R::kDma>();
+    else if (after == 2) wait_vm<2 * R::kDma>();
+    else if (after == 1) wait_vm<R::kDma>();
+    else wait_vm<0>();
+    // (bf16 rows are twice as wide: their V words are read after QK^T so
+    // that they do not hold registers through it)
+    uint32_t vw[4][kVw];
+    if (kE4M3 && gi > 0) read_v(gi - 1, vw);
+    bool moved = false;
+    if (gi < n_groups) moved = qk(gi);
+    if (!kE4M3 && gi > 0) read_v(gi - 1, vw);
+    if (gi > 0) {
+      // the slot of group gi - 1 is free once its V words have arrived
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int k = 0; k < kVw; ++k) asm volatile("" : : "v"(vw[j][k]));
+      if (gi - 1 + R::kSlots < n_groups) issue(gi - 1 + R::kSlots);
+      pv(gi - 1, vw);
+    }
+    if (moved) rescale_o();
+    __builtin_amdgcn_wave_barrier();
   }
 
   // ---- finish: denominators per head, accumulators over the 4 token lanes

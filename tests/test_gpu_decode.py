@@ -98,7 +98,10 @@ def test_mla_shapes_ragged(kv, hq, lens, split):
 
 # ------------------------------------------------------------- edge cases
 @pytest.mark.parametrize("lens,P,split", [([1], 16, 16), ([16, 17, 15], 16, 16), ([1, 2, 3, 4], 64, 64),
-                                          ([300, 1, 257], 32, 96), ([5000, 33], 16, 256)])
+                                          ([300, 1, 257], 32, 96), ([5000, 33], 16, 256),
+                                          ([2100, 1024, 1023, 47], 16, 1024),
+                                          ([4096 + 640, 4096, 65], 64, 4096),
+                                          ([70, 33, 80], 16, 32)])
 @pytest.mark.parametrize("kv", ["fp8", "bf16"])
 def test_ragged_lengths_and_splits(lens, P, split, kv):
     w = W.custom(f"rag{len(lens)}_{P}", 77, lens, hq=8, hkv=2, dk=128, dv=128, page=P, split=split)
