@@ -1,9 +1,11 @@
 """Throughput of the FP8 paged decode step on one MI355X.
 
-A step is one pass of the whole hot path over a batch of decode requests,
-issued on torch's current stream:
+A step is one pass of the whole hot path over a batch of decode requests:
     pkv_verify -> pkv_append (one new token per request) -> pkv_decode_attn
     -> pkv_combine
+captured once as a HIP graph and replayed K times between two device
+synchronizations (wall clock); a separate eager pass times the decode kernel
+with events on the stream it is launched on.
 Default workload: the concurrency-sweep point at batch 64 (contexts uniform
 on [2048, 32768], 64 query / 8 KV heads, head dim 128, page 16, per-head
 e4m3 scales, tag check on). Inputs are built on the GPU before timing.
@@ -136,19 +138,45 @@ class Runner:
         pkv.pkv_combine(s.o_part, s.lse_part, self.lens, s.split_tokens, s.max_seq_len, abort,
                         s.out, s.lse)
 
+    def capture(self):
+        """The whole step as one HIP graph (the step's launches only)."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.one()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.one()
+        torch.cuda.synchronize()
+        return g
+
     def time(self, steps: int, warmup: int):
+        """(ms per step, decode kernel ms). Eager steps with events around the
+        decode launch give the kernel's own duration; the step time is K
+        replays of the captured step between two synchronizations."""
         torch = self.torch
         for _ in range(warmup):
             self.one()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(steps)]
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
         for e in evs:
             self.one(e)
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
         dec_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+        g = self.capture()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        del g
         return (t1 - t0) * 1e3 / steps, dec_ms
 
 

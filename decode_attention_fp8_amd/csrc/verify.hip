@@ -8,35 +8,60 @@
 // between thread groups), so it is its own launch whose flags the decode
 // reads later in stream order.
 //
-// One wave per request: lanes stride over the request's block-table entries
-// (coalesced 4-byte reads of the table and of the recorded tags, one random
-// 4-byte tag read each), then a wave-wide OR.
+// One 256-thread workgroup per request. Each thread takes entries
+// j = j0 + 256u + tid for u < 8 of every 2048-entry round: first all eight
+// block-table entries and recorded tags (coalesced, independent), then all
+// eight pool tags (random 4-byte reads, independent), so a round costs two
+// memory latencies whatever the request length. The workgroup ORs the
+// verdicts and one thread writes the flag; no atomics, no pre-cleared output.
 #include "common.h"
 
 namespace {
 
-__global__ void __launch_bounds__(256) verify_kernel(const uint32_t* __restrict__ page_tags,
-                                                     int32_t num_pages, int32_t page_size,
-                                                     const int32_t* __restrict__ block_table,
-                                                     const uint32_t* __restrict__ expected,
-                                                     const int32_t* __restrict__ seq_lens,
-                                                     int32_t batch, int32_t max_pages,
-                                                     uint8_t* __restrict__ abort_out) {
-  const int b = blockIdx.x * (blockDim.x / pkv::kWave) + threadIdx.x / pkv::kWave;
-  const int lane = threadIdx.x % pkv::kWave;
-  if (b >= batch) return;
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;
+
+__global__ void __launch_bounds__(kThreads) verify_kernel(const uint32_t* __restrict__ page_tags,
+                                                          int32_t num_pages, int32_t page_size,
+                                                          const int32_t* __restrict__ block_table,
+                                                          const uint32_t* __restrict__ expected,
+                                                          const int32_t* __restrict__ seq_lens,
+                                                          int32_t max_pages,
+                                                          uint8_t* __restrict__ abort_out) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
   const int32_t L = seq_lens[b];
   const int64_t need = L > 0 ? (static_cast<int64_t>(L) + page_size - 1) / page_size : 0;
-  bool bad = need > max_pages;
-  const int64_t n = bad ? max_pages : need;
+  // a request needing more pages than its row holds cannot be mapped
+  int bad = need > max_pages ? 1 : 0;
+  const int64_t n = bad ? 0 : need;
   const int32_t* row = block_table + static_cast<int64_t>(b) * max_pages;
   const uint32_t* exp = expected + static_cast<int64_t>(b) * max_pages;
-  for (int64_t j = lane; j < n && !bad; j += pkv::kWave) {
-    const int32_t pid = row[j];
-    bad = pid < 0 || pid >= num_pages || page_tags[pid] != exp[j];
+  for (int64_t j0 = 0; j0 < n; j0 += kThreads * kUnroll) {
+    int32_t pid[kUnroll];
+    uint32_t want[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t j = j0 + u * kThreads + tid;
+      pid[u] = 0;
+      want[u] = 0;
+      if (j < n) {
+        pid[u] = row[j];
+        want[u] = exp[j];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t j = j0 + u * kThreads + tid;
+      if (j < n) {
+        const bool in_pool = pid[u] >= 0 && pid[u] < num_pages;
+        const uint32_t have = in_pool ? page_tags[pid[u]] : 0u;
+        bad |= (!in_pool || have != want[u]) ? 1 : 0;
+      }
+    }
   }
-  const bool any = __any(bad);
-  if (lane == 0) abort_out[b] = any ? 1 : 0;
+  bad = __syncthreads_or(bad);
+  if (tid == 0) abort_out[b] = bad ? 1 : 0;
 }
 
 }  // namespace
@@ -50,10 +75,8 @@ extern "C" int pkv_verify(const pkv_cache* cache, const int32_t* block_table,
   if (!block_table || !expected_tags || !seq_lens || !abort_out || batch < 0 || max_pages < 1)
     return PKV_EINVAL;
   if (batch == 0) return PKV_OK;
-  constexpr int kWavesPerBlock = 4;
-  const int blocks = static_cast<int>(pkv::cdiv(batch, kWavesPerBlock));
-  verify_kernel<<<blocks, kWavesPerBlock * pkv::kWave, 0, stream>>>(
-      cache->page_tags, cache->num_pages, cache->page_size, block_table, expected_tags, seq_lens,
-      batch, max_pages, abort_out);
+  verify_kernel<<<batch, kThreads, 0, stream>>>(cache->page_tags, cache->num_pages,
+                                                cache->page_size, block_table, expected_tags,
+                                                seq_lens, max_pages, abort_out);
   return pkv::launch_status();
 }

@@ -26,6 +26,11 @@ def verify(page_tags, block_table, expected_tags, seq_lens, page_size) -> np.nda
     out = np.zeros(len(lens), dtype=np.uint8)
     for b in range(len(lens)):
         n = -(-int(lens[b]) // page_size) if lens[b] > 0 else 0
+        if n > bt.shape[1]:
+            # tokens beyond the row have no page at all: unmapped, like an
+            # id outside the pool
+            out[b] = 1
+            continue
         for j in range(n):
             pid = int(bt[b, j])
             if pid < 0 or pid >= num_pages or int(page_tags[pid]) != int(exp[b, j]):

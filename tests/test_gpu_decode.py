@@ -179,3 +179,35 @@ def test_fp8_close_to_bf16_reported():
     b = State(w, "bf16").run().float()
     err = (a - b).abs().max().item()
     assert math.isfinite(err) and err < 0.1
+
+
+@pytest.mark.parametrize("make", [W.tiny, lambda: W.sweep(8)])
+def test_graph_replays_match_eager_step(make):
+    """The step captured as a HIP graph and replayed (with eager work and
+    synchronisation between replays) gives the eager step's bits every time."""
+    w = make()
+    st = State(w, "fp8")
+    args = (st.q, st.block_table, st.expected, st.seq_lens, w.sm_scale, st.new_k, st.new_v,
+            st.new_slot, st.new_req)
+    eager = st.step.run(*args).clone()
+    eager_lse = st.step.lse.clone()
+    eager_abort = st.step.abort.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st.step.run(*args)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.step.run(*args)
+    for _ in range(3):
+        st.step.out.zero_()
+        st.step.lse.fill_(1.0)
+        st.step.abort.fill_(7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.step.out.view(torch.int16), eager.view(torch.int16))
+        assert torch.equal(st.step.lse.view(torch.int32), eager_lse.view(torch.int32))
+        assert torch.equal(st.step.abort, eager_abort)

@@ -188,3 +188,29 @@ def test_verify_random_corruptions():
                 tags[int(rng.integers(0, w.num_pages))] += 1
         ref = verify.verify(tags, bt, exp, w.seq_lens, w.page_size)
         assert np.array_equal(_gpu_flags(w, bt, exp, tags), ref), trial
+
+
+def test_verify_long_rows_across_rounds():
+    """Rows of 5000 entries (more than two 2048-entry rounds of the kernel),
+    corruptions exactly at round edges, and a request longer than its row."""
+    P = 16
+    n_ent = 5000
+    B = 9
+    rng = np.random.default_rng(5)
+    num_pages = B * n_ent + 7
+    perm = rng.permutation(num_pages)[:B * n_ent].reshape(B, n_ent).astype(np.int32)
+    tags = rng.integers(0, 2**32, size=num_pages, dtype=np.uint64).astype(np.uint32)
+    exp = tags[perm].copy()
+    lens = np.full(B, n_ent * P, dtype=np.int32)
+    edges = [0, 2047, 2048, 4095, 4096, 4999]
+    for b, j in enumerate(edges):
+        exp[b, j] ^= 0x80000000
+    lens[6] = n_ent * P - 3           # clean, ragged last page
+    lens[7] = n_ent * P + 1           # needs one entry more than the row holds
+    bt = perm.copy()
+    bt[8, 4999] = num_pages           # out-of-pool id in the last entry
+    w = W.custom("vlong", 4242, [16] * B, hq=1, hkv=1, dk=16, dv=16, page=P, pool_pages=num_pages)
+    w.seq_lens[:] = lens
+    ref = verify.verify(tags, bt, exp, lens, P)
+    assert ref.tolist() == [1] * 6 + [0, 1, 1]
+    assert np.array_equal(_gpu_flags(w, bt, exp, tags), ref)

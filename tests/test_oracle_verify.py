@@ -77,3 +77,13 @@ def test_random_against_set_formulation():
             used = set(range(-(-int(lens[b]) // P)))
             bad = {j for j in used if not (0 <= bt[b, j] < n_pages) or tags[bt[b, j]] != exp[b, j]}
             assert got[b] == (1 if bad else 0)
+
+
+def test_request_longer_than_its_row_is_aborted():
+    """Reading of the section's rule: tokens beyond the block-table row have no
+    page, like an id outside the pool, so the request is aborted."""
+    tags = np.arange(8, dtype=np.uint32)
+    bt = np.array([[0, 1], [2, 3]])
+    exp = tags[bt]
+    got = verify.verify(tags, bt, exp, np.array([8, 9]), 4)
+    assert got.tolist() == [0, 1]
