@@ -395,6 +395,302 @@ __global__ void __launch_bounds__(256) decode_mla_kernel(DecodeParams p, int n_s
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide variant for an e4m3 cache and query heads in multiples of 128: one
+// workgroup of 4 waves takes all 128 heads of a (request, split), each wave
+// 32 heads, so every cached byte is converted and read from LDS by 4 waves
+// instead of 8. MFMA 32x32x16 (bf16 in, fp32 out):
+//   A lane l: row l%32, k 8(l/32)..+7;  B lane l: column l%32, k 8(l/32)..+7;
+//   D lane l, element i: row 8(i/4) + 4(l/32) + i%4, column l%32.
+// S^T = K Q^T per 32-token block (M = tokens, N = the wave's 32 heads, 36
+// k-steps of 16 dims), so a lane holds the scores of one head (l%32) for
+// tokens {8u + 4(l/32) + r}; those are exactly the A operand of P V (M =
+// heads, k = tokens) when the V operand is read in the same token order with
+// ds_read_tr8_b64. The 32 x 512 accumulators of a wave live in the
+// accumulation registers.
+//
+// Tile layout in LDS: 16-byte chunk c of row r at position c ^ ((r >> 2) & 3)
+// of the row, which puts any 16 consecutive rows of one chunk (K operand
+// reads) and the 8 rows x 2 half-chunks of a transposing V read on distinct
+// bank groups. The ring holds 4 tiles; tile t + 3 is loaded into the buffer
+// of tile t - 1 right after the barrier that opens tile t, so one barrier per
+// tile suffices.
+//
+// Work unit order: blockIdx.y counts splits from the end of each request
+// downwards (the first units dispatched are the ones far from the end,
+// which are full), so the short last splits run last and fill the tail;
+// the request index is rotated by blockIdx.y so that one request's units
+// spread over all XCDs.
+constexpr int kWideHeads = 32;
+constexpr float kWideTau = 60.0f;  // log2 headroom of the reference max
+constexpr int kWideBufs = 2;
+constexpr int kWideTileBytes = kTile * kDk;          // 36 KB
+constexpr int kWideDma = kWideTileBytes / 1024;      // 36 loads of 1 KB
+constexpr int kWideMine = kWideDma / 4;              // 9 per wave
+
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ int wide_pos(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+__global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p, int n_splits,
+                                                                 int head_groups) {
+  static_assert((kWideBufs - 2) * kWideMine <= 63, "vmcnt counts to 63");
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[kWideBufs * kWideTileBytes];
+  __shared__ int32_t pages[kMaxUnitTiles];
+  __shared__ float l_s[4][kWideHeads];
+  __shared__ int vote[2][4];
+
+  // Consecutive workgroup ids go to the 8 XCDs in turn, so the (request,
+  // head group) index is rotated by the split row: the units of one request
+  // land on different XCDs instead of all on XCD (index mod 8).
+  const int bx = static_cast<int>((blockIdx.x + blockIdx.y) % gridDim.x);
+  const int b = bx / head_groups;
+  const int hg = bx - b * head_groups;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5;     // which half of the k range this lane supplies
+  const int col = lane & 31;    // head (QK, D of S^T) or dim (PV, D of O)
+
+  if (p.abort_flags && p.abort_flags[b]) return;
+  const int L = p.seq_lens[b];
+  if (L > p.max_seq_len || L <= 0) return;
+  const int n_b = (L + p.split_tokens - 1) / p.split_tokens;
+  const int c = n_b - n_splits + static_cast<int>(blockIdx.y);
+  if (c < 0) return;
+  const int t_begin = c * p.split_tokens;
+  const int t_end = min(L, t_begin + p.split_tokens);
+  const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
+  const int h_base = hg * 128 + wave * kWideHeads;
+
+  // q as B operands: k-step ks covers dims 32(ks/2) + 16hh + 8(ks%2) .. +7 for
+  // this lane's head, so one 16-byte K read serves two k-steps
+  bf16x8_t qf[36];
+  {
+    const int qi = b * p.num_q_heads + h_base + col;  // < 2^31 (checked on the host)
+    const uint16_t* qrow = p.q + static_cast<int64_t>(qi) * kDk;
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks)
+      qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * (ks >> 1) + 16 * hh + 8 * (ks & 1));
+  }
+  const float qk_scale = p.k_scale[0] * p.sm_scale_log2;
+  const float o_scale = p.v_scale[0];
+
+  const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_pages;
+  const int first_page = t_begin / kTile;
+  for (int j = tid; j < n_tiles; j += 256) pages[j] = bt[first_page + j];
+#pragma unroll
+  for (int ks = 0; ks < 36; ++ks) asm volatile("" : : "v"(qf[ks]));
+  asm volatile("" : : "s"(qk_scale), "s"(o_scale));
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : : : "memory");
+
+  // per-lane source of this wave's load i of a tile: load k = wave + 4i fills
+  // LDS chunks 64k .. 64k+63, chunk q = row q/36, position q%36
+  auto doff = [&](int i) __attribute__((always_inline)) {
+    const int q = 64 * (wave + 4 * i) + lane;
+    const int r = q / 36;
+    const int pp = q - 36 * r;
+    return static_cast<uint32_t>(r * kDk + wide_pos(r, pp) * 16);
+  };
+  const uint8_t* kpool = static_cast<const uint8_t*>(p.k_pool);
+  const uint32_t tiles0 = lds_addr(tiles);
+  auto page_of = [&](int t) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane(pages[t]);
+  };
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    int page = page_of(t);
+    if (page < 0 || page >= p.num_pages) page = 0;  // loaded but never used
+    const uint8_t* base = kpool + static_cast<int64_t>(page) * kWideTileBytes;
+    const uint32_t buf = tiles0 + (t % kWideBufs) * kWideTileBytes;
+#pragma unroll
+    for (int i = 0; i < kWideMine; ++i) dma16(buf + 1024 * (wave + 4 * i), doff(i), base);
+  };
+
+  floatx16_t O[16];
+#pragma unroll
+  for (int nb = 0; nb < 16; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[nb][i] = 0.f;
+  // Scores are taken relative to a reference max m (log2 domain) that is set
+  // by the first tile and never moves by less than kWideTau: p = 2^(s - m)
+  // stays below 2^kWideTau, far inside bf16 and fp32 range, so O never has to
+  // be rescaled inside the loop. A score above m + kWideTau (not reachable by
+  // attention scores in practice) restarts the unit with the larger m.
+  float m = kMInit;
+  float l = 0.f;
+  const int a16 = (lane >> 4) & 1;
+  const int jj = lane & 15;
+  const int kk = jj >> 1;
+
+  // Per-lane LDS offsets. The swizzle term (r >> 2) & 3 of every row a lane
+  // reads is the same in both halves and both k-steps of a half (row offsets
+  // 32mb + 16u are multiples of 16), so four bases cover all reads:
+  // K operand, chunk 2j + hh of row 32mb + col, sits at position
+  // 4(j/2) + ((2(j%2) + hh) ^ sw): base koff[j%2] + 64(j/2) + 32mb rows;
+  // V operand of k-step (mb, u): the 16 lanes of a group address rows
+  // T[jj/2] of the step, half-chunk jj%2 of chunk 2nb + a16, at position
+  // 4(nb/2) + ((2(nb%2) + a16) ^ sw): base voff[nb%2] + 64(nb/2) + (32mb + 16u) rows.
+  // Lane i of a group then holds dim 32nb + 16a16 + i of the step's 8 tokens
+  // in P's order.
+  uint32_t koff[2], voff[2];
+  {
+    const int rk = col;
+    const int rv = 8 * (kk >> 2) + 4 * hh + (kk & 3);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      koff[x] = static_cast<uint32_t>(rk * kDk + wide_pos(rk, 2 * x + hh) * 16);
+      voff[x] = static_cast<uint32_t>(rv * kDk + wide_pos(rv, 2 * x + a16) * 16 + 8 * (jj & 1));
+    }
+  }
+  bool jump = false;  // a score went above the reference max by more than kWideTau
+
+  // One 32-token half (mb) of a tile: S^T, numerators, O += P V.
+  auto half_tile = [&](const uint8_t* buf, int mb, int nv) __attribute__((always_inline)) {
+    floatx16_t st;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st[i] = 0.f;
+    const uint8_t* kb0 = buf + 32 * mb * kDk + koff[0];
+    const uint8_t* kb1 = buf + 32 * mb * kDk + koff[1];
+    auto k_read = [&](int j) __attribute__((always_inline)) {
+      return *reinterpret_cast<const uint4*>(((j & 1) ? kb1 : kb0) + 64 * (j >> 1));
+    };
+    constexpr int kKAhead = 3;  // 16-byte K reads in flight ahead of their MFMAs
+    uint4 kq[kKAhead];
+#pragma unroll
+    for (int a = 0; a < kKAhead; ++a) kq[a] = k_read(a);
+#pragma unroll
+    for (int j = 0; j < 18; ++j) {
+      const uint4 cur = kq[j % kKAhead];
+      if (j + kKAhead < 18) kq[j % kKAhead] = k_read(j + kKAhead);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(cur.x, cur.y), qf[2 * j], st, 0, 0, 0);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(cur.z, cur.w), qf[2 * j + 1], st, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // scores: st[i] is token 32mb + 8(i/4) + 4hh + i%4 of head h_base + col
+    float lm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float v = st[i] * qk_scale;
+      st[i] = (32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3) < nv) ? v : -INFINITY;
+      lm = fmaxf(lm, st[i]);
+    }
+    if (m == kMInit) {  // first scores of the unit set the reference max
+      lm = fmaxf(lm, __shfl_xor(lm, 32));
+      m = lm > -INFINITY ? lm : kMInit;
+    } else if (lm > m + kWideTau) {
+      jump = true;
+      m = lm;  // raised; the unit is redone with it (see the pipeline)
+    }
+    // numerators as A operands of the two PV k-steps of this half:
+    // k-step u takes st[8u .. 8u+7] (tokens 32mb + 16u + {0..3, 8..11} + 4hh)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float pr[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        pr[k] = __builtin_amdgcn_exp2f(st[8 * u + k] - m);
+        l += pr[k];
+      }
+      bf16x8_t pf;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) pf[k] = static_cast<__bf16>(pr[k]);
+      const uint8_t* vb0 = buf + (32 * mb + 16 * u) * kDk + voff[0];
+      const uint8_t* vb1 = buf + (32 * mb + 16 * u) * kDk + voff[1];
+      auto v_read = [&](int nb) __attribute__((always_inline)) {
+        const uint8_t* ad = ((nb & 1) ? vb1 : vb0) + 64 * (nb >> 1);
+        const v2i_t r8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)ad);
+        return make_uint2(static_cast<uint32_t>(r8[0]), static_cast<uint32_t>(r8[1]));
+      };
+      constexpr int kVAhead = 6;  // tr8 reads in flight ahead of their MFMA
+      uint2 vq[kVAhead];
+#pragma unroll
+      for (int a = 0; a < kVAhead; ++a) vq[a] = v_read(a);
+#pragma unroll
+      for (int nb = 0; nb < 16; ++nb) {
+        const uint2 cur = vq[nb % kVAhead];
+        if (nb + kVAhead < 16) vq[nb % kVAhead] = v_read(nb + kVAhead);
+        O[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf, fp8x8_to_bf16(cur.x, cur.y), O[nb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // ---- tile pipeline: kWideBufs - 1 tiles loaded ahead. A unit in which
+  // some score jumped (see above) is redone from tile 0 with the raised
+  // reference maxima once every wave has voted.
+  bool done = false;
+  while (!done) {
+#pragma unroll
+    for (int t = 0; t < kWideBufs - 1; ++t)
+      if (t < n_tiles) issue(t);
+    for (int t = 0; t < n_tiles; ++t) {
+      const int after = min(kWideBufs - 2, n_tiles - 1 - t);
+      if (after >= 2) wait_vm<2 * kWideMine>();
+      else if (after == 1) wait_vm<kWideMine>();
+      else wait_vm<0>();
+      wg_barrier();  // tile t is in LDS for every wave; every wave is done with tile t - 1
+      if (t + kWideBufs - 1 < n_tiles) issue(t + kWideBufs - 1);
+      const int page = page_of(t);
+      const int nv = min(kTile, t_end - (t_begin + kTile * t));
+      if (page >= 0 && page < p.num_pages) {
+        uint8_t* buf = tiles + (t % kWideBufs) * kWideTileBytes;
+        if (nv < kTile) {
+          // rows past the context hold stale bytes; their V part must be finite
+          const int n16 = (kTile - nv) * (kDk / 16);
+          for (int i = tid; i < n16; i += 256)
+            *reinterpret_cast<uint4*>(buf + nv * kDk + 16 * i) = make_uint4(0u, 0u, 0u, 0u);
+          wg_barrier();
+        }
+#pragma unroll 1
+        for (int mb = 0; mb < 2; ++mb) half_tile(buf, mb, nv);
+      }
+    }
+    if (lane == 0) vote[0][wave] = jump ? 1 : 0;
+    wg_barrier();
+    done = (vote[0][0] | vote[0][1] | vote[0][2] | vote[0][3]) == 0;
+    if (!done) {
+      // drain the loads in flight (none: the last tile waited for all) and
+      // start over; each head keeps its raised reference max
+      wait_vm<0>();
+      jump = false;
+      l = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 16; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) O[nb][i] = 0.f;
+    }
+    wg_barrier();  // the vote has been read before it is written again
+  }
+
+  // ---- finish: denominators per head, then the normalised partial rows.
+  // Lane indices and output addresses are formed afresh here (mbcnt gives
+  // the lane) so that nothing from the prologue stays alive through the loop.
+  const int lane_e = static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+  const int col_e = lane_e & 31, hh_e = lane_e >> 5;
+  l += __shfl_xor(l, 32);
+  if (hh_e == 0) l_s[wave][col_e] = l;
+  __builtin_amdgcn_wave_barrier();
+  int b_out = b, h_out = h_base, c_out = c;
+  asm volatile("" : "+s"(b_out), "+s"(h_out), "+s"(c_out));
+  const int bh0 = b_out * p.num_q_heads + h_out;
+  if (hh_e == 0)
+    p.lse_part[static_cast<int64_t>(bh0 + col_e) * p.max_splits + c_out] =
+        l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+  float f[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float lh = l_s[wave][8 * (i >> 2) + 4 * hh_e + (i & 3)];
+    f[i] = lh > 0.0f ? o_scale / lh : 0.0f;
+  }
+  float* dst0 = p.o_part + (static_cast<int64_t>(bh0 + 4 * hh_e) * p.max_splits + c_out) * kDv + col_e;
+  const int64_t head_stride = static_cast<int64_t>(p.max_splits) * kDv;
+#pragma unroll
+  for (int nb = 0; nb < 16; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      dst0[(8 * (i >> 2) + (i & 3)) * head_stride + 32 * nb] = O[nb][i] * f[i];
+}
+
 }  // namespace
 
 bool mla_fast_path_supported(int dk, int dv, int num_kv_heads, int num_q_heads, int page_size,
@@ -405,6 +701,12 @@ bool mla_fast_path_supported(int dk, int dv, int num_kv_heads, int num_q_heads, 
 
 int launch_decode_mla(const DecodeParams& p, bool e4m3, int n_split_blocks, int batch,
                       hipStream_t stream) {
+  if (e4m3 && p.num_q_heads % 128 == 0 && n_split_blocks <= 65535) {
+    const int head_groups = p.num_q_heads / 128;
+    const dim3 grid(batch * head_groups, n_split_blocks);
+    decode_mla_wide_kernel<<<grid, 256, 0, stream>>>(p, n_split_blocks, head_groups);
+    return pkv::launch_status();
+  }
   const int head_groups = p.num_q_heads / 64;
   const int n_x = (n_split_blocks + 7) / 8 * 8 * head_groups;
   const dim3 grid(n_x, batch);

@@ -88,7 +88,7 @@ def test_mla_sampled_including_aborted(kv):
 
 @pytest.mark.parametrize("kv", ["fp8", "bf16"])
 @pytest.mark.parametrize("hq,lens,split", [(64, [1, 63, 64, 65, 700], 64), (128, [129, 2000], 512),
-                                           (128, [4100, 33], 1024)])
+                                           (128, [4100, 33], 1024), (256, [700, 64, 3000], 2048)])
 def test_mla_shapes_ragged(kv, hq, lens, split):
     w = W.custom(f"mla{hq}", 81, lens, hq=hq, hkv=1, dk=576, dv=512, page=64, latent=True,
                  split=split, sm_scale=1 / math.sqrt(576))
@@ -211,3 +211,37 @@ def test_graph_replays_match_eager_step(make):
         assert torch.equal(st.step.out.view(torch.int16), eager.view(torch.int16))
         assert torch.equal(st.step.lse.view(torch.int32), eager_lse.view(torch.int32))
         assert torch.equal(st.step.abort, eager_abort)
+
+
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+def test_mla_score_jump_far_above_the_first_tile(kv):
+    """Keys of a later page aligned with head 0's query push its score about
+    190 (log2 units) above every score of the first page: the running max
+    must move (or the unit restart) without losing accuracy."""
+    from oracle import attention
+    hq, dk, dv, P, L = 128, 576, 512, 64, 256
+    rng = np.random.default_rng(9)
+    q = torch.from_numpy(rng.standard_normal((1, hq, dk)).astype(np.float32)).to(torch.bfloat16)
+    sign = np.sign(q[0, 0].float().numpy())
+    sign[sign == 0] = 1
+    vals = rng.standard_normal((L, dk)).astype(np.float32) * 0.01   # small keys ...
+    vals[128:192] = 7.0 * sign                                        # ... except page 2
+    scale = np.float32(7.0 / 448.0)
+    cache = pkv.allocate_cache(4, 1, P, dk, dv, kv, latent=True, device=dev)
+    if kv == "fp8":
+        codes = e4m3.encode((vals / scale).astype(np.float32))
+        k_hat = e4m3.DECODE[codes] * np.float64(scale)
+        cache.k_pool[:, 0] = torch.from_numpy(codes.reshape(4, P, dk)).to(dev)
+        cache.k_scale.fill_(float(scale))
+        cache.v_scale = cache.k_scale
+    else:
+        kb = torch.from_numpy(vals).to(torch.bfloat16)
+        k_hat = kb.double().numpy()
+        cache.k_pool[:, 0] = kb.view(4, P, dk).to(dev)
+    bt = torch.arange(4, dtype=torch.int32, device=dev).view(1, 4)
+    lens = torch.tensor([L], dtype=torch.int32, device=dev)
+    sm = 1 / math.sqrt(dk)
+    ds = pkv.DecodeStep(cache, hq, 1, L, 256, verify=False)
+    out = ds.attend(q.to(dev), bt, lens, sm, None).float().cpu().numpy()[0]
+    ref, _ = attention.attend(q[0].double().numpy(), k_hat[:, None, :], k_hat[:, None, :dv], sm)
+    assert_close(out, ref, f"mla score jump {kv}")
