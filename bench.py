@@ -118,7 +118,8 @@ class Runner:
         self.q = w.q_values(dev)
         self.cache = c
         self.step = pkv.DecodeStep(c, w.num_q_heads, w.batch, int(w.seq_lens.max()),
-                                   split or w.split_tokens, verify, dev)
+                                   split or w.split_tokens, verify, dev,
+                                   total_tokens=w.total_tokens)
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
 
@@ -282,7 +283,7 @@ def main():
     del run
     torch.cuda.empty_cache()
     if not args.no_bf16:
-        rb = Runner(w, "bf16", split)
+        rb = Runner(w, "bf16", args.split or None)  # its own suggested split
         ms_b, dec_b = rb.time(args.steps, args.warmup)
         del rb
         torch.cuda.empty_cache()

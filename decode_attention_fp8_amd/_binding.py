@@ -51,7 +51,7 @@ def _load() -> ctypes.CDLL:
         "pkv_verify": (I32, [CP, P, P, P, I32, I32, P, P]),
         "pkv_decode_attn": (I32, [CP, P, I32, P, P, I32, I32, I32, P, F, I32, I32, P, P, P]),
         "pkv_combine": (I32, [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P]),
-        "pkv_suggest_split": (I32, [I32, I32, I32, I32]),
+        "pkv_suggest_split": (I32, [CP, I32, I32, I64, I32]),
         "pkv_strerror": (ctypes.c_char_p, [I32]),
         "pkv_version": (I32, []),
     }
@@ -73,8 +73,14 @@ def pkv_version() -> int:
     return int(_lib.pkv_version())
 
 
-def pkv_suggest_split(batch: int, max_seq_len: int, num_kv_heads: int, page_size: int) -> int:
-    r = int(_lib.pkv_suggest_split(batch, max_seq_len, num_kv_heads, page_size))
+def pkv_suggest_split(cache: Cache, num_q_heads: int, batch: int, total_tokens: int,
+                      max_seq_len: int) -> int:
+    # only the geometry is read; v_pool's NULL-ness marks the latent layout
+    cs = PkvCacheStruct(None, None if cache.v_pool is None else 1, cache.dtype, cache.num_pages,
+                        cache.page_size, cache.num_kv_heads, cache.head_dim_k, cache.head_dim_v,
+                        None, None, None)
+    r = int(_lib.pkv_suggest_split(ctypes.byref(cs), num_q_heads, batch, int(total_tokens),
+                                   max_seq_len))
     if r < 0:
         raise PkvError("pkv_suggest_split", r)
     return r

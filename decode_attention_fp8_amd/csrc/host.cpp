@@ -17,22 +17,44 @@ extern "C" const char* pkv_strerror(int32_t status) {
 
 extern "C" int32_t pkv_version(void) { return 100; }  // 0.1.0
 
-// Enough (request, kv head, split) units to give every compute unit several
-// single-wave workgroups (256 CUs x 8 resident waves, about 8 units each),
-// but splits of 128..512 tokens: shorter ones spend more on partial rows
-// (one per query head per split) and on per-unit set-up than they gain in
-// balance; longer ones leave the last units of long requests running alone.
-extern "C" int32_t pkv_suggest_split(int32_t batch, int32_t max_seq_len, int32_t num_kv_heads,
-                                     int32_t page_size) {
-  if (batch < 1 || max_seq_len < 1 || num_kv_heads < 1 ||
-      (page_size != 16 && page_size != 32 && page_size != 64))
+// Split planning: a longer split writes fewer partial rows (one per query
+// head and split, read again by the merge) and repeats the per-unit set-up
+// less often; a shorter one gives more units to spread over 256 compute
+// units. Measured on MI355X: the grouped-query kernel is flat between 256 and
+// 512 at batch 64 and best at 128..256 for batch 1..8; the wide latent
+// kernel keeps gaining up to 4096-token splits at batch 64.
+extern "C" int32_t pkv_suggest_split(const pkv_cache* cache, int32_t num_q_heads, int32_t batch,
+                                     int64_t total_tokens, int32_t max_seq_len) {
+  if (!cache || batch < 1 || max_seq_len < 1 || num_q_heads < 1 || cache->num_kv_heads < 1 ||
+      num_q_heads % cache->num_kv_heads || total_tokens < 0 ||
+      (cache->page_size != 16 && cache->page_size != 32 && cache->page_size != 64))
     return PKV_EINVAL;
-  constexpr int64_t kTargetUnits = 16384;
-  const int64_t work = static_cast<int64_t>(batch) * num_kv_heads * max_seq_len;
-  int64_t s = 128;
-  while (s < 512 && work / s > kTargetUnits) s *= 2;
-  s = std::max<int64_t>(s, page_size);
-  const int64_t whole = (static_cast<int64_t>(max_seq_len) + page_size - 1) / page_size * page_size;
+  const int64_t P = cache->page_size;
+  const int64_t total = total_tokens > 0 ? total_tokens : static_cast<int64_t>(batch) * max_seq_len;
+  const int64_t whole = (static_cast<int64_t>(max_seq_len) + P - 1) / P * P;
+  // work units of split s: one per (request, split) and head block
+  auto units = [&](int64_t s, int64_t blocks) { return blocks * (total / s + batch / 2 + 1); };
+  const bool latent = cache->v_pool == nullptr;
+  const int G = num_q_heads / cache->num_kv_heads;
+  int64_t s;
+  if (latent && cache->dtype == PKV_KV_E4M3 && cache->head_dim_k == 576 &&
+      cache->head_dim_v == 512 && cache->num_kv_heads == 1 && P == 64 && num_q_heads % 128 == 0) {
+    // wide latent kernel: one workgroup per compute unit and unit; the
+    // longest split that still gives about one unit per compute unit (7/8)
+    s = 4096;
+    while (s > P && units(s, num_q_heads / 128) < 224) s /= 2;
+  } else if (!latent && cache->head_dim_k == 128 && cache->head_dim_v == 128 && G == 8) {
+    // grouped-query kernel: single-wave units, two per SIMD; splits of
+    // 128 .. 512 tokens, the longest giving 4096 units or more
+    s = 512;
+    while (s > 128 && units(s, cache->num_kv_heads) < 4096) s /= 2;
+  } else {
+    constexpr int64_t kTargetUnits = 16384;
+    const int64_t work = static_cast<int64_t>(batch) * cache->num_kv_heads * max_seq_len;
+    s = 128;
+    while (s < 512 && work / s > kTargetUnits) s *= 2;
+  }
+  s = std::max<int64_t>(s, P);
   s = std::min<int64_t>(s, whole);
   return static_cast<int32_t>(s);
 }

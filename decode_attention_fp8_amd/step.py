@@ -43,13 +43,16 @@ class DecodeStep:
     """Output and scratch buffers of a decode step for a fixed batch shape."""
 
     def __init__(self, cache: Cache, num_q_heads: int, batch: int, max_seq_len: int,
-                 split_tokens: int | None = None, verify: bool = True, device="cuda"):
+                 split_tokens: int | None = None, verify: bool = True, device="cuda",
+                 total_tokens: int = 0):
+        """total_tokens (the sum of the requests' lengths, 0 if unknown) only
+        informs the split the library suggests when split_tokens is None."""
         self.cache = cache
         self.num_q_heads = num_q_heads
         self.batch = batch
         self.max_seq_len = max_seq_len
         self.split_tokens = split_tokens or pkv_suggest_split(
-            batch, max_seq_len, cache.num_kv_heads, cache.page_size)
+            cache, num_q_heads, batch, total_tokens, max_seq_len)
         self.max_splits = max(1, -(-max_seq_len // self.split_tokens))
         dv = cache.head_dim_v
         self.o_part = torch.empty((batch, num_q_heads, self.max_splits, dv), dtype=torch.float32,

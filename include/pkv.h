@@ -222,13 +222,21 @@ int pkv_combine(const float* o_part, const float* lse_part,
                 float* lse_out, hipStream_t stream);
 
 /*
- * Host helper: a split size (multiple of page_size) giving enough
- * independent work units to fill the GPU for this batch and context,
- * without cutting splits so short that the merge traffic matters.
- * Returns a positive token count, or PKV_EINVAL.
+ * Host helper: a split size for pkv_decode_attn on this cache and batch.
+ *   num_q_heads   query heads of the batch (as passed to pkv_decode_attn)
+ *   batch         requests in the batch
+ *   total_tokens  sum of the requests' lengths (as in seq_lens), or 0 if
+ *                 unknown (then batch * max_seq_len is assumed)
+ *   max_seq_len   longest request
+ * The result is a multiple of page_size, chosen for the kernel that will
+ * run: as long as possible (fewer partial rows to write and merge) while the
+ * batch still splits into enough work units to occupy every compute unit.
+ * Only the cache's geometry (dtype, page size, heads, dims, latent layout)
+ * is read; no pointer in it is used. Returns a positive token count, or
+ * PKV_EINVAL.
  */
-int32_t pkv_suggest_split(int32_t batch, int32_t max_seq_len,
-                          int32_t num_kv_heads, int32_t page_size);
+int32_t pkv_suggest_split(const pkv_cache* cache, int32_t num_q_heads, int32_t batch,
+                          int64_t total_tokens, int32_t max_seq_len);
 
 /* Host helper: a static string naming a status code. */
 const char* pkv_strerror(int32_t status);

@@ -38,7 +38,7 @@ class State:
         self.max_seq_len = int(w.seq_lens.max())
         split = split_tokens or w.split_tokens
         self.step = pkv.DecodeStep(c, w.num_q_heads, w.batch, self.max_seq_len, split, verify,
-                                   device)
+                                   device, total_tokens=int(w.seq_lens.sum()))
         # the token appended this step: each request's last token
         off = w.token_offsets()
         last = torch.from_numpy(off[1:] - 1).to(device)

@@ -4,6 +4,8 @@ before anything reaches a GPU (no compute calls here)."""
 import ctypes
 import os
 import re
+
+import torch
 import subprocess
 
 import pytest
@@ -41,11 +43,24 @@ def test_host_helpers():
     assert pkv.pkv_version() >= 100
     assert pkv.pkv_strerror(0) == "ok"
     assert pkv.pkv_strerror(-1) == "invalid argument"
-    s = pkv.pkv_suggest_split(64, 32768, 8, 16)
-    assert s > 0 and s % 16 == 0
-    assert pkv.pkv_suggest_split(1, 10, 8, 64) == 64
+    # geometry only: one-page host tensors stand in for the pools
+    gqa = pkv.Cache(torch.empty((1, 8, 16, 128), dtype=torch.uint8),
+                    torch.empty((1, 8, 16, 128), dtype=torch.uint8))
+    # batch 64 of the concurrency sweep: long splits; batch 1: short ones
+    assert pkv.pkv_suggest_split(gqa, 64, 64, 64 * 17000, 32768) == 512
+    assert pkv.pkv_suggest_split(gqa, 64, 8, 8 * 17000, 32768) == 256
+    assert pkv.pkv_suggest_split(gqa, 64, 1, 17000, 17000) == 128
+    # never longer than the longest request (rounded up to whole pages)
+    assert pkv.pkv_suggest_split(gqa, 64, 1, 10, 10) == 16
+    lat = pkv.Cache(torch.empty((1, 1, 64, 576), dtype=torch.uint8), None, latent_dim_v=512)
+    assert pkv.pkv_suggest_split(lat, 128, 64, 907520, 65536) == 4096
+    assert pkv.pkv_suggest_split(lat, 128, 1, 8192, 8192) == 64
+    for s in (pkv.pkv_suggest_split(gqa, 64, 3, 0, 5000), pkv.pkv_suggest_split(lat, 128, 3, 0, 5000)):
+        assert s > 0 and s % 16 == 0
     with pytest.raises(pkv.PkvError):
-        pkv.pkv_suggest_split(1, 10, 8, 17)
+        pkv.pkv_suggest_split(gqa, 63, 1, 10, 10)  # query heads not a multiple of kv heads
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_suggest_split(gqa, 64, 0, 10, 10)
 
 
 def _cache(**kw):
