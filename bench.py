@@ -77,9 +77,14 @@ def measured_traffic(w, split: int):
     return int(round((kib[0] * FETCH_FACTOR + kib[1] * WRITE_FACTOR) * 1024))
 
 
-def kv_bytes(w, elem_bytes: int) -> int:
+def kv_bytes(w, elem_bytes: int, read=None) -> int:
+    """Cache bytes the step reads: every token of every request that is not
+    aborted (read: bool [B] from the device's abort flags; None = all)."""
     per_token = w.num_kv_heads * (w.head_dim_k if w.latent else w.head_dim_k + w.head_dim_v)
-    return int(w.seq_lens.astype("int64").sum()) * per_token * elem_bytes
+    lens = w.seq_lens.astype("int64")
+    if read is not None:
+        lens = lens[read]
+    return int(lens.sum()) * per_token * elem_bytes
 
 
 class Runner:
@@ -249,7 +254,11 @@ def main():
     run = Runner(w, "fp8", args.split or None)
     ms, dec_ms = run.time(args.steps, args.warmup)
     split = run.step.split_tokens
-    fp8_bytes = kv_bytes(w, 1)
+    # requests the step actually reads: those the tag check did not abort
+    read = (run.step.abort.cpu().numpy() == 0) if run.step.verify else None
+    n_aborted = 0 if read is None else int((~read).sum())
+    tokens_read = int(w.seq_lens[read].sum()) if read is not None else w.total_tokens
+    fp8_bytes = kv_bytes(w, 1, read)
     gbs = fp8_bytes / (ms * 1e-3) / 1e9
     dec_gbs = fp8_bytes / (dec_ms * 1e-3) / 1e9
     rec = {
@@ -260,6 +269,7 @@ def main():
         "data": "synthetic (seeded counter-based bf16 N(0,1); lengths U[2048,32768])",
         "config": {"workload": f"{w.name}: {w.description}", "batch": w.batch,
                    "total_context_tokens": w.total_tokens, "split_tokens": split,
+                   "aborted_requests": n_aborted, "context_tokens_read": tokens_read,
                    "kv_dtype": "e4m3", "kv_bytes": fp8_bytes},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "seq_steps_per_s": round(w.batch / (ms * 1e-3), 1),
@@ -267,7 +277,7 @@ def main():
     if w.latent:
         # the dense contraction bounds this kernel: QK^T over 576 dims and PV
         # over 512 for every (token, query head)
-        flop = 2 * w.num_q_heads * (w.head_dim_k + w.head_dim_v) * w.total_tokens
+        flop = 2 * w.num_q_heads * (w.head_dim_k + w.head_dim_v) * tokens_read
         tflops = flop / (dec_ms * 1e-3) / 1e12
         rec["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK,
                            "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK, 4),
@@ -288,7 +298,7 @@ def main():
         del rb
         torch.cuda.empty_cache()
         rec["bf16"] = {"ms_per_step": round(ms_b, 5),
-                       "kv_gbs": round(kv_bytes(w, 2) / (ms_b * 1e-3) / 1e9, 2),
+                       "kv_gbs": round(kv_bytes(w, 2, read) / (ms_b * 1e-3) / 1e9, 2),
                        "decode_ms": round(dec_b, 5),
                        "seq_steps_per_s": round(w.batch / (ms_b * 1e-3), 1)}
         rec["fp8_speedup_over_bf16"] = round(ms_b / ms, 4)
@@ -300,10 +310,11 @@ def main():
             for kv, e in (("fp8", 1), ("bf16", 2)):
                 r = Runner(ws, kv, None)
                 m, d = r.time(max(10, args.steps // 2), 5)
+                nb = kv_bytes(ws, e, r.step.abort.cpu().numpy() == 0)
                 del r
                 torch.cuda.empty_cache()
-                row[kv] = {"ms_per_step": round(m, 5), "kv_gbs": round(kv_bytes(ws, e) / (m * 1e-3) / 1e9, 2),
-                           "hbm_frac": round(kv_bytes(ws, e) / (m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                row[kv] = {"ms_per_step": round(m, 5), "kv_gbs": round(nb / (m * 1e-3) / 1e9, 2),
+                           "hbm_frac": round(nb / (m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                            "seq_steps_per_s": round(B / (m * 1e-3), 1), "decode_ms": round(d, 5)}
             row["fp8_speedup_over_bf16"] = round(row["bf16"]["ms_per_step"] / row["fp8"]["ms_per_step"], 4)
             rows.append(row)
