@@ -38,7 +38,8 @@ MFMA_BF16_PEAK = 2500.0  # TFLOP/s, dense
 # here and WRITE_SIZE in KiB. Entries stop matching once the kernel changes.
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 TRAFFIC_KIB = {
-    ("sweep_b64", 512, "decode_gqa.hip", "ae4dd4fb49899969"): (1199578.1, 81311.7),
+    ("sweep_b64", 512, "decode_gqa.hip", "379eb3d1ff700931"): (1199595.4, 81392.5),
+    ("mla_b64", 4096, "decode_mla.hip", "f3a58c5486d7f247"): (178394.0, 44200.1),
 }
 
 
