@@ -237,12 +237,15 @@ extern "C" int pkv_decode_attn(const pkv_cache* cache, const void* q, int32_t nu
   p.split_tokens = split_tokens;
   p.max_splits = max_splits;
   p.head_groups = head_groups;
+  p.batch = batch;
   p.v_row = latent ? dk : dv;
   p.sm_scale_log2 = sm_scale * kLog2e;
   const bool e4m3 = cache->dtype == PKV_KV_E4M3;
   if (latent && mla_fast_path_supported(dk, dv, cache->num_kv_heads, num_q_heads,
                                         cache->page_size, split_tokens))
     return launch_decode_mla(p, e4m3, static_cast<int>(n_split_blocks), batch, stream);
+  if (e4m3 && gqa_e4m3_path_supported(dk, dv, G, latent, split_tokens, cache->page_size))
+    return launch_decode_gqa_e4m3(p, static_cast<int>(n_split_blocks), batch, stream);
   if (gqa_fast_path_supported(dk, dv, G, latent, split_tokens, cache->page_size))
     return launch_decode_gqa(p, e4m3, static_cast<int>(n_split_blocks), batch, stream);
   return e4m3 ? dispatch<true>(p, latent, dk, G, static_cast<int>(n_split_blocks), batch, stream)

@@ -17,6 +17,7 @@ struct DecodeParams {
   float* lse_part;
   int num_pages, page_size, num_kv_heads, num_q_heads, max_pages, max_seq_len;
   int split_tokens, max_splits, head_groups;
+  int batch;
   int v_row;            // elements per V row in v_pool
   float sm_scale_log2;  // sm_scale * log2(e)
 };
@@ -26,6 +27,12 @@ bool gqa_fast_path_supported(int dk, int dv, int group, bool latent, int split_t
                              int page_size);
 int launch_decode_gqa(const DecodeParams& p, bool e4m3, int n_split_blocks, int batch,
                       hipStream_t stream);
+
+// grouped-query kernel for an e4m3 cache, head dim 128, 8 query heads per kv head
+bool gqa_e4m3_path_supported(int dk, int dv, int group, bool latent, int split_tokens,
+                             int page_size);
+int launch_decode_gqa_e4m3(const DecodeParams& p, int n_split_blocks, int batch,
+                           hipStream_t stream);
 
 // wide-head kernel for one latent kv head (576 / 512), page size 64
 bool mla_fast_path_supported(int dk, int dv, int num_kv_heads, int num_q_heads, int page_size,

@@ -245,3 +245,77 @@ def test_mla_score_jump_far_above_the_first_tile(kv):
     out = ds.attend(q.to(dev), bt, lens, sm, None).float().cpu().numpy()[0]
     ref, _ = attention.attend(q[0].double().numpy(), k_hat[:, None, :], k_hat[:, None, :dv], sm)
     assert_close(out, ref, f"mla score jump {kv}")
+
+
+def _gqa_direct_case(kv, vals_k, vals_v, bt_pages, L, hq, P, split, num_pages, seed=11):
+    """Write K/V rows straight into a pool (token t of the request lives in
+    page bt_pages[t // P]) and decode one request without the tag check."""
+    from oracle import attention
+    dk = vals_k.shape[1]
+    rng = np.random.default_rng(seed)
+    q = torch.from_numpy(rng.standard_normal((1, hq, dk)).astype(np.float32)).to(torch.bfloat16)
+    cache = pkv.allocate_cache(num_pages, 1, P, dk, dk, kv, device=dev)
+    k_hat = np.zeros_like(vals_k, dtype=np.float64)
+    v_hat = np.zeros_like(vals_v, dtype=np.float64)
+    if kv == "fp8":
+        ks = np.float32(np.abs(vals_k).max() / 448.0)
+        vs = np.float32(np.abs(vals_v).max() / 448.0)
+        kc = e4m3.encode((vals_k / ks).astype(np.float32))
+        vc = e4m3.encode((vals_v / vs).astype(np.float32))
+        k_hat[:], v_hat[:] = e4m3.DECODE[kc] * np.float64(ks), e4m3.DECODE[vc] * np.float64(vs)
+        cache.k_scale.fill_(float(ks))
+        cache.v_scale.fill_(float(vs))
+        kt, vt = torch.from_numpy(kc), torch.from_numpy(vc)
+    else:
+        kt = torch.from_numpy(vals_k).to(torch.bfloat16)
+        vt = torch.from_numpy(vals_v).to(torch.bfloat16)
+        k_hat[:], v_hat[:] = kt.double().numpy(), vt.double().numpy()
+    keep = []
+    for t in range(L):
+        pg = bt_pages[t // P]
+        if 0 <= pg < num_pages:
+            cache.k_pool[pg, 0, t % P] = kt[t].to(dev)
+            cache.v_pool[pg, 0, t % P] = vt[t].to(dev)
+            keep.append(t)
+    bt = torch.tensor([bt_pages], dtype=torch.int32, device=dev)
+    lens = torch.tensor([L], dtype=torch.int32, device=dev)
+    sm = 1 / math.sqrt(dk)
+    ds = pkv.DecodeStep(cache, hq, 1, L, split, verify=False)
+    out = ds.attend(q.to(dev), bt, lens, sm, None).float().cpu().numpy()[0]
+    keep = np.asarray(keep)
+    ref, _ = attention.attend(q[0].double().numpy(), k_hat[keep][:, None, :], v_hat[keep][:, None, :], sm)
+    return out, ref
+
+
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+@pytest.mark.parametrize("jump_page", [1, 7, 15])
+def test_gqa_score_jump_far_above_the_first_group(kv, jump_page):
+    """Keys of a later page aligned with head 0's query put its score far
+    above every score of the first 16-token group: the softmax reference must
+    move (or the unit be recomputed) without losing accuracy."""
+    hq, dk, P, L = 8, 128, 16, 256
+    rng = np.random.default_rng(12)
+    q_sign = np.sign(torch.from_numpy(np.random.default_rng(11).standard_normal((1, hq, dk))
+                                      .astype(np.float32)).to(torch.bfloat16)[0, 0].float().numpy())
+    q_sign[q_sign == 0] = 1
+    vals_k = rng.standard_normal((L, dk)).astype(np.float32) * 0.01
+    vals_k[P * jump_page:P * (jump_page + 1)] = 7.0 * q_sign
+    vals_v = rng.standard_normal((L, dk)).astype(np.float32)
+    out, ref = _gqa_direct_case(kv, vals_k, vals_v, list(range(16)), L, hq, P, 256, 16)
+    assert_close(out, ref, f"gqa score jump {kv} page {jump_page}")
+
+
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+@pytest.mark.parametrize("bad", [[0], [3], [0, 1], [6]])
+def test_gqa_out_of_pool_pages_left_out_without_tag_check(kv, bad):
+    """With the no-op tracker a block-table entry outside the pool is never
+    read and its tokens are left out, including the unit's first page."""
+    hq, dk, P, L, n_pages = 8, 128, 16, 100, 8
+    rng = np.random.default_rng(13)
+    vals_k = rng.standard_normal((L, dk)).astype(np.float32)
+    vals_v = rng.standard_normal((L, dk)).astype(np.float32)
+    pages = [1, 2, 3, 4, 5, 6, 7]
+    for j in bad:
+        pages[j] = n_pages + 5 if j % 2 == 0 else -3
+    out, ref = _gqa_direct_case(kv, vals_k, vals_v, pages, L, hq, P, 112, n_pages)
+    assert_close(out, ref, f"gqa out-of-pool pages {bad} {kv}")
