@@ -38,7 +38,7 @@ MFMA_BF16_PEAK = 2500.0  # TFLOP/s, dense
 # here and WRITE_SIZE in KiB. Entries stop matching once the kernel changes.
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 TRAFFIC_KIB = {
-    ("sweep_b64", 512, "decode_gqa.hip", "379eb3d1ff700931"): (1199595.4, 81392.5),
+    ("sweep_b64", 512, "decode_gqa_e4m3.hip", "ce33fa6891eada35"): (1197882.7, 77700.2),
     ("mla_b64", 4096, "decode_mla.hip", "f3a58c5486d7f247"): (178394.0, 44200.1),
 }
 
@@ -67,7 +67,7 @@ def parse():
 def measured_traffic(w, split: int):
     """Scaled HBM bytes per decode launch, or None if no counters match."""
     import hashlib
-    src = "decode_mla.hip" if w.latent else "decode_gqa.hip"
+    src = "decode_mla.hip" if w.latent else "decode_gqa_e4m3.hip"
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "decode_attention_fp8_amd",
                         "csrc", src)
     with open(path, "rb") as f:

@@ -28,11 +28,11 @@
 // 2r and 2r + 1 for the 16 tokens.
 //
 // Softmax. Scores are kept in the log2 domain relative to a reference max
-// m per head, the largest score of the unit's first group. No rescale of the
-// accumulators ever happens inside the loop; if any later score exceeds m by
-// more than kRestart, the unit is recomputed once with m set to the unit's
-// true maximum. Numerators are rounded to f16 (at most 2^kRestart, so they
-// cannot overflow) for the PV products; the denominator sums them unrounded.
+// m per head, the largest score of the first group that has a valid token.
+// The accumulators are rescaled only when a later score exceeds m by more
+// than kTau (a uniform branch that real attention scores almost never take);
+// so numerators are at most 2^kTau and are rounded to f16 for the PV
+// products, while the denominator sums them unrounded.
 //
 // PV. The numerators of a row's two heads are packed into f16 token pairs
 // (tokens 2k, 2k + 1), exchanged through 256 bytes of LDS so every lane holds
@@ -41,7 +41,11 @@
 // consecutive tokens, so token pairs come out of the converts already paired
 // and each lane accumulates 8 heads x 2 dims over all 16 tokens.
 //
-// About 80 VGPRs and 12.5 KB of LDS per wave: three waves per SIMD.
+// Launch: one workgroup (one wave) per work unit, in a one-dimensional grid
+// whose order is chosen for the hardware dispatcher (see find_unit). With
+// two ring slots a wave holds 8.6 KB of LDS and ~85 VGPRs, so 18 waves share
+// a compute unit; a wave waiting for its first bytes (a unit's start costs
+// three dependent memory round trips under load) leaves the others running.
 #include <utility>
 
 #include "common.h"
@@ -54,8 +58,7 @@ typedef int v2i_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
 
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRestart = 15.0f;  // log2 headroom above the reference max
-constexpr float kFloor = -1e30f;   // reference max of a unit with no valid token yet
+constexpr float kTau = 15.0f;  // numerators stay at most 2^kTau (f16 range)
 constexpr int kD = 128;
 constexpr int kG = 8;
 constexpr int kGroupBytes = 4096;  // K 16 x 128 B, then V 16 x 128 B
@@ -82,6 +85,12 @@ __device__ __forceinline__ float dot2_bf16_bcast(float acc, uint32_t a, uint32_t
       : "v"(a), "v"(b), "n"(M));
   return acc;
 }
+// dot(a, b) of bf16 pairs into a fresh fp32 register (no accumulator to zero).
+__device__ __forceinline__ float dot2_bf16_first(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 // The same with f16 pairs.
 template <int M>
 __device__ __forceinline__ float dot2_f16_bcast(float acc, uint32_t a, uint32_t b) {
@@ -94,15 +103,22 @@ __device__ __forceinline__ float dot2_f16_bcast(float acc, uint32_t a, uint32_t 
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float v) {
   return u2f(static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(f2u(v)), kCtrl, 0xf, 0xf, false)));
+      __builtin_amdgcn_mov_dpp(static_cast<int>(f2u(v)), kCtrl, 0xf, 0xf, false)));
+}
+// max without the NaN-quieting canonicalisation fmaxf brings (NaN inputs
+// do not reach it: masked scores are -inf, never NaN, for finite caches).
+__device__ __forceinline__ float fmax_nc(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 // Maximum / sum over the 16 lanes of a row, returned to every lane of it
 // (xor 1, xor 2 within quads, then the half-row and row mirrors).
 __device__ __forceinline__ float row_max(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));
-  v = fmaxf(v, dpp<0x4E>(v));
-  v = fmaxf(v, dpp<0x141>(v));
-  return fmaxf(v, dpp<0x140>(v));
+  v = fmax_nc(v, dpp<0xB1>(v));
+  v = fmax_nc(v, dpp<0x4E>(v));
+  v = fmax_nc(v, dpp<0x141>(v));
+  return fmax_nc(v, dpp<0x140>(v));
 }
 __device__ __forceinline__ float row_sum(float v) {
   v += dpp<0xB1>(v);
@@ -128,6 +144,28 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const uint8_t
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// Wait until at most n vector-memory loads are outstanding (n is uniform; a
+// smaller count than n only waits longer).
+__device__ __forceinline__ void wait_vm_le(int n) {
+  switch (n < 0 ? 0 : n) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<1>(); break;
+    case 2: wait_vm<2>(); break;
+    case 3: wait_vm<3>(); break;
+    case 4: wait_vm<4>(); break;
+    case 5: wait_vm<5>(); break;
+    case 6: wait_vm<6>(); break;
+    case 7: wait_vm<7>(); break;
+    case 8: wait_vm<8>(); break;
+    case 9: wait_vm<9>(); break;
+    case 10: wait_vm<10>(); break;
+    case 11: wait_vm<11>(); break;
+    case 12: wait_vm<12>(); break;
+    case 13: wait_vm<13>(); break;
+    case 14: wait_vm<14>(); break;
+    default: wait_vm<15>(); break;
+  }
 }
 
 // Ring layouts. K: 16-byte chunk c of token row t sits at chunk position
@@ -159,13 +197,16 @@ __device__ __forceinline__ int wave_scan(int x) {
 // batches above 64), so the launch ends on its shortest units; then indices
 // with no unit (the launch is sized for max_seq_len), which exit at once.
 // Aborted requests and empty or over-long contexts have no units.
-__device__ bool find_unit(const DecodeParams& p, int u, int& b_out, int& g_out, int& c_out) {
+__device__ bool find_unit(const DecodeParams& p, int u, int& b_out, int& g_out, int& c_out,
+                          int& L_out) {
   const int lane = threadIdx.x;
   const int S = p.split_tokens, H = p.num_kv_heads;
+  int L = 0;
   auto splits = [&](int j) __attribute__((always_inline)) {
     int n = 0;
+    L = 0;
     if (j < p.batch) {
-      const int L = p.seq_lens[j];
+      L = p.seq_lens[j];
       const bool ab = p.abort_flags && p.abort_flags[j];
       if (!ab && L > 0 && L <= p.max_seq_len) n = (L + S - 1) / S;
     }
@@ -183,6 +224,7 @@ __device__ bool find_unit(const DecodeParams& p, int u, int& b_out, int& g_out, 
       b_out = b0 + bl;
       c_out = r / H;
       g_out = r - c_out * H;
+      L_out = __builtin_amdgcn_readlane(L, bl);
       return true;
     }
     base += total;
@@ -190,7 +232,7 @@ __device__ bool find_unit(const DecodeParams& p, int u, int& b_out, int& g_out, 
   int u2 = u - base;
   if (p.batch <= 64) {
     const int n = splits(lane);
-    const int psz = n > 0 ? p.seq_lens[lane] - (n - 1) * S : -1;
+    const int psz = n > 0 ? L - (n - 1) * S : -1;
     if (u2 >= __popcll(__ballot(n > 0)) * H) return false;
     int rank = 0;
     for (int k = 0; k < 64; ++k) {
@@ -203,6 +245,7 @@ __device__ bool find_unit(const DecodeParams& p, int u, int& b_out, int& g_out, 
     b_out = bl;
     g_out = u2 - R * H;
     c_out = __builtin_amdgcn_readlane(n, bl) - 1;
+    L_out = __builtin_amdgcn_readlane(L, bl);
     return true;
   }
   for (int b0 = 0; b0 < p.batch; b0 += 64) {
@@ -216,6 +259,7 @@ __device__ bool find_unit(const DecodeParams& p, int u, int& b_out, int& g_out, 
       b_out = b0 + bl;
       g_out = r;
       c_out = __builtin_amdgcn_readlane(n, bl) - 1;
+      L_out = __builtin_amdgcn_readlane(L, bl);
       return true;
     }
     u2 -= total;
@@ -223,280 +267,382 @@ __device__ bool find_unit(const DecodeParams& p, int u, int& b_out, int& g_out, 
   return false;
 }
 
-template <int kSlots, int kWaves>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWaves)))
-decode_gqa_e4m3_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kSlots * kGroupBytes];
-  __shared__ __attribute__((aligned(16))) uint32_t pbuf[16 * 4];  // [lane in row][row]
-  __shared__ float fin[2][kG];                                    // l, m per head
-  const int lane = threadIdx.x;
-  int b, g, c;
-  if (!find_unit(p, static_cast<int>(blockIdx.x), b, g, c)) return;
-  const int L = p.seq_lens[b];
-  const int t_begin = c * p.split_tokens;
-  const int t_end = min(L, t_begin + p.split_tokens);
-  const int n_groups = (t_end - t_begin + 15) >> 4;
-  const int P = p.page_size;
-  const int log2P = P == 16 ? 4 : (P == 32 ? 5 : 6);
+// Per-lane constants of the lane layout above.
+struct LaneMap {
+  int r, i, tok;
+  bool lo8;
+  uint32_t pack_sel;                    // v_perm selector of the numerator pack
+  uint32_t kr0, kr1;                    // K read offsets in a ring slot
+  uint32_t vr[2][2];                    // V transposing-read offsets in a slot
+  uint32_t koff0, koff1, voff0, voff1;  // DMA source offsets in a group's K / V block
+};
 
-  const int r = lane >> 4, i = lane & 15;
-  const int tok = 2 * (i & 7) + (i >> 3);  // QK token of this lane
-  const bool lo8 = i < 8;
-
-  // query: qd[h] = bf16 pair (32r + 2i, 32r + 2i + 1) of head g*8 + h
-  uint32_t qd[kG];
-  {
-    const uint32_t* qw = reinterpret_cast<const uint32_t*>(
-        p.q + (static_cast<int64_t>(b) * p.num_q_heads + g * kG) * kD);
-#pragma unroll
-    for (int h = 0; h < kG; ++h) qd[h] = qw[h * (kD / 2) + 16 * r + i];
-  }
-  const float qk_scale = p.k_scale[g] * p.sm_scale_log2;
-  const float o_scale = p.v_scale[g];
-
-  // The unit's pages (at most 64): lane j holds the byte offset of the
-  // (page j, kv head g) block, read back per group with readlane; bit j of
-  // valid says whether page id j is inside the pool (an invalid page is
-  // replaced by page 0 for the loads and its tokens are masked).
-  const int64_t head_stride = static_cast<int64_t>(P) * kD;
-  const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_pages;
-  const int first_page = t_begin >> log2P;
-  const int n_unit_pages = (t_end - t_begin + P - 1) >> log2P;
-  int pg = -1;
-  if (lane < n_unit_pages) pg = bt[first_page + lane];
-  // Every compiler-issued load must be complete before the first DMA, or its
-  // own wait for them would also wait for the ring.
-  asm volatile("" : : "v"(qd[0]), "v"(qd[1]), "v"(qd[2]), "v"(qd[3]), "v"(qd[4]), "v"(qd[5]),
-               "v"(qd[6]), "v"(qd[7]));
-  asm volatile("" : : "v"(qk_scale), "v"(o_scale), "v"(pg));
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" : : : "memory");
-  const bool pg_ok = pg >= 0 && pg < p.num_pages;
-  const uint64_t valid = __ballot(pg_ok);
-  const int64_t blk_off = (static_cast<int64_t>(pg_ok ? pg : 0) * p.num_kv_heads + g) * head_stride;
-  const int off_lo = static_cast<int>(static_cast<uint32_t>(blk_off));
-  const int off_hi = static_cast<int>(static_cast<uint32_t>(static_cast<uint64_t>(blk_off) >> 32));
-
-  const uint8_t* kpool = static_cast<const uint8_t*>(p.k_pool);
-  const uint8_t* vpool = static_cast<const uint8_t*>(p.v_pool);
-  const uint32_t ring0 = lds_addr(ring);
-
-  // DMA source offsets: lane L fills LDS chunk position L & 7 of row L >> 3
-  // (first 1 KB) and of row 8 + (L >> 3) (second).
-  const uint32_t dr0 = lane >> 3, dr1 = 8 + (lane >> 3), dpos = lane & 7;
-  const uint32_t koff0 = dr0 * kD + ((dpos ^ kswz(dr0)) << 4);
-  const uint32_t koff1 = dr1 * kD + ((dpos ^ kswz(dr1)) << 4);
-  const uint32_t voff0 = dr0 * kD + ((dpos ^ vswz(dr0)) << 4);
-  const uint32_t voff1 = dr1 * kD + ((dpos ^ vswz(dr1)) << 4);
-  // LDS read offsets inside a slot: K chunks 2r, 2r + 1 of row tok; the
-  // transposing V reads of octet o, chunk 2r + s address row 8o + (i >> 1).
-  const uint32_t kr0 = tok * kD + (((2 * r) ^ kswz(tok)) << 4);
-  const uint32_t kr1 = tok * kD + (((2 * r + 1) ^ kswz(tok)) << 4);
-  uint32_t vr[2][2];
+__device__ __forceinline__ LaneMap lane_map(int lane) {
+  LaneMap m;
+  m.r = lane >> 4;
+  m.i = lane & 15;
+  m.tok = 2 * (m.i & 7) + (m.i >> 3);
+  m.lo8 = m.i < 8;
+  // lane i < 8 packs (own head-2r value, partner's), lane i >= 8 (partner's
+  // head-2r+1 value, own): bytes of {partner, own} for v_perm
+  m.pack_sel = m.lo8 ? 0x05040100u : 0x03020706u;
+  m.kr0 = m.tok * kD + (((2 * m.r) ^ kswz(m.tok)) << 4);
+  m.kr1 = m.tok * kD + (((2 * m.r + 1) ^ kswz(m.tok)) << 4);
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int o = 0; o < 2; ++o) {
-      const uint32_t t = 8 * o + (i >> 1);
-      vr[s][o] = 2048 + t * kD + (((2 * r + s) ^ vswz(t)) << 4) + 8 * (i & 1);
+      const uint32_t t = 8 * o + (m.i >> 1);
+      m.vr[s][o] = 2048 + t * kD + (((2 * m.r + s) ^ vswz(t)) << 4) + 8 * (m.i & 1);
     }
+  // lane L fills LDS chunk position L & 7 of row L >> 3 (first 1 KB of a
+  // block) and of row 8 + (L >> 3) (second)
+  const uint32_t dr0 = lane >> 3, dr1 = 8 + (lane >> 3), dpos = lane & 7;
+  m.koff0 = dr0 * kD + ((dpos ^ kswz(dr0)) << 4);
+  m.koff1 = dr1 * kD + ((dpos ^ kswz(dr1)) << 4);
+  m.voff0 = dr0 * kD + ((dpos ^ vswz(dr0)) << 4);
+  m.voff1 = dr1 * kD + ((dpos ^ vswz(dr1)) << 4);
+  return m;
+}
 
-  auto group_tokens = [&](int gi) __attribute__((always_inline)) {
-    const bool ok = ((valid >> ((gi << 4) >> log2P)) & 1u) != 0;
-    return ok ? min(16, t_end - (t_begin + (gi << 4))) : 0;
-  };
-  auto issue = [&](int gi) __attribute__((always_inline)) {
-    const int j = (gi << 4) >> log2P;
-    const uint64_t off =
-        (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(off_hi, j))) << 32) |
-        static_cast<uint32_t>(__builtin_amdgcn_readlane(off_lo, j));
-    const uint32_t row_off = static_cast<uint32_t>(((gi << 4) & (P - 1)) * kD);
-    const uint8_t* kb = kpool + off + row_off;
-    const uint8_t* vb = vpool + off + row_off;
-    const uint32_t slot = ring0 + (gi % kSlots) * kGroupBytes;
-    dma16(slot, koff0, kb);
-    dma16(slot + 1024, koff1, kb);
-    dma16(slot + 2048, voff0, vb);
-    dma16(slot + 3072, voff1, vb);
-  };
+// A work unit: request b, kv head g, split c (tokens [t_begin, t_end)).
+struct Unit {
+  int b, g, c, t_begin, t_end, n_groups, first_page, n_pages;
+};
 
-  float m_ref[2] = {kFloor, kFloor};
-  float l[2], xmax[2];
-  float o[kG][2];
+__device__ __forceinline__ Unit make_unit(int b, int g, int c, int L, int S, int log2P) {
+  Unit u;
+  u.b = b;
+  u.g = g;
+  u.c = c;
+  u.t_begin = c * S;
+  u.t_end = min(L, u.t_begin + S);
+  u.n_groups = (u.t_end - u.t_begin + 15) >> 4;
+  u.first_page = u.t_begin >> log2P;
+  u.n_pages = (u.t_end - u.t_begin + (1 << log2P) - 1) >> log2P;
+  return u;
+}
 
-  for (int pass = 0;; ++pass) {
-    l[0] = l[1] = 0.0f;
-    xmax[0] = xmax[1] = -INFINITY;
+// The unit's pages (at most 64): lane j holds the byte offset of the
+// (page j, kv head g) block, read back per group with readlane; bit j of
+// valid says whether page id j is inside the pool (an invalid page is
+// replaced by page 0 for the loads and its tokens are masked).
+struct Pages {
+  uint64_t valid;
+  int lo, hi;
+};
+
+__device__ __forceinline__ Pages page_offsets(const DecodeParams& p, int pg, int g) {
+  Pages pgs;
+  const bool ok = pg >= 0 && pg < p.num_pages;
+  pgs.valid = __ballot(ok);
+  const int64_t off =
+      (static_cast<int64_t>(ok ? pg : 0) * p.num_kv_heads + g) * (static_cast<int64_t>(p.page_size) * kD);
+  pgs.lo = static_cast<int>(static_cast<uint32_t>(off));
+  pgs.hi = static_cast<int>(static_cast<uint32_t>(static_cast<uint64_t>(off) >> 32));
+  return pgs;
+}
+
+__device__ __forceinline__ int group_tokens(const Unit& u, const Pages& pgs, int gi, int log2P) {
+  const bool ok = ((pgs.valid >> ((gi << 4) >> log2P)) & 1u) != 0;
+  return ok ? min(16, u.t_end - (u.t_begin + (gi << 4))) : 0;
+}
+
+// DMA of group gi of a unit into the ring slot at LDS address slot.
+__device__ __forceinline__ void issue_group(uint32_t slot, const LaneMap& lm, const DecodeParams& p,
+                                            const Pages& pgs, int gi, int log2P) {
+  const int j = (gi << 4) >> log2P;
+  const uint64_t off =
+      (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(pgs.hi, j))) << 32) |
+      static_cast<uint32_t>(__builtin_amdgcn_readlane(pgs.lo, j));
+  const uint32_t row_off = static_cast<uint32_t>(((gi << 4) & (p.page_size - 1)) * kD);
+  const uint8_t* kb = static_cast<const uint8_t*>(p.k_pool) + off + row_off;
+  const uint8_t* vb = static_cast<const uint8_t*>(p.v_pool) + off + row_off;
+  dma16(slot, lm.koff0, kb);
+  dma16(slot + 1024, lm.koff1, kb);
+  dma16(slot + 2048, lm.voff0, vb);
+  dma16(slot + 3072, lm.voff1, vb);
+}
+
+// Running softmax state of a lane (heads 2r, 2r + 1).
+struct Softmax {
+  float m[2];  // reference max (log2 domain), once set
+  float l[2];  // denominators over this lane's tokens
+  bool set;    // (wave-uniform) a valid token has been seen
+};
+
+// The query operands of a unit.
+struct Query {
+  uint32_t qd[kG];   // bf16 pair (32r + 2i, 32r + 2i + 1) of head h
+  uint32_t qb0[kG];  // pair 0 of the row, in every lane of the row
+  float qk_scale;    // k_scale * sm_scale * log2(e)
+  float o_scale;     // v_scale
+};
+
+__device__ __forceinline__ void finish_query(Query& q) {
 #pragma unroll
-    for (int h = 0; h < kG; ++h) o[h][0] = o[h][1] = 0.0f;
+  for (int h = 0; h < kG; ++h)
+    q.qb0[h] = static_cast<uint32_t>(
+        __builtin_amdgcn_mov_dpp(static_cast<int>(q.qd[h]), 0x150, 0xf, 0xf, false));
+}
 
+// One 16-token group: K words kw0/kw1 and V words vw (already in registers)
+// into the softmax state and the accumulators o[h][s] (head h, dim
+// 32r + 16s + i). pbuf: 256 B of LDS for the numerator exchange; abuf: 8
+// floats for the rare rescale.
+__device__ __forceinline__ void group_math(const LaneMap& lm, const uint4& kw0, const uint4& kw1,
+                                           uint32_t (&vw)[2][2][2], int nv, const Query& q,
+                                           Softmax& st, float (&o)[kG][2], uint32_t* pbuf,
+                                           float* abuf) {
+  if (nv < 16) {
+    // tokens past the context or of an invalid page: V bytes to 0
 #pragma unroll
-    for (int k = 0; k < kSlots; ++k)
-      if (k < n_groups) issue(k);
-
-    for (int gi = 0; gi < n_groups; ++gi) {
-      // groups gi + 1 .. gi + kSlots - 1 may still be in flight
-      const int after = min(kSlots - 1, n_groups - 1 - gi);
-      if (kSlots > 3 && after >= 3) wait_vm<12>();
-      else if (kSlots > 2 && after >= 2) wait_vm<8>();
-      else if (after >= 1) wait_vm<4>();
-      else wait_vm<0>();
-
-      const uint8_t* slot = ring + (gi % kSlots) * kGroupBytes;
-      const uint4 kw0 = *reinterpret_cast<const uint4*>(slot + kr0);
-      const uint4 kw1 = *reinterpret_cast<const uint4*>(slot + kr1);
-      uint32_t vw[2][2][2];  // [chunk s][octet o][word]
+    for (int o2 = 0; o2 < 2; ++o2) {
+      const int vo = min(8, max(0, nv - 8 * o2));
+      const uint64_t m64 = vo >= 8 ? ~0ull : ((1ull << (8 * vo)) - 1ull);
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int o2 = 0; o2 < 2; ++o2) {
-          const v2i_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(slot + vr[s][o2]));
-          vw[s][o2][0] = static_cast<uint32_t>(x[0]);
-          vw[s][o2][1] = static_cast<uint32_t>(x[1]);
-        }
-      // the slot is free once its bytes are in registers
-      asm volatile("" : : "v"(kw0.x), "v"(kw0.y), "v"(kw0.z), "v"(kw0.w), "v"(kw1.x), "v"(kw1.y),
-                   "v"(kw1.z), "v"(kw1.w));
-      asm volatile("" : : "v"(vw[0][0][0]), "v"(vw[0][0][1]), "v"(vw[0][1][0]), "v"(vw[0][1][1]),
-                   "v"(vw[1][0][0]), "v"(vw[1][0][1]), "v"(vw[1][1][0]), "v"(vw[1][1][1]));
-      if (gi + kSlots < n_groups) issue(gi + kSlots);
-
-      const int nv = group_tokens(gi);
-      if (nv < 16) {
-        // tokens past the context or of an invalid page: V bytes to 0
-#pragma unroll
-        for (int o2 = 0; o2 < 2; ++o2) {
-          const int vo = min(8, max(0, nv - 8 * o2));
-          const uint64_t m64 = vo >= 8 ? ~0ull : ((1ull << (8 * vo)) - 1ull);
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            vw[s][o2][0] &= static_cast<uint32_t>(m64);
-            vw[s][o2][1] &= static_cast<uint32_t>(m64 >> 32);
-          }
-        }
+      for (int s2 = 0; s2 < 2; ++s2) {
+        vw[s2][o2][0] &= static_cast<uint32_t>(m64);
+        vw[s2][o2][1] &= static_cast<uint32_t>(m64 >> 32);
       }
-
-      // ---- QK^T: row partial dots of token tok for the 8 heads
-      float a[kG];
-#pragma unroll
-      for (int h = 0; h < kG; ++h) a[h] = 0.0f;
-      const uint32_t kw[8] = {kw0.x, kw0.y, kw0.z, kw0.w, kw1.x, kw1.y, kw1.z, kw1.w};
-      unroll<8>([&](auto wc) {
-        constexpr int w = decltype(wc)::value;
-        const uint32_t x0 = __builtin_bit_cast(
-            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[w], 1.0f, false));
-        const uint32_t x1 = __builtin_bit_cast(
-            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[w], 1.0f, true));
-        unroll<kG>([&](auto hc) {
-          constexpr int h = decltype(hc)::value;
-          a[h] = dot2_bf16_bcast<2 * w>(a[h], qd[h], x0);
-        });
-        unroll<kG>([&](auto hc) {
-          constexpr int h = decltype(hc)::value;
-          a[h] = dot2_bf16_bcast<2 * w + 1>(a[h], qd[h], x1);
-        });
-      });
-      // reduce-scatter over the four rows: row r keeps heads 2r, 2r + 1
-      float u[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const auto rr = __builtin_amdgcn_permlane32_swap(f2u(a[h]), f2u(a[h + 4]), false, false);
-        u[h] = u2f(rr[0]) + u2f(rr[1]);
-      }
-      float raw[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const auto rr = __builtin_amdgcn_permlane16_swap(f2u(u[j]), f2u(u[j + 2]), false, false);
-        const float sc = (u2f(rr[0]) + u2f(rr[1])) * qk_scale;
-        raw[j] = tok < nv ? sc : -INFINITY;
-      }
-      if (pass == 0 && gi == 0) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) m_ref[j] = fmaxf(row_max(raw[j]), kFloor);
-      }
-
-      // ---- softmax numerators, packed into f16 token pairs
-      float pr[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        xmax[j] = fmaxf(xmax[j], raw[j]);
-        pr[j] = __builtin_amdgcn_exp2f(raw[j] - m_ref[j]);
-        l[j] += pr[j];
-      }
-      // lanes i and i ^ 8 hold tokens 2(i & 7) and 2(i & 7) + 1: lane i < 8
-      // packs head 2r, lane i >= 8 head 2r + 1, both for pair k = i & 7
-      const float send = lo8 ? pr[1] : pr[0];
-      const float recv = dpp<0x128>(send);  // row_ror:8
-      const float lo = lo8 ? pr[0] : recv;
-      const float hi = lo8 ? recv : pr[1];
-      const half2_t ph = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
-      pbuf[i * 4 + r] = __builtin_bit_cast(uint32_t, ph);
-      __builtin_amdgcn_wave_barrier();
-      const uint4 G4 = *reinterpret_cast<const uint4*>(&pbuf[i * 4]);
-      const uint32_t Gp[4] = {G4.x, G4.y, G4.z, G4.w};  // Gp[j]: heads 2j (lanes 0-7), 2j+1 (8-15)
-
-      // ---- PV: o[h][s] += sum over token pairs k of p[h][2k..2k+1] . v
-      unroll<2>([&](auto sc_) {
-        constexpr int s = decltype(sc_)::value;
-        unroll<4>([&](auto wc) {
-          constexpr int ow = decltype(wc)::value;  // octet ow >> 1, word ow & 1
-          const uint32_t word = vw[s][ow >> 1][ow & 1];
-          const uint32_t v0 = __builtin_bit_cast(
-              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false));
-          const uint32_t v1 = __builtin_bit_cast(
-              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, true));
-          constexpr int k0 = 2 * ow;  // pair index of v0 (tokens 4ow, 4ow + 1)
-          unroll<kG>([&](auto hc) {
-            constexpr int h = decltype(hc)::value;
-            o[h][s] = dot2_f16_bcast<8 * (h & 1) + k0>(o[h][s], Gp[h >> 1], v0);
-          });
-          unroll<kG>([&](auto hc) {
-            constexpr int h = decltype(hc)::value;
-            o[h][s] = dot2_f16_bcast<8 * (h & 1) + k0 + 1>(o[h][s], Gp[h >> 1], v1);
-          });
-        });
-      });
     }
-
-    // ---- a later score above the reference max by more than kRestart:
-    // recompute the unit once with the true maximum
-    float xm[2];
-    bool over = false;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      xm[j] = row_max(xmax[j]);
-      over = over || (xm[j] > m_ref[j] + kRestart);
-    }
-    if (pass > 0 || !__any(over)) break;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) m_ref[j] = fmaxf(xm[j], kFloor);
   }
 
-  // ---- finish: denominators per head, then o / l for this lane's 16 values
-  float ls[2];
+  // ---- QK^T: row partial dots of token tok for the 8 heads
+  float a[kG];
+  const uint32_t kw[8] = {kw0.x, kw0.y, kw0.z, kw0.w, kw1.x, kw1.y, kw1.z, kw1.w};
+  unroll<8>([&](auto wc) {
+    constexpr int w = decltype(wc)::value;
+    const uint32_t x0 = __builtin_bit_cast(
+        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[w], 1.0f, false));
+    const uint32_t x1 = __builtin_bit_cast(
+        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[w], 1.0f, true));
+    unroll<kG>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      if constexpr (w == 0)
+        a[h] = dot2_bf16_first(q.qb0[h], x0);
+      else
+        a[h] = dot2_bf16_bcast<2 * w>(a[h], q.qd[h], x0);
+    });
+    unroll<kG>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      a[h] = dot2_bf16_bcast<2 * w + 1>(a[h], q.qd[h], x1);
+    });
+  });
+  // reduce-scatter over the four rows: row r keeps heads 2r, 2r + 1
+  float u[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) ls[j] = row_sum(l[j]);
-  if (i == 0) {
+  for (int h = 0; h < 4; ++h) {
+    const auto rr = __builtin_amdgcn_permlane32_swap(f2u(a[h]), f2u(a[h + 4]), false, false);
+    u[h] = u2f(rr[0]) + u2f(rr[1]);
+  }
+  float sc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const auto rr = __builtin_amdgcn_permlane16_swap(f2u(u[j]), f2u(u[j + 2]), false, false);
+    sc[j] = u2f(rr[0]) + u2f(rr[1]);
+  }
+
+  // ---- scores relative to the reference max (log2 domain)
+  const bool tv = lm.tok < nv;
+  float d[2];
+  if (!st.set) {
+    // the first group with a valid token sets the reference max
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      fin[0][2 * r + j] = ls[j];
-      fin[1][2 * r + j] = m_ref[j];
+      const float raw = tv ? sc[j] * q.qk_scale : -INFINITY;
+      if (nv > 0) st.m[j] = row_max(raw);
+      d[j] = nv > 0 ? raw - st.m[j] : -INFINITY;
+    }
+    st.set = nv > 0;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) d[j] = tv ? __builtin_fmaf(sc[j], q.qk_scale, -st.m[j]) : -INFINITY;
+    if (__any(d[0] > kTau || d[1] > kTau)) {
+      // rare: raise the reference max of the heads that need it, rescale
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float mx = row_max(d[j]);
+        const float sh = mx > 0.0f ? mx : 0.0f;
+        st.m[j] += sh;
+        d[j] -= sh;
+        const float al = __builtin_amdgcn_exp2f(-sh);
+        st.l[j] *= al;
+        if (lm.i == 0) abuf[2 * lm.r + j] = al;
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int h = 0; h < kG; ++h) {
+        const float al = abuf[h];
+        o[h][0] *= al;
+        o[h][1] *= al;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+
+  // ---- numerators, packed into f16 token pairs and shared with all rows
+  float pr[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    pr[j] = __builtin_amdgcn_exp2f(d[j]);
+    st.l[j] += pr[j];
+  }
+  // lanes i and i ^ 8 hold tokens 2(i & 7) and 2(i & 7) + 1 (row_ror:8
+  // swaps them): lane i < 8 packs head 2r, lane i >= 8 head 2r + 1, both
+  // for token pair k = i & 7
+  const half2_t own = {static_cast<_Float16>(pr[0]), static_cast<_Float16>(pr[1])};
+  const uint32_t ownu = __builtin_bit_cast(uint32_t, own);
+  const uint32_t other = static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(ownu), 0x128, 0xf, 0xf, false));
+  pbuf[lm.i * 4 + lm.r] = __builtin_amdgcn_perm(other, ownu, lm.pack_sel);
+  __builtin_amdgcn_wave_barrier();
+  const uint4 G4 = *reinterpret_cast<const uint4*>(&pbuf[lm.i * 4]);
+  const uint32_t Gp[4] = {G4.x, G4.y, G4.z, G4.w};  // Gp[j]: heads 2j (lanes 0-7), 2j+1 (8-15)
+  __builtin_amdgcn_wave_barrier();
+
+  // ---- PV: o[h][s] += sum over token pairs k of p[h][2k..2k+1] . v
+  unroll<2>([&](auto sc_) {
+    constexpr int s2 = decltype(sc_)::value;
+    unroll<4>([&](auto wc) {
+      constexpr int ow = decltype(wc)::value;  // octet ow >> 1, word ow & 1
+      const uint32_t word = vw[s2][ow >> 1][ow & 1];
+      const uint32_t v0 = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false));
+      const uint32_t v1 = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, true));
+      constexpr int k0 = 2 * ow;  // pair index of v0 (tokens 4ow, 4ow + 1)
+      unroll<kG>([&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        o[h][s2] = dot2_f16_bcast<8 * (h & 1) + k0>(o[h][s2], Gp[h >> 1], v0);
+      });
+      unroll<kG>([&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        o[h][s2] = dot2_f16_bcast<8 * (h & 1) + k0 + 1>(o[h][s2], Gp[h >> 1], v1);
+      });
+    });
+  });
+}
+
+// K and V words of the group in the ring slot at LDS pointer slot.
+__device__ __forceinline__ void read_group(const uint8_t* slot, const LaneMap& lm, uint4& kw0,
+                                           uint4& kw1, uint32_t (&vw)[2][2][2]) {
+  kw0 = *reinterpret_cast<const uint4*>(slot + lm.kr0);
+  kw1 = *reinterpret_cast<const uint4*>(slot + lm.kr1);
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int o2 = 0; o2 < 2; ++o2) {
+      const v2i_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(slot + lm.vr[s2][o2]));
+      vw[s2][o2][0] = static_cast<uint32_t>(x[0]);
+      vw[s2][o2][1] = static_cast<uint32_t>(x[1]);
+    }
+  // the slot may be refilled once its bytes are in registers
+  asm volatile("" : : "v"(kw0.x), "v"(kw0.y), "v"(kw0.z), "v"(kw0.w), "v"(kw1.x), "v"(kw1.y),
+               "v"(kw1.z), "v"(kw1.w));
+  asm volatile("" : : "v"(vw[0][0][0]), "v"(vw[0][0][1]), "v"(vw[0][1][0]), "v"(vw[0][1][1]),
+               "v"(vw[1][0][0]), "v"(vw[1][0][1]), "v"(vw[1][1][0]), "v"(vw[1][1][1]));
+}
+
+// Partial output of a finished unit: o / l per head and lse = m + log2 l
+// (natural-log units). fin: 16 floats of LDS.
+__device__ __forceinline__ void finish_unit(const DecodeParams& p, const LaneMap& lm, const Unit& u,
+                                            const Softmax& st, const float (&o)[kG][2],
+                                            float o_scale, float* fin) {
+  float ls[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) ls[j] = row_sum(st.l[j]);
+  if (lm.i == 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      fin[2 * lm.r + j] = ls[j];
+      fin[kG + 2 * lm.r + j] = st.set ? st.m[j] : 0.0f;
     }
   }
   __builtin_amdgcn_wave_barrier();
-  const int64_t bh0 = static_cast<int64_t>(b) * p.num_q_heads + g * kG;
+  const int64_t bh0 = static_cast<int64_t>(u.b) * p.num_q_heads + u.g * kG;
 #pragma unroll
   for (int h = 0; h < kG; ++h) {
-    const float lh = fin[0][h];
+    const float lh = fin[h];
     const float f = lh > 0.0f ? o_scale / lh : 0.0f;
-    float* dst = p.o_part + ((bh0 + h) * p.max_splits + c) * kD + 32 * r + i;
+    float* dst = p.o_part + ((bh0 + h) * p.max_splits + u.c) * kD + 32 * lm.r + lm.i;
     dst[0] = o[h][0] * f;
     dst[16] = o[h][1] * f;
   }
+  const int lane = threadIdx.x;
   if (lane < kG) {
-    const float lh = fin[0][lane];
-    p.lse_part[(bh0 + lane) * p.max_splits + c] =
-        lh > 0.0f ? (fin[1][lane] + __log2f(lh)) * kLn2 : -INFINITY;
+    const float lh = fin[lane];
+    p.lse_part[(bh0 + lane) * p.max_splits + u.c] =
+        lh > 0.0f ? (fin[kG + lane] + __log2f(lh)) * kLn2 : -INFINITY;
   }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// ------------------------------------------------------------ dispatched
+template <int kSlots>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3)))
+decode_gqa_e4m3_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kSlots * kGroupBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t pbuf[16 * 4];  // [lane in row][row]
+  __shared__ float fin[2 * kG];
+  __shared__ float abuf[kG];
+  const int lane = threadIdx.x;
+  int b, g, c, L;
+  if (!find_unit(p, static_cast<int>(blockIdx.x), b, g, c, L)) return;
+  const int log2P = p.page_size == 16 ? 4 : (p.page_size == 32 ? 5 : 6);
+  const Unit u = make_unit(b, g, c, L, p.split_tokens, log2P);
+  const LaneMap lm = lane_map(lane);
+
+  Query q;
+  {
+    const uint32_t* qw = reinterpret_cast<const uint32_t*>(
+        p.q + (static_cast<int64_t>(b) * p.num_q_heads + g * kG) * kD);
+#pragma unroll
+    for (int h = 0; h < kG; ++h) q.qd[h] = qw[h * (kD / 2) + lane];
+  }
+  q.qk_scale = p.k_scale[g] * p.sm_scale_log2;
+  q.o_scale = p.v_scale[g];
+  const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_pages;
+  int pg = -1;
+  if (lane < u.n_pages) pg = bt[u.first_page + lane];
+  // Every compiler-issued load must be complete before the first DMA, or its
+  // own wait for them would also wait for the ring.
+  asm volatile("" : : "v"(q.qd[0]), "v"(q.qd[1]), "v"(q.qd[2]), "v"(q.qd[3]), "v"(q.qd[4]),
+               "v"(q.qd[5]), "v"(q.qd[6]), "v"(q.qd[7]));
+  asm volatile("" : : "v"(q.qk_scale), "v"(q.o_scale), "v"(pg));
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" : : : "memory");
+  finish_query(q);
+  const Pages pgs = page_offsets(p, pg, g);
+  const uint32_t ring0 = lds_addr(ring);
+
+  Softmax st;
+  st.set = false;
+  st.m[0] = st.m[1] = 0.0f;
+  st.l[0] = st.l[1] = 0.0f;
+  float o[kG][2];
+#pragma unroll
+  for (int h = 0; h < kG; ++h) o[h][0] = o[h][1] = 0.0f;
+
+  const int n_groups = u.n_groups;
+  unroll<kSlots>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    if (k < n_groups) issue_group(ring0 + k * kGroupBytes, lm, p, pgs, k, log2P);
+  });
+  for (int g0 = 0; g0 < n_groups; g0 += kSlots) {
+    unroll<kSlots>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      const int gi = g0 + k;
+      if (gi >= n_groups) return;
+      // groups gi + 1 .. gi + kSlots - 1 may still be in flight
+      wait_vm_le(4 * min(kSlots - 1, n_groups - 1 - gi));
+      uint4 kw0, kw1;
+      uint32_t vw[2][2][2];
+      read_group(ring + k * kGroupBytes, lm, kw0, kw1, vw);
+      if (gi + kSlots < n_groups) issue_group(ring0 + k * kGroupBytes, lm, p, pgs, gi + kSlots, log2P);
+      group_math(lm, kw0, kw1, vw, group_tokens(u, pgs, gi, log2P), q, st, o, pbuf, abuf);
+    });
+  }
+  finish_unit(p, lm, u, st, o, q.o_scale, fin);
 }
 
 }  // namespace
@@ -511,6 +657,6 @@ int launch_decode_gqa_e4m3(const DecodeParams& p, int n_split_blocks, int batch,
                            hipStream_t stream) {
   const int64_t units = static_cast<int64_t>(n_split_blocks) * p.num_kv_heads * batch;
   if (units > 0x7FFFFFFF) return launch_decode_gqa(p, true, n_split_blocks, batch, stream);
-  decode_gqa_e4m3_kernel<3, 3><<<dim3(static_cast<uint32_t>(units)), 64, 0, stream>>>(p);
+  decode_gqa_e4m3_kernel<2><<<dim3(static_cast<uint32_t>(units)), 64, 0, stream>>>(p);
   return pkv::launch_status();
 }

@@ -319,3 +319,15 @@ def test_gqa_out_of_pool_pages_left_out_without_tag_check(kv, bad):
         pages[j] = n_pages + 5 if j % 2 == 0 else -3
     out, ref = _gqa_direct_case(kv, vals_k, vals_v, pages, L, hq, P, 112, n_pages)
     assert_close(out, ref, f"gqa out-of-pool pages {bad} {kv}")
+
+
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+def test_batch_above_64(kv):
+    """More requests than one wave has lanes (the e4m3 path's one-workgroup-
+    per-unit launch), ragged lengths including one-token requests."""
+    lens = [int(x) for x in np.random.default_rng(21).integers(1, 400, size=70)]
+    lens[3] = 1
+    lens[40] = 16
+    w = W.custom("b70", 81, lens, hq=16, hkv=2, dk=128, dv=128, page=16, split=64)
+    st = State(w, kv)
+    _check_requests(st, range(0, w.batch, 3))
