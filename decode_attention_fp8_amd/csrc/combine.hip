@@ -12,11 +12,13 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// One workgroup of four waves per (request, query head). The maximum lse is
-// reduced over the whole workgroup; then wave w merges splits w, w+4, ...
-// (each lane owns VPL consecutive values of the head) and the four partial
-// sums meet in LDS.
-template <int VPL>
+// One workgroup of 256 threads per (request, query head). The maximum lse is
+// reduced over the workgroup; then the threads split into P = 256 / (Dv / 4)
+// groups, group sg merging splits sg, sg + P, ... with each thread owning
+// one 16-byte chunk of the head, so a workgroup reads P whole split rows per
+// step and consecutive steps' loads are independent. The P partial sums meet
+// in LDS.
+template <int DV>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
                                                       const int32_t* __restrict__ seq_lens,
@@ -25,72 +27,64 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
                                                       const uint8_t* __restrict__ abort_flags,
                                                       uint16_t* __restrict__ out,
                                                       float* __restrict__ lse_out) {
-  constexpr int kDv = VPL * 64;
-  constexpr int kWaves = 4;
+  constexpr int kC = DV / 4;     // 16-byte chunks per split row
+  constexpr int kP = 256 / kC;   // split rows merged side by side
   const int b = blockIdx.y;
   const int h = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int sg = t / kC, ch = t % kC;
   const int64_t bh = static_cast<int64_t>(b) * heads + h;
   const int32_t L = seq_lens[b];
   const bool aborted = abort_flags && abort_flags[b];
   const bool overflow = L > max_seq_len;
   const int n = (overflow || aborted || L <= 0) ? 0 : (L + split_tokens - 1) / split_tokens;
   const float* lse = lse_part + bh * max_splits;
-  const float* op = o_part + bh * max_splits * kDv;
+  const float4* op = reinterpret_cast<const float4*>(o_part + bh * max_splits * DV);
 
-  __shared__ float red[kWaves];
-  __shared__ float den_s[kWaves];
-  __shared__ float acc_s[kWaves][kDv];
+  __shared__ float red[4];
+  __shared__ float den_s[kP];
+  __shared__ float4 acc_s[kP][kC];
 
   float mx = -INFINITY;
-  for (int c = threadIdx.x; c < n; c += blockDim.x) mx = fmaxf(mx, lse[c]);
+  for (int c = t; c < n; c += 256) mx = fmaxf(mx, lse[c]);
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if (lane == 0) red[wave] = mx;
   __syncthreads();
   const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const bool empty = (M == -INFINITY);
 
-  float acc[VPL];
-#pragma unroll
-  for (int k = 0; k < VPL; ++k) acc[k] = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float den = 0.0f;
   if (!empty) {
-    for (int c = wave; c < n; c += kWaves) {
+#pragma unroll 4
+    for (int c = sg; c < n; c += kP) {
       const float w = exp2f((lse[c] - M) * kLog2e);
+      const float4 v = op[static_cast<int64_t>(c) * kC + ch];
       den += w;
-      const float* src = op + static_cast<int64_t>(c) * kDv + lane * VPL;
-      if constexpr (VPL == 1) {
-        acc[0] += w * src[0];
-      } else if constexpr (VPL == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(src);
-        acc[0] += w * v.x;
-        acc[1] += w * v.y;
-      } else {
-#pragma unroll
-        for (int k = 0; k < VPL; k += 4) {
-          const float4 v = *reinterpret_cast<const float4*>(src + k);
-          acc[k] += w * v.x;
-          acc[k + 1] += w * v.y;
-          acc[k + 2] += w * v.z;
-          acc[k + 3] += w * v.w;
-        }
-      }
+      acc.x += w * v.x;
+      acc.y += w * v.y;
+      acc.z += w * v.z;
+      acc.w += w * v.w;
     }
   }
-#pragma unroll
-  for (int k = 0; k < VPL; ++k) acc_s[wave][lane * VPL + k] = acc[k];
-  if (lane == 0) den_s[wave] = den;
+  acc_s[sg][ch] = acc;
+  if (ch == 0) den_s[sg] = den;
   __syncthreads();
 
-  const float D = den_s[0] + den_s[1] + den_s[2] + den_s[3];
-  for (int d = threadIdx.x; d < kDv; d += blockDim.x) {
-    float x = (acc_s[0][d] + acc_s[1][d] + acc_s[2][d] + acc_s[3][d]) / D;
+  float D = 0.0f;
+#pragma unroll
+  for (int g = 0; g < kP; ++g) D += den_s[g];
+  for (int d = t; d < DV; d += 256) {
+    float x = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kP; ++g) x += reinterpret_cast<const float*>(acc_s[g])[d];
+    x /= D;
     if (aborted || n == 0 || empty) x = 0.0f;
     if (overflow && !aborted) x = NAN;
-    out[bh * kDv + d] = pkv::f32_to_bf16_rne(x);
+    out[bh * DV + d] = pkv::f32_to_bf16_rne(x);
   }
-  if (lse_out && threadIdx.x == 0) {
+  if (lse_out && t == 0) {
     float l = M + __log2f(D) * kLn2;
     if (aborted || n == 0 || empty) l = -INFINITY;
     if (overflow && !aborted) l = NAN;
@@ -98,11 +92,11 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   }
 }
 
-template <int VPL>
+template <int DV>
 int launch(const float* o_part, const float* lse_part, const int32_t* seq_lens, int batch,
            int heads, int split_tokens, int max_splits, int max_seq_len,
            const uint8_t* abort_flags, uint16_t* out, float* lse_out, hipStream_t stream) {
-  combine_kernel<VPL><<<dim3(heads, batch), 256, 0, stream>>>(
+  combine_kernel<DV><<<dim3(heads, batch), 256, 0, stream>>>(
       o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags, out,
       lse_out);
   return pkv::launch_status();
@@ -126,16 +120,16 @@ extern "C" int pkv_combine(const float* o_part, const float* lse_part, const int
   auto* o = static_cast<uint16_t*>(out);
   switch (head_dim_v) {
     case 64:
-      return launch<1>(o_part, lse_part, seq_lens, batch, num_q_heads, split_tokens, max_splits,
+      return launch<64>(o_part, lse_part, seq_lens, batch, num_q_heads, split_tokens, max_splits,
                        max_seq_len, abort_flags, o, lse_out, stream);
     case 128:
-      return launch<2>(o_part, lse_part, seq_lens, batch, num_q_heads, split_tokens, max_splits,
+      return launch<128>(o_part, lse_part, seq_lens, batch, num_q_heads, split_tokens, max_splits,
                        max_seq_len, abort_flags, o, lse_out, stream);
     case 256:
-      return launch<4>(o_part, lse_part, seq_lens, batch, num_q_heads, split_tokens, max_splits,
+      return launch<256>(o_part, lse_part, seq_lens, batch, num_q_heads, split_tokens, max_splits,
                        max_seq_len, abort_flags, o, lse_out, stream);
     case 512:
-      return launch<8>(o_part, lse_part, seq_lens, batch, num_q_heads, split_tokens, max_splits,
+      return launch<512>(o_part, lse_part, seq_lens, batch, num_q_heads, split_tokens, max_splits,
                        max_seq_len, abort_flags, o, lse_out, stream);
     default:
       return PKV_EUNSUPPORTED;
