@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true", help="also time batch 1/8/16/32")
     ap.add_argument("--integrity", action="store_true",
                     help="also time verify on/off at batch 1/2/4/8, context 8692")
+    ap.add_argument("--handoff", action="store_true",
+                    help="also time pkv_requantize_pages: 8192 BF16 pages (Hkv 8, page 16, "
+                         "head dim 128) re-encoded into an e4m3 pool")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -185,6 +188,41 @@ class Runner:
         t1 = time.perf_counter()
         del g
         return (t1 - t0) * 1e3 / steps, dec_ms
+
+
+def time_handoff(steps: int, n_pages: int = 8192):
+    """pkv_requantize_pages over n_pages BF16 pages (Hkv 8, page 16, head dim
+    128; seeded N(0,1) values) into an e4m3 pool, pages in a random order.
+    Bytes moved: 2 B read + 1 B written per value, K and V."""
+    import torch
+
+    import decode_attention_fp8_amd as pkv
+    H, P, D = 8, 16, 128
+    g = torch.Generator(device="cuda").manual_seed(1007)
+    src = pkv.allocate_cache(n_pages, H, P, D, D, "bf16", False, "cuda", poison=False)
+    src.k_pool.copy_(torch.randn(src.k_pool.shape, generator=g, device="cuda"))
+    src.v_pool.copy_(torch.randn(src.v_pool.shape, generator=g, device="cuda"))
+    dst = pkv.allocate_cache(n_pages, H, P, D, D, "fp8", False, "cuda")
+    pkv.pkv_scales_from_amax(src.k_pool.view(n_pages, H, P * D), False, dst.k_scale)
+    pkv.pkv_scales_from_amax(src.v_pool.view(n_pages, H, P * D), False, dst.v_scale)
+    sp = torch.randperm(n_pages, generator=g, device="cuda").to(torch.int32)
+    dp = torch.randperm(n_pages, generator=g, device="cuda").to(torch.int32)
+    tags = torch.randint(0, 2**31 - 1, (n_pages,), generator=g, device="cuda", dtype=torch.int32)
+    for _ in range(3):
+        pkv.pkv_requantize_pages(src, dst, sp, dp, tags)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(steps, 10)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        pkv.pkv_requantize_pages(src, dst, sp, dp, tags)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    moved = n_pages * H * P * D * 2 * 3
+    return {"pages": n_pages, "ms": round(ms, 5), "bytes": moved,
+            "gbs": round(moved / ms / 1e6, 2), "hbm_frac": round(moved / ms / 1e6 / HBM_PEAK_GBS, 4),
+            "kernel": "requant_kernel (bf16 pages -> e4m3, tags)"}
 
 
 def cpu_baseline(w, budget_s: float = 12.0):
@@ -334,6 +372,8 @@ def main():
             rows.append({"batch": B, "ms_verify_on": round(m_on, 5), "ms_noop": round(m_off, 5),
                          "overhead": round((m_on - m_off) / m_off, 4)})
         rec["integrity_cost"] = rows
+    if args.handoff:
+        rec["handoff"] = time_handoff(args.steps)
     if not args.no_cpu_baseline and not w.latent:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

@@ -20,7 +20,8 @@ PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP = 0, -1, -2, -3
 PKV_KV_E4M3, PKV_KV_BF16 = 1, 2
 
 EXPORTS = ("pkv_scales_from_amax", "pkv_append", "pkv_verify", "pkv_decode_attn",
-           "pkv_combine", "pkv_suggest_split", "pkv_strerror", "pkv_version")
+           "pkv_combine", "pkv_requantize_pages", "pkv_suggest_split", "pkv_strerror",
+           "pkv_version")
 
 
 class PkvError(RuntimeError):
@@ -41,7 +42,7 @@ class PkvCacheStruct(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m decode_attention_fp8_amd.build`")
+                          "`python decode_attention_fp8_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     CP = ctypes.POINTER(PkvCacheStruct)
@@ -51,6 +52,7 @@ def _load() -> ctypes.CDLL:
         "pkv_verify": (I32, [CP, P, P, P, I32, I32, P, P]),
         "pkv_decode_attn": (I32, [CP, P, I32, P, P, I32, I32, I32, P, F, I32, I32, P, P, P]),
         "pkv_combine": (I32, [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P]),
+        "pkv_requantize_pages": (I32, [CP, CP, P, P, P, P, I32, P]),
         "pkv_suggest_split": (I32, [CP, I32, I32, I64, I32]),
         "pkv_strerror": (ctypes.c_char_p, [I32]),
         "pkv_version": (I32, []),
@@ -193,6 +195,26 @@ def pkv_append(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor | None,
     _check("pkv_append", _lib.pkv_append(
         ctypes.byref(cs), _ptr(k_new), _ptr(v_new), _ptr(slot), _ptr(token_req),
         _ptr(abort_flags), int(slot.numel()), _stream(stream)))
+
+
+def pkv_requantize_pages(src: Cache, dst: Cache, src_pages: torch.Tensor, dst_pages: torch.Tensor,
+                         new_tags: torch.Tensor | None = None, stream=None) -> None:
+    """Re-encode BF16 pages of src into e4m3 pages of dst; with new_tags, the
+    destination pages' tags in dst.page_tags become new_tags."""
+    _need(src_pages, torch.int32, "src_pages")
+    _need(dst_pages, torch.int32, "dst_pages")
+    if src_pages.numel() != dst_pages.numel():
+        raise ValueError("src_pages and dst_pages differ in length")
+    if new_tags is not None:
+        if new_tags.numel() != src_pages.numel() or new_tags.element_size() != 4:
+            raise ValueError("new_tags: one 32-bit tag per page pair")
+        if dst.page_tags is None:
+            raise ValueError("new_tags needs dst.page_tags")
+    ss, ds = src.struct(), dst.struct()
+    _check("pkv_requantize_pages", _lib.pkv_requantize_pages(
+        ctypes.byref(ss), ctypes.byref(ds), _ptr(src_pages), _ptr(dst_pages), _ptr(new_tags),
+        _ptr(dst.page_tags) if new_tags is not None else None, int(src_pages.numel()),
+        _stream(stream)))
 
 
 def pkv_verify(cache: Cache, block_table: torch.Tensor, expected_tags: torch.Tensor,

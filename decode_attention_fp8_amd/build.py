@@ -1,6 +1,6 @@
 """Build libpkv.so (the HIP kernels and the C ABI) for gfx950, in place.
 
-    python -m decode_attention_fp8_amd.build
+    python decode_attention_fp8_amd/build.py
 
 Compiles every source under csrc/ with hipcc into
 decode_attention_fp8_amd/libpkv.so. No fast-math; packed FP32 instructions

@@ -12,24 +12,6 @@
 
 namespace {
 
-// float32 -> e4m3 code, round to nearest even, saturating, from the IEEE
-// bit layout: 4-bit exponent with bias 7 and 3 mantissa bits; below 2^-6
-// the grid is the multiples of 2^-9.
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return sign | 0x7Fu;   // NaN
-  if (a >= 0x43E00000u) return sign | 0x7Eu;  // |y| >= 448 or infinite
-  if (a < 0x3C800000u) {                      // |y| < 2^-6: count of 2^-9 steps
-    return sign | static_cast<uint32_t>(rintf(__uint_as_float(a) * 512.0f));
-  }
-  uint32_t code = (((a >> 23) - 120u) << 3) | ((a >> 20) & 7u);
-  const uint32_t rem = a & 0xFFFFFu;
-  code += (rem > 0x80000u) || (rem == 0x80000u && (code & 1u));
-  return sign | code;
-}
-
 struct AppendArgs {
   const uint16_t* src;  // bf16 [n][heads][dim]
   uint8_t* pool;        // [pages][heads][P][dim] elements of elem_bytes
@@ -63,24 +45,7 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a, const int32_t
     const uint4 w1 = *reinterpret_cast<const uint4*>(src + 8);
     const int64_t dst_elem = ((page * heads + h) * page_size + row) * a.pool_dim + c * 16;
     if constexpr (kE4M3) {
-      const float s_h = a.scale[h];
-      const uint32_t in[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      uint32_t out[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint32_t pair = in[2 * k + j];
-          const float lo = __uint_as_float(pair << 16);
-          const float hi = __uint_as_float(pair & 0xFFFF0000u);
-          const uint32_t c0 = e4m3_rne_sat(__fdiv_rn(lo, s_h));
-          const uint32_t c1 = e4m3_rne_sat(__fdiv_rn(hi, s_h));
-          word |= (c0 | (c1 << 8)) << (16 * j);
-        }
-        out[k] = word;
-      }
-      *reinterpret_cast<uint4*>(a.pool + dst_elem) = make_uint4(out[0], out[1], out[2], out[3]);
+      *reinterpret_cast<uint4*>(a.pool + dst_elem) = pkv::encode16(w0, w1, a.scale[h]);
     } else {
       uint4* dst = reinterpret_cast<uint4*>(a.pool + dst_elem * 2);
       dst[0] = w0;

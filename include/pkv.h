@@ -222,6 +222,36 @@ int pkv_combine(const float* o_part, const float* lse_part,
                 float* lse_out, hipStream_t stream);
 
 /*
+ * Prefill -> decode handoff of whole pages (section "Quantizing the KV
+ * cache": decode holds the cache as e4m3 while prefill keeps BF16, so a
+ * prefill's pages are re-encoded on their way into the decode pool; section
+ * "Protecting a shared KV cache": a page's tag changes whenever it is
+ * reallocated).
+ *
+ * For every pair i < n_pages, kv head h, row r < page_size and dim d:
+ *   dst->k_pool[dst_pages[i]][h][r][d] =
+ *       RNE_SAT(fl32(src->k_pool[src_pages[i]][h][r][d] / dst->k_scale[h]))
+ *   (V likewise from dst->v_scale; a latent cache converts its whole rows)
+ *   dst_tags[dst_pages[i]] = new_tags[i]        (when both are non-NULL)
+ * with the encoding of pkv_append. The scales are the destination pool's
+ * (set once, e.g. by pkv_scales_from_amax over the prefill pool viewed as
+ * [pages][num_kv_heads][page_size * head_dim]); values beyond them saturate.
+ *   src:       a PKV_KV_BF16 cache; dst: a PKV_KV_E4M3 cache with the same
+ *              page size, kv heads, head dims and layout (separate or latent V)
+ *   src_pages, dst_pages: int32 [n_pages] device arrays; a pair naming a
+ *              page outside its pool is skipped (nothing written)
+ *   new_tags:  uint32 [n_pages] or NULL; dst_tags: uint32 [dst num_pages]
+ *              (the destination's page tags) or NULL; both or neither
+ * Two pairs with the same destination page race. Device pointers, caller-owned.
+ * EINVAL: NULL pointers, dtypes or geometries that do not match, only one of
+ * new_tags / dst_tags, n_pages < 0, pools not 16-byte aligned.
+ */
+int pkv_requantize_pages(const pkv_cache* src, const pkv_cache* dst,
+                         const int32_t* src_pages, const int32_t* dst_pages,
+                         const uint32_t* new_tags, uint32_t* dst_tags, int32_t n_pages,
+                         hipStream_t stream);
+
+/*
  * Host helper: a split size for pkv_decode_attn on this cache and batch.
  *   num_q_heads   query heads of the batch (as passed to pkv_decode_attn)
  *   batch         requests in the batch
