@@ -67,3 +67,34 @@ def weights(q, k, sm_scale: float) -> np.ndarray:
         e = np.exp(s - s.max())
         out.append(e / e.sum())
     return np.stack(out)
+
+
+def attend_drafts(q, k, v, sm_scale: float):
+    """Decode attention of a request whose last T cached tokens are the current
+    token and its T - 1 draft tokens, verified together (speculative decoding).
+
+    Cloudflare's post on the infrastructure for serving extra-large models
+    (its speculative decoding section) has a small draft model propose a few
+    future tokens that the target model accepts or rejects in one forward
+    pass; in that pass the drafts go through attention together.
+    Each query position sees the context up to and including itself and no
+    later draft (causal among the drafts): query j (0 <= j < T), the token at
+    position L - T + j, attends to cached tokens 0 .. L - T + j.
+
+    q: [T, Hq, Dk]; k: [L, Hkv, Dk]; v: [L, Hkv, Dv] (float64, dequantised).
+    Returns (o [T, Hq, Dv], lse [T, Hq]); a query that sees no token (L < T
+    leaves the first ones without any) gets o = 0 and lse = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    T, hq = q.shape[0], q.shape[1]
+    L = k.shape[0]
+    o = np.zeros((T, hq, v.shape[2]), dtype=np.float64)
+    lse = np.full((T, hq), -np.inf, dtype=np.float64)
+    for j in range(T):
+        n = L - T + j + 1
+        if n <= 0:
+            continue
+        o[j], lse[j] = attend(q[j], k[:n], v[:n], sm_scale)
+    return o, lse

@@ -138,3 +138,70 @@ def test_planted_sign_error_is_caught():
     o, _ = attention.attend(-q, k, v, 0.5)  # mutant: negated scores
     ob, _ = _brute(q, k, v, 0.5)
     assert not np.allclose(o, ob, atol=1e-6)
+
+
+# ------------------------------------------------- drafts verified together
+def _masked_brute(q, k, v, sm):
+    """The same quantity written as one masked softmax per (query, head):
+    scores of tokens after the query's own position are -inf; math.fsum and
+    math.exp only."""
+    import math
+    T, hq, _ = q.shape
+    L, hkv, _ = k.shape
+    g = hq // hkv
+    o = np.zeros((T, hq, v.shape[2]))
+    for j in range(T):
+        for h in range(hq):
+            s = []
+            for t in range(L):
+                if t > L - T + j:
+                    s.append(-math.inf)
+                else:
+                    s.append(sm * math.fsum(q[j, h, d] * k[t, h // g, d] for d in range(k.shape[2])))
+            m = max(s)
+            e = [math.exp(x - m) if x != -math.inf else 0.0 for x in s]
+            den = math.fsum(e)
+            for d in range(v.shape[2]):
+                o[j, h, d] = math.fsum(e[t] * v[t, h // g, d] for t in range(L)) / den
+    return o
+
+
+def test_drafts_match_masked_brute_force():
+    rng = np.random.default_rng(31)
+    T, L, hq, hkv, D = 3, 9, 4, 2, 5
+    q = rng.standard_normal((T, hq, D))
+    k = rng.standard_normal((L, hkv, D))
+    v = rng.standard_normal((L, hkv, D))
+    o, lse = attention.attend_drafts(q, k, v, 0.7)
+    assert np.allclose(o, _masked_brute(q, k, v, 0.7), rtol=0, atol=1e-12)
+    assert np.all(np.isfinite(lse))
+
+
+def test_drafts_single_query_is_plain_decode_and_rows_are_prefix_decodes():
+    rng = np.random.default_rng(32)
+    L, hq, hkv, D = 12, 4, 1, 6
+    q = rng.standard_normal((4, hq, D))
+    k = rng.standard_normal((L, hkv, D))
+    v = rng.standard_normal((L, hkv, D))
+    o1, l1 = attention.attend_drafts(q[:1], k, v, 0.3)
+    o, l = attention.attend(q[0], k, v, 0.3)
+    assert np.array_equal(o1[0], o) and np.array_equal(l1[0], l)
+    # the first of 4 drafts sees 9 tokens, the last all 12
+    o4, _ = attention.attend_drafts(q, k, v, 0.3)
+    assert np.allclose(o4[0], attention.attend(q[0], k[:9], v[:9], 0.3)[0], atol=1e-12)
+    assert np.allclose(o4[3], attention.attend(q[3], k, v, 0.3)[0], atol=1e-12)
+
+
+def test_drafts_edge_cases():
+    rng = np.random.default_rng(33)
+    D = 4
+    v = rng.standard_normal((3, 1, D))
+    k = rng.standard_normal((3, 1, D))
+    q = rng.standard_normal((3, 2, D))
+    # L == T: the first query sees only token 0, so its output is v_0 exactly
+    o, lse = attention.attend_drafts(q, k, v, 1.0)
+    assert np.allclose(o[0, :, :], v[0, 0][None, :], atol=1e-15)
+    # L < T: the first queries see nothing
+    o, lse = attention.attend_drafts(q, k[:2], v[:2], 1.0)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+    assert np.allclose(o[1], v[0, 0][None, :], atol=1e-15)
