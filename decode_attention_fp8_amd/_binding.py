@@ -20,7 +20,7 @@ PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP = 0, -1, -2, -3
 PKV_KV_E4M3, PKV_KV_BF16 = 1, 2
 
 EXPORTS = ("pkv_scales_from_amax", "pkv_append", "pkv_verify", "pkv_decode_attn",
-           "pkv_combine", "pkv_requantize_pages", "pkv_suggest_split", "pkv_strerror",
+           "pkv_combine", "pkv_decode_attn_drafts", "pkv_requantize_pages", "pkv_suggest_split", "pkv_strerror",
            "pkv_version")
 
 
@@ -52,6 +52,8 @@ def _load() -> ctypes.CDLL:
         "pkv_verify": (I32, [CP, P, P, P, I32, I32, P, P]),
         "pkv_decode_attn": (I32, [CP, P, I32, P, P, I32, I32, I32, P, F, I32, I32, P, P, P]),
         "pkv_combine": (I32, [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P]),
+        "pkv_decode_attn_drafts": (I32, [CP, P, I32, I32, P, P, I32, I32, I32, P, F, I32, I32, P,
+                                         P, P]),
         "pkv_requantize_pages": (I32, [CP, CP, P, P, P, P, I32, P]),
         "pkv_suggest_split": (I32, [CP, I32, I32, I64, I32]),
         "pkv_strerror": (ctypes.c_char_p, [I32]),
@@ -195,6 +197,25 @@ def pkv_append(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor | None,
     _check("pkv_append", _lib.pkv_append(
         ctypes.byref(cs), _ptr(k_new), _ptr(v_new), _ptr(slot), _ptr(token_req),
         _ptr(abort_flags), int(slot.numel()), _stream(stream)))
+
+
+def pkv_decode_attn_drafts(cache: Cache, q: torch.Tensor, block_table: torch.Tensor,
+                           seq_lens: torch.Tensor, max_seq_len: int,
+                           abort_flags: torch.Tensor | None, sm_scale: float, split_tokens: int,
+                           o_part: torch.Tensor, lse_part: torch.Tensor, stream=None) -> None:
+    """q: bf16 [B, q_len, Hq, Dk] (a token and its drafts per request);
+    o_part [B, q_len*Hq, max_splits, Dv], lse_part [B, q_len*Hq, max_splits]."""
+    _need(q, torch.bfloat16, "q")
+    B, T, Hq, _ = q.shape
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    if o_part.shape[1] != T * Hq or lse_part.shape[1] != T * Hq:
+        raise ValueError("o_part / lse_part need q_len * num_q_heads rows per request")
+    cs = cache.struct()
+    _check("pkv_decode_attn_drafts", _lib.pkv_decode_attn_drafts(
+        ctypes.byref(cs), _ptr(q), Hq, T, _ptr(block_table), _ptr(seq_lens), B,
+        int(block_table.shape[1]), int(max_seq_len), _ptr(abort_flags), float(sm_scale),
+        int(split_tokens), int(o_part.shape[2]), _ptr(o_part), _ptr(lse_part), _stream(stream)))
 
 
 def pkv_requantize_pages(src: Cache, dst: Cache, src_pages: torch.Tensor, dst_pages: torch.Tensor,

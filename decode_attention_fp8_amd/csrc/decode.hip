@@ -238,6 +238,7 @@ extern "C" int pkv_decode_attn(const pkv_cache* cache, const void* q, int32_t nu
   p.max_splits = max_splits;
   p.head_groups = head_groups;
   p.batch = batch;
+  p.q_len = 1;
   p.v_row = latent ? dk : dv;
   p.sm_scale_log2 = sm_scale * kLog2e;
   const bool e4m3 = cache->dtype == PKV_KV_E4M3;
@@ -250,4 +251,56 @@ extern "C" int pkv_decode_attn(const pkv_cache* cache, const void* q, int32_t nu
     return launch_decode_gqa(p, e4m3, static_cast<int>(n_split_blocks), batch, stream);
   return e4m3 ? dispatch<true>(p, latent, dk, G, static_cast<int>(n_split_blocks), batch, stream)
               : dispatch<false>(p, latent, dk, G, static_cast<int>(n_split_blocks), batch, stream);
+}
+
+extern "C" int pkv_decode_attn_drafts(const pkv_cache* cache, const void* q, int32_t num_q_heads,
+                                      int32_t q_len, const int32_t* block_table,
+                                      const int32_t* seq_lens, int32_t batch, int32_t max_pages,
+                                      int32_t max_seq_len, const uint8_t* abort_flags,
+                                      float sm_scale, int32_t split_tokens, int32_t max_splits,
+                                      float* o_part, float* lse_part, hipStream_t stream) {
+  int st = pkv::check_cache(cache);
+  if (st) return st;
+  if (!q || !block_table || !seq_lens || !o_part || !lse_part) return PKV_EINVAL;
+  if (batch < 0 || max_pages < 1 || max_seq_len < 0 || max_splits < 1) return PKV_EINVAL;
+  if (q_len < 1 || q_len > 64) return PKV_EINVAL;
+  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads) return PKV_EINVAL;
+  if (split_tokens < cache->page_size || split_tokens % cache->page_size) return PKV_EINVAL;
+  if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_pages) * cache->page_size)
+    return PKV_EINVAL;
+  const int64_t n_split_blocks = pkv::cdiv(max_seq_len, split_tokens);
+  if (n_split_blocks > max_splits) return PKV_EINVAL;
+  if (!(sm_scale == sm_scale)) return PKV_EINVAL;
+  const bool latent = cache->v_pool == nullptr;
+  if (!drafts_path_supported(cache->head_dim_k, cache->head_dim_v, latent,
+                             cache->dtype == PKV_KV_E4M3))
+    return PKV_EUNSUPPORTED;
+  if (batch == 0 || n_split_blocks == 0) return PKV_OK;
+  const int G = num_q_heads / cache->num_kv_heads;
+  const int row_groups = static_cast<int>((static_cast<int64_t>(q_len) * G + 31) / 32);
+  Params p{};
+  p.k_pool = cache->k_pool;
+  p.v_pool = cache->v_pool;
+  p.k_scale = cache->k_scale;
+  p.v_scale = cache->v_scale;
+  p.q = static_cast<const uint16_t*>(q);
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.abort_flags = abort_flags;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.num_pages = cache->num_pages;
+  p.page_size = cache->page_size;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.num_q_heads = num_q_heads;
+  p.max_pages = max_pages;
+  p.max_seq_len = max_seq_len;
+  p.split_tokens = split_tokens;
+  p.max_splits = max_splits;
+  p.head_groups = 1;
+  p.batch = batch;
+  p.q_len = q_len;
+  p.v_row = cache->head_dim_v;
+  p.sm_scale_log2 = sm_scale * kLog2e;
+  return launch_decode_drafts(p, static_cast<int>(n_split_blocks), batch, row_groups, stream);
 }

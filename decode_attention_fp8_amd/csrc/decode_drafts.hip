@@ -1,0 +1,354 @@
+// Decode attention of a token and its drafts verified together, over an e4m3
+// cache with head dim 128.
+//
+// Cloudflare's post on serving extra-large models, speculative decoding
+// section: a small draft model proposes a few future tokens, and the target
+// model accepts or rejects them in one forward pass. In that pass each
+// request has q_len query positions (the current token and q_len - 1 drafts,
+// whose K and V were appended this step); query j sees the cached tokens up
+// to and including its own position L - q_len + j. "Smaller, faster, safer",
+// section "Quantizing the KV cache": the cache is read as e4m3 and converted
+// on the way in.
+//
+// With G query heads per kv head, a kv head serves q_len * G query rows, so
+// QK^T and PV are real dense contractions (32 rows for 4 positions of 8
+// heads): this kernel runs them on MFMA 32x32x16 with fp32 accumulation, QK^T
+// in bf16 (the query is bf16; K codes convert exactly) and PV in f16 (V codes
+// convert exactly; numerators rounded to f16, 3 bits more than bf16).
+//
+// One wave per work unit (request, kv head, split, group of 32 query rows),
+// in the unit order of the one-dimensional launches. The split is processed
+// in tiles of 32 tokens; a tile's K and V bytes (4 KB each) travel HBM -> LDS
+// by direct-to-LDS loads into a ring of kSlots tiles.
+//
+// MFMA operand layouts (32x32x16, lane l, c = l % 32, h = l / 32):
+//   A: row c, k 8h .. 8h+7;  B: column c, k 8h .. 8h+7;
+//   D element i: row 8(i/4) + 4h + i%4, column c.
+// S^T = K Q^T per tile (M = tokens, N = query rows, 8 k-steps of 16 dims:
+// k-step s covers dims 32(s/2) + 16h + 8(s%2) .. +7, so one 16-byte K read
+// serves two k-steps). A lane then holds query row c's scores for tokens
+// {8(i/4) + 4h + i%4}; those are the A operand of O += P V (M = query rows,
+// k = tokens) once V is read in the same token order with ds_read_tr8_b64,
+// which hands lane i of a 16-lane group byte i (one dim) of 8 rows.
+//
+// Softmax: log2 domain, per query row a reference max set by the row's first
+// valid scores; a later score more than kTau above it raises it and rescales
+// the row's accumulators (a uniform branch real scores almost never take), so
+// numerators stay at most 2^kTau, inside f16 range.
+#include "common.h"
+#include "decode_params.h"
+#include "unit_order.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
+
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kTau = 15.0f;      // f16 numerators stay at most 2^kTau
+constexpr float kMUnset = -1e30f;  // reference max of a row with no valid score yet
+constexpr int kD = 128;
+constexpr int kTile = 32;                    // tokens per tile
+constexpr int kHalf = kTile * kD;            // K (or V) bytes of a tile
+constexpr int kTileBytes = 2 * kHalf;        // K then V: 8 KB
+constexpr int kSlots = 2;
+constexpr int kMaxUnitPages = 64;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const uint8_t* base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(base)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ f16x8_t fp8x8_to_f16(uint32_t w0, uint32_t w1) {
+  const f16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const f16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const f16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const f16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  return f16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Tile layouts: K chunk c of token row t at c ^ ((t >> 1) & 7) (the 32 rows
+// a K read touches at one chunk land on distinct bank groups); V chunk c of
+// row t at c ^ vswz(t), vswz(t) = bits 1 and 3 of t moved to bits 1 and 2
+// (the 8 rows x 2 chunks of a half-wave's transposing read, likewise).
+__device__ __forceinline__ uint32_t kswz(uint32_t t) { return (t >> 1) & 7u; }
+__device__ __forceinline__ uint32_t vswz(uint32_t t) {
+  return (((t >> 1) & 1u) << 1) | (((t >> 3) & 1u) << 2);
+}
+
+__global__ void __launch_bounds__(64) decode_drafts_kernel(DecodeParams p, int row_groups) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kSlots * kTileBytes];
+  __shared__ float rowbuf[2][32];
+  const int lane = threadIdx.x;
+  const int col = lane & 31, hl = lane >> 5;
+  const int rg = static_cast<int>(blockIdx.x) % row_groups;
+  int b, g, c, L;
+  if (!pkv::find_unit(p, static_cast<int>(blockIdx.x) / row_groups, b, g, c, L)) return;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int T = p.q_len;
+  const int rows = T * G;
+  const int t_begin = c * p.split_tokens;
+  const int t_end = min(L, t_begin + p.split_tokens);
+  const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
+  const int P = p.page_size;
+  const int log2P = P == 16 ? 4 : (P == 32 ? 5 : 6);
+
+  // this lane's query row (S^T column): position j, head g*G + hh
+  const int r_mine = 32 * rg + col;
+  const bool row_ok = r_mine < rows;
+  const int j_mine = row_ok ? r_mine / G : 0;
+  // tokens this row may see inside the unit: [t_begin, lim)
+  const int lim = row_ok ? min(t_end, L - T + j_mine + 1) : t_begin;
+
+  // query as B operands: k-step s covers dims 32(s/2) + 16h + 8(s%2) .. +7
+  bf16x8_t qf[8];
+  {
+    const int hh = row_ok ? r_mine - j_mine * G : 0;
+    const uint16_t* qrow =
+        p.q + ((static_cast<int64_t>(b) * T + j_mine) * p.num_q_heads + g * G + hh) * kD;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if (row_ok) {
+        qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * (s >> 1) + 16 * hl + 8 * (s & 1));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[s][e] = static_cast<__bf16>(0.0f);
+      }
+    }
+  }
+  const float qk_scale = p.k_scale[g] * p.sm_scale_log2;
+  const float o_scale = p.v_scale[g];
+
+  // the unit's pages: lane j holds the byte offset of (page j, kv head g)
+  const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_pages;
+  const int first_page = t_begin >> log2P;
+  const int n_pages = (t_end - t_begin + P - 1) >> log2P;
+  int pg = -1;
+  if (lane < n_pages) pg = bt[first_page + lane];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) asm volatile("" : : "v"(qf[s]));
+  asm volatile("" : : "v"(qk_scale), "v"(o_scale), "v"(pg));
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" : : : "memory");
+  const bool pg_ok = pg >= 0 && pg < p.num_pages;
+  const uint64_t valid = __ballot(pg_ok);
+  const int64_t blk = (static_cast<int64_t>(pg_ok ? pg : 0) * p.num_kv_heads + g) *
+                      (static_cast<int64_t>(P) * kD);
+  const int off_lo = static_cast<int>(static_cast<uint32_t>(blk));
+  const int off_hi = static_cast<int>(static_cast<uint32_t>(static_cast<uint64_t>(blk) >> 32));
+
+  // DMA source offsets inside a 16-token group block: lane L fills LDS chunk
+  // position L & 7 of group row L >> 3 (first 1 KB) and 8 + (L >> 3)
+  const uint32_t dr0 = lane >> 3, dr1 = 8 + (lane >> 3), dpos = lane & 7;
+  const uint32_t koff0 = dr0 * kD + ((dpos ^ kswz(dr0)) << 4);
+  const uint32_t koff1 = dr1 * kD + ((dpos ^ kswz(dr1)) << 4);
+  const uint32_t voff0 = dr0 * kD + ((dpos ^ vswz(dr0)) << 4);
+  const uint32_t voff1 = dr1 * kD + ((dpos ^ vswz(dr1)) << 4);
+  const uint8_t* kpool = static_cast<const uint8_t*>(p.k_pool);
+  const uint8_t* vpool = static_cast<const uint8_t*>(p.v_pool);
+  const uint32_t ring0 = lds_addr(ring);
+
+  auto group_base = [&](int gg) __attribute__((always_inline)) {
+    const int j = (gg << 4) >> log2P;
+    const uint64_t off =
+        (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(off_hi, j))) << 32) |
+        static_cast<uint32_t>(__builtin_amdgcn_readlane(off_lo, j));
+    return off + static_cast<uint32_t>(((gg << 4) & (P - 1)) * kD);
+  };
+  // 8 loads per tile, always: a 16-token group past the unit's end loads the
+  // tile's first group again (its rows are masked and their V zeroed)
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const uint32_t slot = ring0 + (t % kSlots) * kTileBytes;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int gg = (t_begin + kTile * t + 16 * x < t_end) ? 2 * t + x : 2 * t;
+      const uint64_t off = group_base(gg);
+      dma16(slot + 2048 * x, koff0, kpool + off);
+      dma16(slot + 2048 * x + 1024, koff1, kpool + off);
+      dma16(slot + kHalf + 2048 * x, voff0, vpool + off);
+      dma16(slot + kHalf + 2048 * x + 1024, voff1, vpool + off);
+    }
+  };
+
+  // per-lane LDS offsets. K operand, chunk 2kp + h of token row col.
+  // V operand of (k-step u, dim block nb): the 16 lanes of a group address
+  // row 16u + tokv (the e-th token of the step in P's order, e = (l & 15) / 2)
+  // half l & 1 of chunk 2nb + ((l >> 4) & 1).
+  uint32_t koff[4];
+#pragma unroll
+  for (int kp = 0; kp < 4; ++kp)
+    koff[kp] = col * kD + ((static_cast<uint32_t>(2 * kp + hl) ^ kswz(col)) << 4);
+  const int e_row = (lane & 15) >> 1;
+  const int tokv = 4 * hl + (e_row & 3) + 8 * (e_row >> 2);
+  const int a16 = (lane >> 4) & 1;
+  uint32_t voff[2][4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const uint32_t row = 16 * u + tokv;
+      voff[u][nb] = kHalf + row * kD + ((static_cast<uint32_t>(2 * nb + a16) ^ vswz(row)) << 4) +
+                    8 * (lane & 1);
+    }
+
+  floatx16_t O[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[nb][i] = 0.0f;
+  float m = kMUnset;  // reference max of query row col (both halves agree)
+  float l = 0.0f;     // this lane's part of row col's denominator
+
+#pragma unroll
+  for (int k = 0; k < kSlots - 1; ++k)
+    if (k < n_tiles) issue(k);
+  for (int t = 0; t < n_tiles; ++t) {
+    if (t + kSlots - 1 < n_tiles) {
+      issue(t + kSlots - 1);
+      wait_vm<8 * (kSlots - 1)>();
+    } else {
+      wait_vm<0>();
+    }
+    uint8_t* buf = ring + (t % kSlots) * kTileBytes;
+    const int tile0 = t_begin + kTile * t;
+    // rows past the unit or of a page outside the pool: V to zero (their
+    // scores are masked, and 0 * NaN must not reach the accumulators)
+    const bool g0_ok = ((valid >> (((2 * t) << 4) >> log2P)) & 1u) != 0;
+    const bool g1_ok = tile0 + 16 < t_end && ((valid >> (((2 * t + 1) << 4) >> log2P)) & 1u) != 0;
+    const int nv = min(kTile, t_end - tile0);
+    if (!g0_ok || !g1_ok || nv < kTile) {
+      for (int q = lane; q < kTile * (kD / 16); q += 64) {
+        const int row = q >> 3;
+        const bool keep = row < nv && (row < 16 ? g0_ok : g1_ok);
+        if (!keep) *reinterpret_cast<uint4*>(buf + kHalf + 16 * q) = make_uint4(0u, 0u, 0u, 0u);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+
+    // ---- S^T = K Q^T for the tile
+    floatx16_t st;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st[i] = 0.0f;
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) {
+      const uint4 kq = *reinterpret_cast<const uint4*>(buf + koff[kp]);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(kq.x, kq.y), qf[2 * kp], st, 0, 0, 0);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(kq.z, kq.w), qf[2 * kp + 1], st, 0, 0, 0);
+    }
+    // st[i]: token tile0 + 8(i/4) + 4h + i%4 of query row col
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tt = 8 * (i >> 2) + 4 * hl + (i & 3);
+      const bool ok = tile0 + tt < lim && (tt < 16 ? g0_ok : g1_ok);
+      st[i] = ok ? st[i] * qk_scale : -INFINITY;
+      tmax = fmaxf(tmax, st[i]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    if (m == kMUnset && tmax > -INFINITY) m = tmax;
+    if (__any(tmax > m + kTau)) {
+      // rare: raise the reference max of the rows that need it, rescale
+      const float mn = tmax > m + kTau ? tmax : m;
+      const float al = __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      l *= al;
+      if (hl == 0) rowbuf[0][col] = al;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float a = rowbuf[0][8 * (i >> 2) + 4 * hl + (i & 3)];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) O[nb][i] *= a;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+
+    // ---- O += P V, two k-steps of 16 tokens
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      f16x8_t pf;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float pr = __builtin_amdgcn_exp2f(st[8 * u + k] - m);
+        l += pr;
+        pf[k] = static_cast<_Float16>(pr);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const v2i_t r8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(buf + voff[u][nb]));
+        O[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            pf, fp8x8_to_f16(static_cast<uint32_t>(r8[0]), static_cast<uint32_t>(r8[1])), O[nb],
+            0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- finish: per query row, o / l and lse = m + log2 l (natural-log units)
+  l += __shfl_xor(l, 32);
+  if (hl == 0) {
+    rowbuf[0][col] = l;
+    rowbuf[1][col] = m;
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int64_t heads_all = static_cast<int64_t>(T) * p.num_q_heads;
+  auto out_head = [&](int r) __attribute__((always_inline)) {
+    const int j = r / G;
+    return static_cast<int64_t>(b) * heads_all + static_cast<int64_t>(j) * p.num_q_heads + g * G +
+           (r - j * G);
+  };
+  if (hl == 0 && row_ok)
+    p.lse_part[out_head(r_mine) * p.max_splits + c] =
+        l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = 8 * (i >> 2) + 4 * hl + (i & 3);
+    const int r = 32 * rg + row;
+    if (r >= rows) continue;
+    const float lr = rowbuf[0][row];
+    const float f = lr > 0.0f ? o_scale / lr : 0.0f;
+    float* dst = p.o_part + (out_head(r) * p.max_splits + c) * kD + col;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) dst[32 * nb] = O[nb][i] * f;
+  }
+}
+
+}  // namespace
+
+bool drafts_path_supported(int dk, int dv, bool latent, bool e4m3) {
+  return e4m3 && !latent && dk == kD && dv == kD;
+}
+
+int launch_decode_drafts(const DecodeParams& p, int n_split_blocks, int batch, int row_groups,
+                         hipStream_t stream) {
+  if (p.split_tokens > kMaxUnitPages * p.page_size) return PKV_EUNSUPPORTED;
+  const int64_t units =
+      static_cast<int64_t>(n_split_blocks) * p.num_kv_heads * batch * row_groups;
+  if (units > 0x7FFFFFFF) return PKV_EUNSUPPORTED;
+  decode_drafts_kernel<<<dim3(static_cast<uint32_t>(units)), 64, 0, stream>>>(p, row_groups);
+  return pkv::launch_status();
+}

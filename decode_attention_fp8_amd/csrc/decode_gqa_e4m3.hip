@@ -50,6 +50,7 @@
 
 #include "common.h"
 #include "decode_params.h"
+#include "unit_order.h"
 
 namespace {
 
@@ -177,94 +178,6 @@ __device__ __forceinline__ uint32_t kswz(uint32_t t) { return (t >> 1) & 7u; }
 __device__ __forceinline__ uint32_t vswz(uint32_t t) {
   const uint32_t j = (t >> 1) & 3u;
   return (j & 1u) | ((j & 2u) << 1);
-}
-
-// Inclusive prefix sum over the wave.
-__device__ __forceinline__ int wave_scan(int x) {
-  const int lane = threadIdx.x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  return x;
-}
-
-// Work unit u of the one-dimensional launch -> (request b, kv head g,
-// split c). The hardware dispatcher hands out workgroups in index order, so
-// the order is chosen for it: every full split first (request, split, kv
-// head), then each request's last split, longest first (request order for
-// batches above 64), so the launch ends on its shortest units; then indices
-// with no unit (the launch is sized for max_seq_len), which exit at once.
-// Aborted requests and empty or over-long contexts have no units.
-__device__ bool find_unit(const DecodeParams& p, int u, int& b_out, int& g_out, int& c_out,
-                          int& L_out) {
-  const int lane = threadIdx.x;
-  const int S = p.split_tokens, H = p.num_kv_heads;
-  int L = 0;
-  auto splits = [&](int j) __attribute__((always_inline)) {
-    int n = 0;
-    L = 0;
-    if (j < p.batch) {
-      L = p.seq_lens[j];
-      const bool ab = p.abort_flags && p.abort_flags[j];
-      if (!ab && L > 0 && L <= p.max_seq_len) n = (L + S - 1) / S;
-    }
-    return n;
-  };
-  int base = 0;  // full units of the requests before this batch of 64
-  for (int b0 = 0; b0 < p.batch; b0 += 64) {
-    const int n = splits(b0 + lane);
-    const int full = n > 0 ? (n - 1) * H : 0;
-    const int incl = wave_scan(full);
-    const int total = __builtin_amdgcn_readlane(incl, 63);
-    if (u < base + total) {
-      const int bl = __popcll(__ballot(base + incl <= u));
-      const int r = u - base - __builtin_amdgcn_readlane(incl - full, bl);
-      b_out = b0 + bl;
-      c_out = r / H;
-      g_out = r - c_out * H;
-      L_out = __builtin_amdgcn_readlane(L, bl);
-      return true;
-    }
-    base += total;
-  }
-  int u2 = u - base;
-  if (p.batch <= 64) {
-    const int n = splits(lane);
-    const int psz = n > 0 ? L - (n - 1) * S : -1;
-    if (u2 >= __popcll(__ballot(n > 0)) * H) return false;
-    int rank = 0;
-    for (int k = 0; k < 64; ++k) {
-      const int pk = __builtin_amdgcn_readlane(psz, k);
-      rank += (pk > psz || (pk == psz && k < lane)) ? 1 : 0;
-    }
-    const int R = u2 / H;
-    const uint64_t hit = __ballot(n > 0 && rank == R);
-    const int bl = static_cast<int>(__builtin_ctzll(hit));
-    b_out = bl;
-    g_out = u2 - R * H;
-    c_out = __builtin_amdgcn_readlane(n, bl) - 1;
-    L_out = __builtin_amdgcn_readlane(L, bl);
-    return true;
-  }
-  for (int b0 = 0; b0 < p.batch; b0 += 64) {
-    const int n = splits(b0 + lane);
-    const int part = n > 0 ? H : 0;
-    const int incl = wave_scan(part);
-    const int total = __builtin_amdgcn_readlane(incl, 63);
-    if (u2 < total) {
-      const int bl = __popcll(__ballot(incl <= u2));
-      const int r = u2 - __builtin_amdgcn_readlane(incl - part, bl);
-      b_out = b0 + bl;
-      g_out = r;
-      c_out = __builtin_amdgcn_readlane(n, bl) - 1;
-      L_out = __builtin_amdgcn_readlane(L, bl);
-      return true;
-    }
-    u2 -= total;
-  }
-  return false;
 }
 
 // Per-lane constants of the lane layout above.
@@ -588,7 +501,7 @@ decode_gqa_e4m3_kernel(DecodeParams p) {
   __shared__ float abuf[kG];
   const int lane = threadIdx.x;
   int b, g, c, L;
-  if (!find_unit(p, static_cast<int>(blockIdx.x), b, g, c, L)) return;
+  if (!pkv::find_unit(p, static_cast<int>(blockIdx.x), b, g, c, L)) return;
   const int log2P = p.page_size == 16 ? 4 : (p.page_size == 32 ? 5 : 6);
   const Unit u = make_unit(b, g, c, L, p.split_tokens, log2P);
   const LaneMap lm = lane_map(lane);

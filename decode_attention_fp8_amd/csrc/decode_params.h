@@ -18,6 +18,7 @@ struct DecodeParams {
   int num_pages, page_size, num_kv_heads, num_q_heads, max_pages, max_seq_len;
   int split_tokens, max_splits, head_groups;
   int batch;
+  int q_len;            // query positions per request (drafts verified together)
   int v_row;            // elements per V row in v_pool
   float sm_scale_log2;  // sm_scale * log2(e)
 };
@@ -33,6 +34,11 @@ bool gqa_e4m3_path_supported(int dk, int dv, int group, bool latent, int split_t
                              int page_size);
 int launch_decode_gqa_e4m3(const DecodeParams& p, int n_split_blocks, int batch,
                            hipStream_t stream);
+
+// several query positions per request (a token and its drafts), e4m3, head dim 128
+bool drafts_path_supported(int dk, int dv, bool latent, bool e4m3);
+int launch_decode_drafts(const DecodeParams& p, int n_split_blocks, int batch, int row_groups,
+                         hipStream_t stream);
 
 // wide-head kernel for one latent kv head (576 / 512), page size 64
 bool mla_fast_path_supported(int dk, int dv, int num_kv_heads, int num_q_heads, int page_size,

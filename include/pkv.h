@@ -222,6 +222,37 @@ int pkv_combine(const float* o_part, const float* lse_part,
                 float* lse_out, hipStream_t stream);
 
 /*
+ * Decode attention of a token and its drafts verified together (Cloudflare's
+ * post on serving extra-large models, speculative decoding section: a draft
+ * model proposes a few future tokens and the target model checks them in
+ * one forward pass; "Smaller, faster, safer", section "Quantizing the KV
+ * cache": the cache is read as e4m3).
+ *
+ * Request b's last q_len cached tokens are the current token and its q_len - 1
+ * drafts (appended this step). Query position j < q_len, the token at
+ * position L - q_len + j, attends to cached tokens 0 .. L - q_len + j only:
+ * for split c and query row (j, h),
+ *   o_part / lse_part as for pkv_decode_attn over the tokens
+ *   [c*S, min((c+1)*S, L - q_len + j + 1)), with o = 0 and lse = -inf where
+ *   that range is empty.
+ *   q:        bf16 [batch][q_len][num_q_heads][head_dim_k]
+ *   o_part:   float32 [batch][q_len * num_q_heads][max_splits][head_dim_v]
+ *   lse_part: float32 [batch][q_len * num_q_heads][max_splits]
+ * Every split c < ceil(L / S) of every query row is written, so pkv_combine
+ * with num_q_heads' = q_len * num_q_heads merges them into
+ * out bf16 [batch][q_len][num_q_heads][head_dim_v].
+ * Other arguments and errors as for pkv_decode_attn; also EINVAL for
+ * q_len outside [1, 64]. EUNSUPPORTED unless the cache is e4m3 with
+ * separate K and V pools and head_dim_k == head_dim_v == 128.
+ */
+int pkv_decode_attn_drafts(const pkv_cache* cache, const void* q, int32_t num_q_heads,
+                           int32_t q_len, const int32_t* block_table, const int32_t* seq_lens,
+                           int32_t batch, int32_t max_pages, int32_t max_seq_len,
+                           const uint8_t* abort_flags, float sm_scale, int32_t split_tokens,
+                           int32_t max_splits, float* o_part, float* lse_part,
+                           hipStream_t stream);
+
+/*
  * Prefill -> decode handoff of whole pages (section "Quantizing the KV
  * cache": decode holds the cache as e4m3 while prefill keeps BF16, so a
  * prefill's pages are re-encoded on their way into the decode pool; section
