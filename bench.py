@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--handoff", action="store_true",
                     help="also time pkv_requantize_pages: 8192 BF16 pages (Hkv 8, page 16, "
                          "head dim 128) re-encoded into an e4m3 pool")
+    ap.add_argument("--drafts", type=int, default=0, metavar="T",
+                    help="also time decode of a token and T-1 drafts per request on the same cache")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -225,6 +227,60 @@ def time_handoff(steps: int, n_pages: int = 8192):
             "kernel": "requant_kernel (bf16 pages -> e4m3, tags)"}
 
 
+def time_drafts(run, T: int, steps: int, warmup: int, read, dec_ms: float):
+    """pkv_decode_attn_drafts + pkv_combine over the Runner's resident cache:
+    each request verifies its last T tokens together (query j sees the
+    context up to L - T + j). The kernel reads the same cache bytes as a
+    one-token decode; flops grow with T (QK^T and PV for T x Hq rows)."""
+    import torch
+
+    pkv, w, s = run.pkv, run.w, run.step
+    g = torch.Generator(device="cuda").manual_seed(2029)
+    q = torch.randn((w.batch, T, w.num_q_heads, w.head_dim_k), generator=g, device="cuda")
+    q = q.to(torch.bfloat16)
+    L = s.max_seq_len
+    split = s.split_tokens
+    n_split = -(-L // split)
+    o_part = torch.empty((w.batch, T * w.num_q_heads, n_split, w.head_dim_v),
+                         dtype=torch.float32, device="cuda")
+    lse_part = torch.empty((w.batch, T * w.num_q_heads, n_split), dtype=torch.float32,
+                           device="cuda")
+    out = torch.empty((w.batch, T * w.num_q_heads, w.head_dim_v), dtype=torch.bfloat16,
+                      device="cuda")
+    lse = torch.empty((w.batch, T * w.num_q_heads), dtype=torch.float32, device="cuda")
+    abort = s.abort if s.verify else None
+
+    def one(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pkv.pkv_decode_attn_drafts(run.cache, q, run.bt, run.lens, L, abort, w.sm_scale, split,
+                                   o_part, lse_part)
+        if ev is not None:
+            ev[1].record()
+        pkv.pkv_combine(o_part, lse_part, run.lens, split, L, abort, out, lse)
+
+    for _ in range(warmup):
+        one()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        one(e)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    nbytes = kv_bytes(w, 1, read)
+    tokens = int(w.seq_lens[read].sum()) if read is not None else w.total_tokens
+    flop = 2 * T * w.num_q_heads * (w.head_dim_k + w.head_dim_v) * tokens
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"q_len": T, "decode_ms": round(ms, 5), "eager_ms_per_step": round((t1 - t0) * 1e3 / steps, 5),
+            "kv_gbs": round(gbs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+            "vs_q_len_single_token_decodes": round(T * dec_ms / ms, 3),
+            "kernel": "decode_drafts_kernel (e4m3, MFMA 32x32x16 bf16/f16)"}
+
+
 def cpu_baseline(w, budget_s: float = 12.0):
     """The oracle (quantise + tag check + attention) on a bounded sample of the
     same workload: whole requests in order, until the time budget is spent."""
@@ -329,6 +385,11 @@ def main():
                            "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                            "traffic": measured_traffic(w, split), "kernel": "pkv_decode_attn (e4m3)",
                            "avg_ms": round(dec_ms, 5)}
+    if args.drafts:
+        if w.latent or w.head_dim_k != 128 or w.head_dim_v != 128:
+            rec["drafts"] = {"error": "the drafts path takes head dim 128 without a latent cache"}
+        else:
+            rec["drafts"] = time_drafts(run, args.drafts, args.steps, args.warmup, read, dec_ms)
     del run
     torch.cuda.empty_cache()
     if not args.no_bf16:
