@@ -38,7 +38,6 @@ MFMA_BF16_PEAK = 2500.0  # TFLOP/s, dense
 # here and WRITE_SIZE in KiB. Entries stop matching once the kernel changes.
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 TRAFFIC_KIB = {
-    ("sweep_b64", 512, "decode_gqa_e4m3.hip", "5b60754af5d82337"): (1197882.8, 77717.3),
     ("mla_b64", 4096, "decode_mla.hip", "f3a58c5486d7f247"): (178394.0, 44200.1),
 }
 
@@ -72,7 +71,7 @@ def parse():
 def measured_traffic(w, split: int):
     """Scaled HBM bytes per decode launch, or None if no counters match."""
     import hashlib
-    src = "decode_mla.hip" if w.latent else "decode_gqa_e4m3.hip"
+    src = "decode_mla.hip" if w.latent else "decode_gqa_mfma.hip"
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "decode_attention_fp8_amd",
                         "csrc", src)
     with open(path, "rb") as f:

@@ -245,6 +245,8 @@ extern "C" int pkv_decode_attn(const pkv_cache* cache, const void* q, int32_t nu
   if (latent && mla_fast_path_supported(dk, dv, cache->num_kv_heads, num_q_heads,
                                         cache->page_size, split_tokens))
     return launch_decode_mla(p, e4m3, static_cast<int>(n_split_blocks), batch, stream);
+  if (e4m3 && gqa_mfma_path_supported(dk, dv, G, latent, split_tokens, cache->page_size))
+    return launch_decode_gqa_mfma(p, static_cast<int>(n_split_blocks), batch, stream);
   if (e4m3 && gqa_e4m3_path_supported(dk, dv, G, latent, split_tokens, cache->page_size))
     return launch_decode_gqa_e4m3(p, static_cast<int>(n_split_blocks), batch, stream);
   if (gqa_fast_path_supported(dk, dv, G, latent, split_tokens, cache->page_size))

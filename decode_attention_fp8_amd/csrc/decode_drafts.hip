@@ -37,17 +37,10 @@
 // numerators stay at most 2^kTau, inside f16 range.
 #include "common.h"
 #include "decode_params.h"
+#include "mfma_tile.h"
 #include "unit_order.h"
 
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef float floatx16_t __attribute__((ext_vector_type(16)));
-typedef int v2i_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 15.0f;      // f16 numerators stay at most 2^kTau
@@ -58,39 +51,6 @@ constexpr int kHalf = kTile * kD;            // K (or V) bytes of a tile
 constexpr int kTileBytes = 2 * kHalf;        // K then V: 8 KB
 constexpr int kSlots = 2;
 constexpr int kMaxUnitPages = 64;
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
-}
-
-__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const uint8_t* base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds), "v"(voff), "s"(base)
-               : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
-  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
-  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
-  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-__device__ __forceinline__ f16x8_t fp8x8_to_f16(uint32_t w0, uint32_t w1) {
-  const f16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
-  const f16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
-  const f16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
-  const f16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
-  return f16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
 
 // Tile layouts: K chunk c of token row t at c ^ ((t >> 1) & 7) (the 32 rows
 // a K read touches at one chunk land on distinct bank groups); V chunk c of

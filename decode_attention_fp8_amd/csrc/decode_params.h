@@ -35,6 +35,13 @@ bool gqa_e4m3_path_supported(int dk, int dv, int group, bool latent, int split_t
 int launch_decode_gqa_e4m3(const DecodeParams& p, int n_split_blocks, int batch,
                            hipStream_t stream);
 
+// grouped-query kernel on MFMA for an e4m3 cache, head dim 128, up to 16
+// query heads per kv head
+bool gqa_mfma_path_supported(int dk, int dv, int group, bool latent, int split_tokens,
+                             int page_size);
+int launch_decode_gqa_mfma(const DecodeParams& p, int n_split_blocks, int batch,
+                           hipStream_t stream);
+
 // several query positions per request (a token and its drafts), e4m3, head dim 128
 bool drafts_path_supported(int dk, int dv, bool latent, bool e4m3);
 int launch_decode_drafts(const DecodeParams& p, int n_split_blocks, int batch, int row_groups,
