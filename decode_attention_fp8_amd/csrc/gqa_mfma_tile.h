@@ -1,0 +1,258 @@
+// One 32-token tile of grouped-query decode on MFMA 16x16x32 (internal),
+// shared by the dispatched and the persistent e4m3 kernels.
+//
+// "Smaller, faster, safer: running Kimi and GLM at scale" (Cloudflare blog),
+// section "Quantizing the KV cache": K and V are held as e4m3 and the
+// attention kernel converts codes as it reads them.
+//
+// The G <= 16 query heads of a kv head share every cached K and V row, so
+// for 32 cached tokens QK^T is a [32 x 128] x [128 x G] product and PV a
+// [G x 32] x [32 x 128] one. Both run on MFMA 16x16x32 with fp32
+// accumulation, the G heads padded to 16 rows: QK^T in bf16 (the query is
+// bf16; K codes convert exactly), PV in f16 (V codes convert exactly;
+// numerators rounded to f16). The VALU keeps only the exact converts and the
+// softmax.
+//
+// A tile's K and V bytes (4 KB each, two 16-token groups of each) sit in an
+// 8 KB LDS slot, written by direct-to-LDS loads.
+//
+// MFMA 16x16x32 operand layouts (lane l, c = l % 16, q = l / 16):
+//   A: row c, k 8q .. 8q+7;  B: column c, k 8q .. 8q+7;
+//   D element i: row 4q + i, column c.
+// QK^T runs transposed, S^T = K Q^T (M = 16 tokens, N = 16 heads), with the
+// contraction order permuted so that a lane's K operand is one 32-byte run
+// of its token row: in k-step s, slot 8q + j is dim 32q + 8s + j. A lane then
+// holds head c's scores for tokens 4q .. 4q+3 of each 16-token half of the
+// tile, which is already the A operand of O += P V (M = heads, 32 tokens of
+// contraction; slot 8q + e is token 4q + e of the first half for e < 4 and
+// token 4q + e - 4 of the second half otherwise) once V is read in that
+// token order with ds_read_tr8_b64: lane i of a 16-lane group gets byte i of
+// the 8 rows the group's lane pairs address.
+//
+// Softmax: log2 domain, per head a reference max set by the first tile with
+// a valid token; a later score more than kTau above it raises it and
+// rescales the head's accumulators (a uniform branch real scores almost
+// never take), so the f16 numerators stay at most 2^kTau.
+#pragma once
+
+#include "decode_params.h"
+#include "mfma_tile.h"
+
+namespace gqa_mfma {
+
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kTau = 15.0f;      // f16 numerators stay at most 2^kTau
+constexpr float kMUnset = -1e30f;  // reference max before the first valid score
+constexpr int kD = 128;
+constexpr int kRows = 16;              // query heads per MFMA tile (G padded)
+constexpr int kTile = 32;              // tokens per tile
+constexpr int kHalf = kTile * kD;      // K (or V) bytes of a tile
+constexpr int kTileBytes = 2 * kHalf;  // K then V: 8 KB
+
+// LDS layouts, 64 banks of 4 bytes (bank = 32 (row & 1) + 4 chunk position
+// for 128-byte rows). K chunk c of tile row t sits at c ^ kswz(t): the 16
+// rows one 16-lane phase of a K read touches at one chunk fall on distinct
+// banks. V chunk c of row t sits at c ^ vswz(t), vswz(t) = bits 1, 2 and 4
+// of t: the 16 rows of a half-wave's transposing read at one chunk, likewise.
+__device__ __forceinline__ uint32_t kswz(uint32_t t) { return (t >> 1) & 7u; }
+__device__ __forceinline__ uint32_t vswz(uint32_t t) {
+  return ((t >> 1) & 3u) | (((t >> 4) & 1u) << 2);
+}
+
+// Per-lane byte offsets, fixed for the whole kernel.
+struct LaneOffsets {
+  // DMA sources inside a 16-token group block: lane L fills LDS chunk
+  // position L & 7 of group row L >> 3 (first 1 KB) and of row 8 + (L >> 3)
+  // (second 1 KB); position pos of tile row t holds chunk pos ^ swz(t)
+  uint32_t kdma0, kdma1;
+  uint32_t vdma[2][2];  // [half of the tile][first / second 1 KB]
+  // LDS reads: K operand of half x, read r = chunk 2 qg + r (dims
+  // 32 qg + 16 r ..) of tile row 16 x + col; V operand of dim block nb =
+  // halves of chunk nb of row tv(e) for lane pair 2e, 2e+1 of a group
+  uint32_t kread[2][2];
+  uint32_t vread[8];
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
+  LaneOffsets o;
+  const int col = lane & 15, qg = lane >> 4;
+  const uint32_t dr0 = lane >> 3, dr1 = 8 + (lane >> 3), dpos = lane & 7;
+  o.kdma0 = dr0 * kD + ((dpos ^ kswz(dr0)) << 4);
+  o.kdma1 = dr1 * kD + ((dpos ^ kswz(dr1)) << 4);
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    o.vdma[x][0] = dr0 * kD + ((dpos ^ vswz(16 * x + dr0)) << 4);
+    o.vdma[x][1] = dr1 * kD + ((dpos ^ vswz(16 * x + dr1)) << 4);
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const uint32_t row = 16 * x + col;
+      o.kread[x][r] = row * kD + ((static_cast<uint32_t>(2 * qg + r) ^ kswz(row)) << 4);
+    }
+  const int e_row = (lane & 15) >> 1;
+  const uint32_t tv = e_row < 4 ? 4 * qg + e_row : 16 + 4 * qg + (e_row - 4);
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+    o.vread[nb] =
+        kHalf + tv * kD + ((static_cast<uint32_t>(nb) ^ vswz(tv)) << 4) + 8 * (lane & 1);
+  return o;
+}
+
+// DMA of one 16-token group (K and V, 2 KB each) into half x of a slot.
+__device__ __forceinline__ void dma_group(uint32_t slot, int x, const LaneOffsets& o,
+                                          const uint8_t* kgroup, const uint8_t* vgroup) {
+  dma16(slot + 2048 * x, o.kdma0, kgroup);
+  dma16(slot + 2048 * x + 1024, o.kdma1, kgroup);
+  dma16(slot + kHalf + 2048 * x, o.vdma[x][0], vgroup);
+  dma16(slot + kHalf + 2048 * x + 1024, o.vdma[x][1], vgroup);
+}
+
+struct Acc {
+  floatx4_t O[8];  // head 4 qg + i, dim 16 nb + col
+  float m;         // reference max of head col (its four lanes agree)
+  float l;         // this lane's part of head col's denominator
+};
+
+__device__ __forceinline__ void acc_init(Acc& a) {
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a.O[nb][i] = 0.0f;
+  a.m = kMUnset;
+  a.l = 0.0f;
+}
+
+// QK^T, softmax and PV of the tile in buf. Group x of the tile holds valid
+// rows only if gx_ok (its page is in the pool); of the tile's 32 rows the
+// first nv are in the unit. rowbuf: 16 floats of LDS.
+__device__ __forceinline__ void tile_math(uint8_t* buf, const LaneOffsets& o,
+                                          const bf16x8_t (&qf)[4], float qk_scale, bool g0_ok,
+                                          bool g1_ok, int nv, float* rowbuf, Acc& a) {
+  const int lane = threadIdx.x;
+  const int col = lane & 15, qg = lane >> 4;
+  const bool full = g0_ok && g1_ok && nv == kTile;
+  if (!full) {
+    // rows past the unit or of a page outside the pool: V to zero (their
+    // scores are masked, and 0 * NaN must not reach the accumulators)
+    for (int q = lane; q < kTile * (kD / 16); q += 64) {
+      const int row = q >> 3;
+      const bool keep = row < nv && (row < 16 ? g0_ok : g1_ok);
+      if (!keep) *reinterpret_cast<uint4*>(buf + kHalf + 16 * q) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- S^T = K Q^T, one 16-token half at a time
+  floatx4_t s[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[x][i] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const uint4 kq = *reinterpret_cast<const uint4*>(buf + o.kread[x][r]);
+      s[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(kq.x, kq.y), qf[2 * r], s[x],
+                                                     0, 0, 0);
+      s[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(kq.z, kq.w), qf[2 * r + 1],
+                                                     s[x], 0, 0, 0);
+    }
+  }
+  // s[x][i]: head col, tile row 16 x + 4 qg + i
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = s[x][i] * qk_scale;
+      if (!full) {
+        const int tt = 16 * x + 4 * qg + i;
+        v = (tt < nv && (x == 0 ? g0_ok : g1_ok)) ? v : -INFINITY;
+      }
+      s[x][i] = v;
+      tmax = fmaxf(tmax, v);
+    }
+  // every head has its first valid score in the same tile, so m is unset
+  // in all lanes or in none
+  if (a.m == kMUnset) {
+    float hm = fmaxf(tmax, __shfl_xor(tmax, 16));
+    hm = fmaxf(hm, __shfl_xor(hm, 32));
+    if (hm > -INFINITY) a.m = hm;
+  }
+  if (__any(tmax > a.m + kTau)) {
+    // rare: raise the reference max of the heads that need it, rescale
+    float hm = fmaxf(tmax, __shfl_xor(tmax, 16));
+    hm = fmaxf(hm, __shfl_xor(hm, 32));
+    const float mn = hm > a.m + kTau ? hm : a.m;
+    const float al = __builtin_amdgcn_exp2f(a.m - mn);
+    a.m = mn;
+    a.l *= al;
+    if (qg == 0) rowbuf[col] = al;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float f = rowbuf[4 * qg + i];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) a.O[nb][i] *= f;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- O += P V over the 32 tokens, 8 blocks of 16 dims
+  f16x8_t pf;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pr = __builtin_amdgcn_exp2f(s[x][i] - a.m);
+      a.l += pr;
+      pf[4 * x + i] = static_cast<_Float16>(pr);
+    }
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const v2i_t r8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(buf + o.vread[nb]));
+    a.O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        pf, fp8x8_to_f16(static_cast<uint32_t>(r8[0]), static_cast<uint32_t>(r8[1])), a.O[nb], 0,
+        0, 0);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// The unit's partials: per query head g G + h (h < G) of request b, split c,
+// o = v_scale O / l and lse = (m + log2 l) ln 2 (o = 0, lse = -inf where no
+// token was valid).
+__device__ __forceinline__ void finish(const DecodeParams& p, int b, int g, int c, int G,
+                                       float o_scale, float* rowbuf, Acc& a) {
+  const int lane = threadIdx.x;
+  const int col = lane & 15, qg = lane >> 4;
+  float l = a.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (qg == 0) rowbuf[col] = l;
+  __builtin_amdgcn_wave_barrier();
+  const int64_t head0 = static_cast<int64_t>(b) * p.num_q_heads + g * G;
+  if (qg == 0 && col < G)
+    p.lse_part[(head0 + col) * p.max_splits + c] =
+        l > 0.0f ? (a.m + __log2f(l)) * kLn2 : -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * qg + i;
+    if (h >= G) continue;
+    const float lr = rowbuf[h];
+    const float f = lr > 0.0f ? o_scale / lr : 0.0f;
+    float* dst = p.o_part + ((head0 + h) * p.max_splits + c) * kD + col;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) dst[16 * nb] = a.O[nb][i] * f;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// one of four values by a wave-uniform index (values, not addresses, so the
+// four stay in registers)
+template <typename T>
+__device__ __forceinline__ T pick4(int h, T a, T b, T c, T d) {
+  return h == 0 ? a : h == 1 ? b : h == 2 ? c : d;
+}
+
+}  // namespace gqa_mfma
