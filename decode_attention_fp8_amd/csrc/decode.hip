@@ -247,8 +247,6 @@ extern "C" int pkv_decode_attn(const pkv_cache* cache, const void* q, int32_t nu
     return launch_decode_mla(p, e4m3, static_cast<int>(n_split_blocks), batch, stream);
   if (e4m3 && gqa_mfma_path_supported(dk, dv, G, latent, split_tokens, cache->page_size))
     return launch_decode_gqa_mfma(p, static_cast<int>(n_split_blocks), batch, stream);
-  if (e4m3 && gqa_e4m3_path_supported(dk, dv, G, latent, split_tokens, cache->page_size))
-    return launch_decode_gqa_e4m3(p, static_cast<int>(n_split_blocks), batch, stream);
   if (gqa_fast_path_supported(dk, dv, G, latent, split_tokens, cache->page_size))
     return launch_decode_gqa(p, e4m3, static_cast<int>(n_split_blocks), batch, stream);
   return e4m3 ? dispatch<true>(p, latent, dk, G, static_cast<int>(n_split_blocks), batch, stream)

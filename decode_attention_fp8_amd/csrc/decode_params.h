@@ -29,12 +29,6 @@ bool gqa_fast_path_supported(int dk, int dv, int group, bool latent, int split_t
 int launch_decode_gqa(const DecodeParams& p, bool e4m3, int n_split_blocks, int batch,
                       hipStream_t stream);
 
-// grouped-query kernel for an e4m3 cache, head dim 128, 8 query heads per kv head
-bool gqa_e4m3_path_supported(int dk, int dv, int group, bool latent, int split_tokens,
-                             int page_size);
-int launch_decode_gqa_e4m3(const DecodeParams& p, int n_split_blocks, int batch,
-                           hipStream_t stream);
-
 // grouped-query kernel on MFMA for an e4m3 cache, head dim 128, up to 16
 // query heads per kv head
 bool gqa_mfma_path_supported(int dk, int dv, int group, bool latent, int split_tokens,
