@@ -22,10 +22,11 @@ Modules:
   combine  split partials and their log-sum-exp merge
   step     one decode step of a workload, request by request
   handoff  prefill -> decode page handoff: BF16 pages re-encoded, tags set
+  int4     INT4 weight-only linear layer of the decode phase
 
 Parity status: every function is pinned by tests/test_oracle_*.py; the only
 unpinned quantity is the accuracy of FP8 against BF16 attention (the pages'
 evidence for it is model-level benchmark scores), which is reported, never
 asserted.
 """
-from . import attention, combine, e4m3, handoff, quant, step, verify  # noqa: F401
+from . import attention, combine, e4m3, handoff, int4, quant, step, verify  # noqa: F401

@@ -162,6 +162,23 @@ def bf16_block(keys, n: int, device="cpu", outliers: bool = False,
     return out
 
 
+def u8_from_index(keys, idx: torch.Tensor) -> torch.Tensor:
+    """Uniform bytes for int64 element indices ``idx``: the top 8 bits of
+    mix32(mix32(idx ^ k0) ^ k1)."""
+    k0, k1 = keys[0], keys[1]
+    return (mix32_t(mix32_t(idx ^ k0) ^ k1) >> 24).to(torch.uint8)
+
+
+def u8_block(keys, n: int, device="cpu", chunk: int = 1 << 26) -> torch.Tensor:
+    """The first ``n`` bytes of a stream, as a flat uint8 tensor."""
+    out = torch.empty(n, dtype=torch.uint8, device=device)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        idx = torch.arange(s, e, dtype=torch.int64, device=device)
+        out[s:e] = u8_from_index(keys, idx)
+    return out
+
+
 # ----------------------------------------------------------------------------
 # exact max |value| of a stream prefix, by inverting the hash
 # ----------------------------------------------------------------------------
