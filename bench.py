@@ -63,6 +63,8 @@ def parse():
                          "head dim 128) re-encoded into an e4m3 pool")
     ap.add_argument("--drafts", type=int, default=0, metavar="T",
                     help="also time decode of a token and T-1 drafts per request on the same cache")
+    ap.add_argument("--int4", action="store_true",
+                    help="also time the INT4 weight-only linear layer at batch 1..64")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -281,6 +283,72 @@ def time_drafts(run, T: int, steps: int, warmup: int, read, dec_ms: float):
             "kernel": "decode_drafts_kernel (e4m3, MFMA 32x32x16 bf16/f16)"}
 
 
+def time_int4(steps: int, warmup: int, layers: int = 16, n: int = 8192, k: int = 8192):
+    """pkv_int4_linear over a stack of `layers` distinct n x k INT4 layers
+    (codes + group scales: layers * (n*k/2 + n*k/64) bytes, above the MALL),
+    one launch per layer, at batch 1 .. 64; beside it the same shapes as
+    bf16 weights through torch's library GEMM. Each step is a captured HIP
+    graph, replayed."""
+    import torch
+
+    import decode_attention_fp8_amd as pkv
+    import workloads as W
+    rows = []
+    lays = [W.Int4Layer(f"int4_stack_{i}", 2000 + i, n, k, 64) for i in range(layers)]
+    codes = [l.codes("cuda") for l in lays]
+    scales = [l.scales("cuda") for l in lays]
+    g = torch.Generator(device="cuda").manual_seed(2031)
+    wbf = [torch.randn((n, k), generator=g, device="cuda").to(torch.bfloat16) for _ in range(layers)]
+    w_bytes = layers * (n * k // 2 + (k // 128) * n * 2)
+    for B in (1, 8, 16, 32, 64):
+        x = lays[0].x("cuda")[:B].contiguous()
+        y = torch.empty((B, n), dtype=torch.bfloat16, device="cuda")
+
+        def step_int4():
+            for i in range(layers):
+                pkv.pkv_int4_linear(x, codes[i], scales[i], y)
+
+        def step_bf16():
+            for i in range(layers):
+                torch.matmul(x, wbf[i].t(), out=y)
+
+        res = {"batch": B}
+        for name, fn in (("int4", step_int4), ("bf16", step_bf16)):
+            # the step (one launch per layer) captured once and replayed, so
+            # host launch costs do not enter the layer time
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for _ in range(warmup):
+                    fn()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                fn()
+            for _ in range(warmup):
+                graph.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / (steps * layers)
+            del graph
+            res[name] = {"ms_per_layer": round(ms, 5)}
+        nb = w_bytes / layers + B * k * 2 + B * n * 2
+        gbs = nb / (res["int4"]["ms_per_layer"] * 1e-3) / 1e9
+        res["int4"].update({"gbs": round(gbs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+        res["int4_speedup_over_bf16"] = round(res["bf16"]["ms_per_layer"] / res["int4"]["ms_per_layer"], 3)
+        rows.append(res)
+    del codes, scales, wbf
+    torch.cuda.empty_cache()
+    return {"layer": f"{n}x{k} INT4 (group 128, bf16 scales), {layers} distinct layers per step",
+            "bytes_per_layer": w_bytes // layers, "kernel": "int4_linear_kernel", "rows": rows}
+
+
 def cpu_baseline(w, budget_s: float = 12.0):
     """The oracle (quantise + tag check + attention) on a bounded sample of the
     same workload: whole requests in order, until the time budget is spent."""
@@ -435,6 +503,8 @@ def main():
         rec["integrity_cost"] = rows
     if args.handoff:
         rec["handoff"] = time_handoff(args.steps)
+    if args.int4:
+        rec["int4_linear"] = time_int4(max(10, args.steps // 2), 3)
     if not args.no_cpu_baseline and not w.latent:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

@@ -20,8 +20,8 @@ PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP = 0, -1, -2, -3
 PKV_KV_E4M3, PKV_KV_BF16 = 1, 2
 
 EXPORTS = ("pkv_scales_from_amax", "pkv_append", "pkv_verify", "pkv_decode_attn",
-           "pkv_combine", "pkv_decode_attn_drafts", "pkv_requantize_pages", "pkv_suggest_split", "pkv_strerror",
-           "pkv_version")
+           "pkv_combine", "pkv_decode_attn_drafts", "pkv_requantize_pages", "pkv_int4_linear",
+           "pkv_suggest_split", "pkv_strerror", "pkv_version")
 
 
 class PkvError(RuntimeError):
@@ -55,6 +55,7 @@ def _load() -> ctypes.CDLL:
         "pkv_decode_attn_drafts": (I32, [CP, P, I32, I32, P, P, I32, I32, I32, P, F, I32, I32, P,
                                          P, P]),
         "pkv_requantize_pages": (I32, [CP, CP, P, P, P, P, I32, P]),
+        "pkv_int4_linear": (I32, [P, P, P, I32, I32, I32, P, P]),
         "pkv_suggest_split": (I32, [CP, I32, I32, I64, I32]),
         "pkv_strerror": (ctypes.c_char_p, [I32]),
         "pkv_version": (I32, []),
@@ -216,6 +217,23 @@ def pkv_decode_attn_drafts(cache: Cache, q: torch.Tensor, block_table: torch.Ten
         ctypes.byref(cs), _ptr(q), Hq, T, _ptr(block_table), _ptr(seq_lens), B,
         int(block_table.shape[1]), int(max_seq_len), _ptr(abort_flags), float(sm_scale),
         int(split_tokens), int(o_part.shape[2]), _ptr(o_part), _ptr(lse_part), _stream(stream)))
+
+
+def pkv_int4_linear(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor, y: torch.Tensor,
+                    stream=None) -> None:
+    """y bf16 [B, n] = x bf16 [B, k] times the INT4 weights w uint8 [n, k/2]
+    with bf16 group scales [k/128, n]."""
+    _need(x, torch.bfloat16, "x")
+    _need(scales, torch.bfloat16, "scales")
+    _need(y, torch.bfloat16, "y")
+    if w.dtype != torch.uint8 or not w.is_contiguous():
+        raise ValueError("w: contiguous uint8 [n, k/2]")
+    B, k = x.shape
+    n = w.shape[0]
+    if w.shape[1] * 2 != k or tuple(scales.shape) != (k // 128, n) or tuple(y.shape) != (B, n):
+        raise ValueError("pkv_int4_linear: shapes x [B, k], w [n, k/2], scales [k/128, n], y [B, n]")
+    _check("pkv_int4_linear", _lib.pkv_int4_linear(_ptr(x), _ptr(w), _ptr(scales), B, n, k,
+                                                   _ptr(y), _stream(stream)))
 
 
 def pkv_requantize_pages(src: Cache, dst: Cache, src_pages: torch.Tensor, dst_pages: torch.Tensor,

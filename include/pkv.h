@@ -283,6 +283,27 @@ int pkv_requantize_pages(const pkv_cache* src, const pkv_cache* dst,
                          hipStream_t stream);
 
 /*
+ * INT4 weight-only linear layer of the decode phase ("Smaller, faster,
+ * safer", section on model weights: GLM's weights held as 4-bit integers for
+ * decode, where each token streams them out of GPU memory).
+ *
+ *   y[b][r] = bf16_RNE( sum_k x[b][k] * q[r][k] * scales[k / 128][r] )
+ * for b < batch, r < n, with q[r][k] the 4-bit two's-complement code of
+ * input k of row r (-8 .. 7).
+ *   x:      bf16 [batch][k]
+ *   w:      uint8 [n][k / 2]; input k of row r in byte k / 2 of the row,
+ *           even k in the low nibble (bits 0..3), odd k in the high nibble
+ *   scales: bf16 [k / 128][n] (group-major: one group's scales of
+ *           consecutive rows are contiguous)
+ *   y:      bf16 [batch][n], fully written
+ * Accumulation is fp32. Device pointers, caller-owned; x, w and scales
+ * 16-byte aligned. EINVAL: NULL pointers, batch outside [1, 64], n not a
+ * multiple of 32, k not a multiple of 1024, misaligned pointers.
+ */
+int pkv_int4_linear(const void* x, const uint8_t* w, const void* scales, int32_t batch,
+                    int32_t n, int32_t k, void* y, hipStream_t stream);
+
+/*
  * Host helper: a split size for pkv_decode_attn on this cache and batch.
  *   num_q_heads   query heads of the batch (as passed to pkv_decode_attn)
  *   batch         requests in the batch

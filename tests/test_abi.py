@@ -109,6 +109,14 @@ def test_invalid_arguments_rejected_on_host():
     assert lib.pkv_combine(None, P, P, 1, 1, 64, 16, 4, 64, None, P, None, None) == E
     assert lib.pkv_combine(P, P, P, 1, 1, 64, 16, 3, 64, None, P, None, None) == E
     assert lib.pkv_combine(P, P, P, 1, 1, 60, 16, 4, 64, None, P, None, None) == E
+    # INT4 linear: NULL, batch outside [1, 64], n not a multiple of 32, k not a
+    # multiple of 1024, misaligned pointers
+    assert lib.pkv_int4_linear(None, P, P, 1, 32, 1024, P, None) == E
+    assert lib.pkv_int4_linear(P, P, P, 0, 32, 1024, P, None) == E
+    assert lib.pkv_int4_linear(P, P, P, 65, 32, 1024, P, None) == E
+    assert lib.pkv_int4_linear(P, P, P, 1, 48, 1024, P, None) == E
+    assert lib.pkv_int4_linear(P, P, P, 1, 32, 1536, P, None) == E
+    assert lib.pkv_int4_linear(P + 8, P, P, 1, 32, 1024, P, None) == E
 
 
 def test_binding_refuses_host_tensors():

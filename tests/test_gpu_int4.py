@@ -1,0 +1,75 @@
+"""GPU parity of the INT4 weight-only linear layer (pkv_int4_linear) against
+the float64 oracle (oracle.int4.linear) on the counter-based inputs,
+element by element within |gpu - ref| <= 2e-3 + 1e-2 |ref| (the output is
+bf16; accumulation fp32)."""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_fp8_amd as pkv
+import workloads as W
+from oracle import int4
+from tests.gpu_state import assert_close
+
+pytestmark = pytest.mark.gpu
+dev = "cuda"
+
+
+def _gpu(lay, codes=None, scales=None):
+    x = lay.x(dev)
+    w = lay.codes(dev) if codes is None else codes.to(dev)
+    s = lay.scales(dev) if scales is None else scales.to(dev)
+    y = torch.full((lay.batch, lay.n), float("nan"), dtype=torch.bfloat16, device=dev)
+    pkv.pkv_int4_linear(x, w, s, y)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy()
+
+
+def _ref(lay, rows, codes=None, scales=None):
+    x = lay.x().float().numpy().astype(np.float64)
+    packed = (lay.codes(rows=rows) if codes is None else codes[rows]).numpy()
+    s = (lay.scales() if scales is None else scales).float().numpy().astype(np.float64)
+    return int4.linear(x, packed, s[:, rows])
+
+
+@pytest.mark.parametrize("batch", [1, 5, 16, 17, 33, 64])
+@pytest.mark.parametrize("n,k", [(64, 1024), (96, 2048), (32, 4096)])
+def test_small_layers_every_output(batch, n, k):
+    """One to eight groups per wave, one to four token tiles, ragged batches."""
+    lay = W.int4_custom(f"i4_{n}_{k}_{batch}", 40 + batch, n, k, batch)
+    y = _gpu(lay)
+    assert_close(y, _ref(lay, np.arange(n)), f"{lay.name}")
+
+
+@pytest.mark.parametrize("batch", [1, 64])
+def test_full_size_sampled_rows(batch):
+    """The benchmark's 8192 x 8192 layer: every token of 48 sampled rows
+    (first and last rows of workgroups, random others)."""
+    lay = W.int4_layer(batch)
+    y = _gpu(lay)
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([[0, 31, 32, 8191], rng.integers(0, lay.n, 44)]))
+    assert_close(y[:, rows], _ref(lay, rows), f"{lay.name} sampled rows")
+
+
+@pytest.mark.parametrize("byte", [0x88, 0x77, 0x0F, 0xF0])
+def test_extreme_and_mixed_sign_codes(byte):
+    """All codes -8, all 7, and alternating 0 / -1 patterns."""
+    lay = W.int4_custom("i4x", 50, 64, 1024, 16)
+    codes = torch.full((64, 512), byte, dtype=torch.uint8)
+    y = _gpu(lay, codes=codes)
+    assert_close(y, _ref(lay, np.arange(64), codes=codes), f"codes 0x{byte:02x}")
+
+
+def test_bad_arguments_raise():
+    lay = W.int4_custom("i4b", 51, 32, 1024, 2)
+    x, w, s = lay.x(dev), lay.codes(dev), lay.scales(dev)
+    y = torch.empty((2, 32), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        pkv.pkv_int4_linear(x, w[:, :256], s, y)
+    with pytest.raises(ValueError):
+        pkv.pkv_int4_linear(x.float(), w, s, y)
+    big = W.int4_custom("i4c", 52, 32, 1024, 65)
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_int4_linear(big.x(dev), w, s, torch.empty((65, 32), dtype=torch.bfloat16,
+                                                          device=dev))
