@@ -39,3 +39,31 @@ def quantize(x, s) -> np.ndarray:
 def dequantize(codes, s) -> np.ndarray:
     """float64 value each code stands for: decode(code) * s."""
     return e4m3.decode(codes) * np.float64(np.float32(s))
+
+
+# ----------------------------------------------------------------------------
+# Scales set at append, one per cached row
+# ----------------------------------------------------------------------------
+# The pages give no scale granularity. The finer reading taken here: every
+# appended row (one token of one kv head, K and V separately) gets its own
+# scale from its own largest magnitude, by the same rule as the static
+# scales, and is encoded under it.
+
+
+def quantize_rows(x):
+    """x: float [..., D] rows of bf16 values -> (uint8 codes [..., D],
+    float32 scales [...]): scale_from_amax of each row, then quantize."""
+    a = np.asarray(x, dtype=np.float64)
+    flat = a.reshape(-1, a.shape[-1])
+    codes = np.empty(flat.shape, dtype=np.uint8)
+    scales = np.empty(flat.shape[0], dtype=np.float32)
+    for i, row in enumerate(flat):
+        s = scale_from_amax(np.abs(row).max() if row.size else 0.0)
+        scales[i] = s
+        codes[i] = quantize(row, s)
+    return codes.reshape(a.shape), scales.reshape(a.shape[:-1])
+
+
+def dequantize_rows(codes, scales) -> np.ndarray:
+    """float64 [..., D]: decode(code) times its row's scale."""
+    return e4m3.decode(codes) * np.asarray(scales, dtype=np.float64)[..., None]

@@ -79,3 +79,44 @@ def test_fp8_pool_is_half_the_bf16_pool():
     # the pages' own rounded figures agree with an exact doubling to 0.2%
     r = g["tokens_held"]["fp8_e4m3"] / g["tokens_held"]["bf16"]
     assert abs(r - g["stated_ratio"]) < 0.005
+
+
+# ---- scales set at append, one per row
+
+
+def test_row_scale_puts_each_rows_largest_value_at_448():
+    """The largest magnitude of every row encodes to +-448 (code 0x7E / 0xFE),
+    whatever the row's range: the per-row rule always uses the full code range."""
+    rng = np.random.default_rng(3)
+    rows = rng.standard_normal((50, 128)) * np.logspace(-6, 4, 50)[:, None]
+    rows = rows.astype(np.float32).astype(np.float64)
+    codes, scales = quant.quantize_rows(rows)
+    for r in range(50):
+        j = int(np.argmax(np.abs(rows[r])))
+        assert codes[r, j] in (0x7E, 0xFE)
+        assert scales[r] == quant.scale_from_amax(np.abs(rows[r]).max())
+
+
+def test_row_scale_error_within_half_a_step():
+    """Each value is off by at most half the e4m3 step at its magnitude, in
+    units of its own row's scale (the RNE bound), never saturating."""
+    rng = np.random.default_rng(4)
+    rows = (rng.standard_normal((40, 64)) * rng.uniform(1e-3, 1e3, (40, 1))).astype(np.float32)
+    codes, scales = quant.quantize_rows(rows)
+    back = quant.dequantize_rows(codes, scales)
+    y = np.abs(rows.astype(np.float64) / scales.astype(np.float64)[:, None])
+    # e4m3 step at |y|: 2^(floor(log2 y) - 3) for normals, 2^-9 below 2^-6
+    e = np.floor(np.log2(np.maximum(y, 2.0 ** -6)))
+    step = 2.0 ** (e - 3)
+    err = np.abs(back - rows) / scales.astype(np.float64)[:, None]
+    assert np.all(err <= step / 2 + 1e-12)
+
+
+def test_row_scale_zero_row_and_exact_grid_rows():
+    codes, scales = quant.quantize_rows(np.zeros((2, 16)))
+    assert np.all(codes == 0) and np.all(scales == 1.0)
+    # a row whose values are table values times a power of two round-trips
+    vals = e4m3.decode(np.array([0x7E, 0x01, 0x38, 0xC0, 0x00, 0x22], dtype=np.uint8))
+    row = vals * 2.0 ** -7
+    c, s = quant.quantize_rows(row[None, :])
+    assert np.array_equal(quant.dequantize_rows(c, s)[0], row)
