@@ -63,6 +63,8 @@ def parse():
                          "head dim 128) re-encoded into an e4m3 pool")
     ap.add_argument("--drafts", type=int, default=0, metavar="T",
                     help="also time decode of a token and T-1 drafts per request on the same cache")
+    ap.add_argument("--row-scales", action="store_true",
+                    help="also time the workload with scales set at append, one per cached row")
     ap.add_argument("--int4", action="store_true",
                     help="also time the INT4 weight-only linear layer at batch 1..64")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -98,7 +100,8 @@ def kv_bytes(w, elem_bytes: int, read=None) -> int:
 class Runner:
     """Device state of one workload and its timed step."""
 
-    def __init__(self, w, kv_dtype: str, split: int | None, verify: bool = True):
+    def __init__(self, w, kv_dtype: str, split: int | None, verify: bool = True,
+                 row_scales: bool = False):
         import numpy as np
         import torch
 
@@ -106,10 +109,10 @@ class Runner:
         self.torch, self.pkv, self.w = torch, pkv, w
         dev = "cuda"
         c = pkv.allocate_cache(w.num_pages, w.num_kv_heads, w.page_size, w.head_dim_k,
-                               w.head_dim_v, kv_dtype, w.latent, dev)
+                               w.head_dim_v, kv_dtype, w.latent, dev, row_scales=row_scales)
         k = w.k_all(dev)
         v = None if w.latent else w.v_all(dev)
-        if kv_dtype == "fp8":
+        if kv_dtype == "fp8" and not row_scales:
             pkv.pkv_scales_from_amax(k, w.per_head_scales, c.k_scale)
             if w.latent:
                 c.v_scale = c.k_scale
@@ -503,6 +506,19 @@ def main():
         rec["integrity_cost"] = rows
     if args.handoff:
         rec["handoff"] = time_handoff(args.steps)
+    if args.row_scales and not w.latent:
+        rr = Runner(w, "fp8", args.split or None, row_scales=True)
+        ms_r, dec_r = rr.time(args.steps, args.warmup)
+        del rr
+        torch.cuda.empty_cache()
+        scale_bytes = int(w.seq_lens[read].sum() if read is not None else w.total_tokens) * \
+            w.num_kv_heads * 2 * 4
+        rec["row_scales"] = {
+            "ms_per_step": round(ms_r, 5), "decode_ms": round(dec_r, 5),
+            "kv_gbs": round(fp8_bytes / (ms_r * 1e-3) / 1e9, 2),
+            "decode_gbs_codes_and_scales": round((fp8_bytes + scale_bytes) / (dec_r * 1e-3) / 1e9, 2),
+            "step_vs_static_scales": round(ms_r / ms, 4),
+            "kernel": "decode_gqa_mfma_kernel<2, true>"}
     if args.int4:
         rec["int4_linear"] = time_int4(max(10, args.steps // 2), 3)
     if not args.no_cpu_baseline and not w.latent:

@@ -36,7 +36,8 @@ class PkvCacheStruct(ctypes.Structure):
                 ("page_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
                 ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
-                ("page_tags", ctypes.c_void_p)]
+                ("page_tags", ctypes.c_void_p),
+                ("k_row_scale", ctypes.c_void_p), ("v_row_scale", ctypes.c_void_p)]
 
 
 def _load() -> ctypes.CDLL:
@@ -120,6 +121,9 @@ class Cache:
             (V is the first ``latent_dim_v`` values of each K row)
     k_scale, v_scale: float32 [Hkv] (e4m3 only)
     page_tags: int32 or uint32 [num_pages]
+    k_row_scale, v_row_scale: float32 [num_pages, Hkv, P], scales set at
+            append, one per row (e4m3 with separate pools); None = the
+            static per-head scales
     """
     k_pool: torch.Tensor
     v_pool: torch.Tensor | None = None
@@ -127,6 +131,8 @@ class Cache:
     v_scale: torch.Tensor | None = None
     page_tags: torch.Tensor | None = None
     latent_dim_v: int | None = None
+    k_row_scale: torch.Tensor | None = None
+    v_row_scale: torch.Tensor | None = None
 
     @property
     def dtype(self) -> int:
@@ -159,15 +165,20 @@ class Cache:
             raise ValueError("K and V pools differ in dtype")
         if self.v_pool is None and self.latent_dim_v is None:
             raise ValueError("latent layout needs latent_dim_v")
-        for t in (self.k_scale, self.v_scale):
+        for t in (self.k_scale, self.v_scale, self.k_row_scale, self.v_row_scale):
             if t is not None and t.dtype != torch.float32:
                 raise ValueError("scales are float32")
+        for t in (self.k_row_scale, self.v_row_scale):
+            if t is not None and tuple(t.shape) != (self.num_pages, self.num_kv_heads,
+                                                    self.page_size):
+                raise ValueError("row scales are [num_pages, num_kv_heads, page_size]")
         if self.page_tags is not None and self.page_tags.element_size() != 4:
             raise ValueError("page tags are 32-bit")
         return PkvCacheStruct(_ptr(self.k_pool), _ptr(self.v_pool), self.dtype, self.num_pages,
                               self.page_size, self.num_kv_heads, self.head_dim_k,
                               self.head_dim_v, _ptr(self.k_scale), _ptr(self.v_scale),
-                              _ptr(self.page_tags))
+                              _ptr(self.page_tags), _ptr(self.k_row_scale),
+                              _ptr(self.v_row_scale))
 
 
 def _need(t: torch.Tensor, dtype, name: str):

@@ -22,7 +22,11 @@ inline int check_cache(const pkv_cache* c) {
   if (c->head_dim_k < 16 || c->head_dim_k % 16 || c->head_dim_v < 16 || c->head_dim_v % 16)
     return PKV_EINVAL;
   if (!c->v_pool && c->head_dim_v > c->head_dim_k) return PKV_EINVAL;
-  if (c->dtype == PKV_KV_E4M3 && (!c->k_scale || (c->v_pool && !c->v_scale))) return PKV_EINVAL;
+  const bool rows = c->k_row_scale || c->v_row_scale;
+  if (rows && (!c->k_row_scale || !c->v_row_scale || c->dtype != PKV_KV_E4M3 || !c->v_pool))
+    return PKV_EINVAL;
+  if (c->dtype == PKV_KV_E4M3 && !rows && (!c->k_scale || (c->v_pool && !c->v_scale)))
+    return PKV_EINVAL;
   return PKV_OK;
 }
 

@@ -222,6 +222,8 @@ extern "C" int pkv_decode_attn(const pkv_cache* cache, const void* q, int32_t nu
   p.v_pool = latent ? cache->k_pool : cache->v_pool;
   p.k_scale = cache->k_scale;
   p.v_scale = latent ? cache->k_scale : cache->v_scale;
+  p.k_row_scale = cache->k_row_scale;
+  p.v_row_scale = cache->v_row_scale;
   p.q = static_cast<const uint16_t*>(q);
   p.block_table = block_table;
   p.seq_lens = seq_lens;
@@ -242,6 +244,12 @@ extern "C" int pkv_decode_attn(const pkv_cache* cache, const void* q, int32_t nu
   p.v_row = latent ? dk : dv;
   p.sm_scale_log2 = sm_scale * kLog2e;
   const bool e4m3 = cache->dtype == PKV_KV_E4M3;
+  if (cache->k_row_scale) {
+    // scales set at append: the grouped-query MFMA kernel reads them
+    if (gqa_mfma_path_supported(dk, dv, G, latent, split_tokens, cache->page_size))
+      return launch_decode_gqa_mfma(p, static_cast<int>(n_split_blocks), batch, stream);
+    return PKV_EUNSUPPORTED;
+  }
   if (latent && mla_fast_path_supported(dk, dv, cache->num_kv_heads, num_q_heads,
                                         cache->page_size, split_tokens))
     return launch_decode_mla(p, e4m3, static_cast<int>(n_split_blocks), batch, stream);
@@ -272,6 +280,7 @@ extern "C" int pkv_decode_attn_drafts(const pkv_cache* cache, const void* q, int
   if (n_split_blocks > max_splits) return PKV_EINVAL;
   if (!(sm_scale == sm_scale)) return PKV_EINVAL;
   const bool latent = cache->v_pool == nullptr;
+  if (cache->k_row_scale) return PKV_EUNSUPPORTED;
   if (!drafts_path_supported(cache->head_dim_k, cache->head_dim_v, latent,
                              cache->dtype == PKV_KV_E4M3))
     return PKV_EUNSUPPORTED;

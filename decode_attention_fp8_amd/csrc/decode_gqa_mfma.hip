@@ -9,7 +9,8 @@
 // One wave per work unit (request, kv head, split), in the one-dimensional
 // longest-first order of find_unit. A split runs in tiles of 32 tokens whose
 // K and V bytes (4 KB each) travel HBM -> LDS by direct-to-LDS loads into a
-// ring of kSlots tiles.
+// ring of kSlots tiles. With scales set at append (one per row), a tile's 32
+// K and 32 V row scales travel with it (two more loads, 512 bytes of slot).
 #include "common.h"
 #include "decode_params.h"
 #include "gqa_mfma_tile.h"
@@ -22,24 +23,26 @@ using namespace gqa_mfma;
 constexpr int kPageVecs = 4;  // page offsets per lane
 constexpr int kMaxUnitPages = 64 * kPageVecs;
 
-template <int N>
+// every tile is L loads; wait until only the `ahead` younger tiles remain
+template <int N, int L>
 __device__ __forceinline__ void wait_tiles(int ahead) {
-  // every tile is 8 loads; wait until only the `ahead` younger tiles remain
   if (N >= 3 && ahead >= 3) {
-    wait_vm<24>();
+    wait_vm<3 * L>();
   } else if (N >= 2 && ahead >= 2) {
-    wait_vm<16>();
+    wait_vm<2 * L>();
   } else if (ahead >= 1) {
-    wait_vm<8>();
+    wait_vm<L>();
   } else {
     wait_vm<0>();
   }
 }
 
-template <int kSlots>
+template <int kSlots, bool kRowScales>
 __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
   static_assert(kSlots >= 2 && kSlots <= 4, "ring of 2 to 4 tiles");
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kSlots * kTileBytes];
+  constexpr int kSlotBytes = kTileBytes + (kRowScales ? 512 : 0);
+  constexpr int kLoads = kRowScales ? 10 : 8;  // loads per tile
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kSlots * kSlotBytes];
   __shared__ float rowbuf[kRows];
   const int lane = threadIdx.x;
   const int col = lane & 15, qg = lane >> 4;
@@ -70,8 +73,9 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
       }
     }
   }
-  const float qk_scale = p.k_scale[g] * p.sm_scale_log2;
-  const float o_scale = p.v_scale[g];
+  // row scales: each row's own, applied per token in the tile math
+  const float qk_scale = kRowScales ? p.sm_scale_log2 : p.k_scale[g] * p.sm_scale_log2;
+  const float o_scale = kRowScales ? 1.0f : p.v_scale[g];
 
   // the unit's pages: lane j holds the byte offsets of (page 64 h + j, kv
   // head g) in vector h < kPageVecs (named variables, so that selecting one
@@ -123,15 +127,25 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(o), jl));
     return off + static_cast<uint32_t>(((gg << 4) & (P - 1)) * kD);
   };
-  // 8 loads per tile, always: a 16-token group past the unit's end loads the
-  // tile's first group again (its scores are masked and its V rows zeroed)
+  // kLoads loads per tile, always: a 16-token group past the unit's end
+  // loads the tile's first group again (its scores are masked and its V rows
+  // zeroed)
   auto issue = [&](int t) __attribute__((always_inline)) {
-    const uint32_t slot = ring0 + (t % kSlots) * kTileBytes;
+    const uint32_t slot = ring0 + (t % kSlots) * kSlotBytes;
+    uint64_t offs[2];
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int gg = (t_begin + kTile * t + 16 * x < t_end) ? 2 * t + x : 2 * t;
-      const uint64_t off = group_base(gg);
-      dma_group(slot, x, lo, kpool + off, vpool + off);
+      offs[x] = group_base(gg);
+      dma_group(slot, x, lo, kpool + offs[x], vpool + offs[x]);
+    }
+    if constexpr (kRowScales) {
+      // a row's scale sits at 4 bytes per 128 of its codes; lanes 0..31 load
+      // the tile rows' scales (lanes 32..63 repeat them)
+      const uint32_t so = static_cast<uint32_t>(((lane >> 4) & 1 ? offs[1] : offs[0]) >> 5) +
+                          4u * (lane & 15);
+      dma4(slot + kTileBytes, so, reinterpret_cast<const uint8_t*>(p.k_row_scale));
+      dma4(slot + kTileBytes + 256, so, reinterpret_cast<const uint8_t*>(p.v_row_scale));
     }
   };
 
@@ -142,12 +156,13 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
     if (k < n_tiles) issue(k);
   for (int t = 0; t < n_tiles; ++t) {
     if (t + kSlots - 1 < n_tiles) issue(t + kSlots - 1);
-    wait_tiles<kSlots - 1>(min(kSlots - 1, n_tiles - 1 - t));
+    wait_tiles<kSlots - 1, kLoads>(min(kSlots - 1, n_tiles - 1 - t));
     const int tile0 = t_begin + kTile * t;
     const bool g0_ok = page_ok(((2 * t) << 4) >> log2P);
     const bool g1_ok = tile0 + 16 < t_end && page_ok(((2 * t + 1) << 4) >> log2P);
-    tile_math(ring + (t % kSlots) * kTileBytes, lo, qf, qk_scale, g0_ok, g1_ok,
-              min(kTile, t_end - tile0), rowbuf, a);
+    uint8_t* buf = ring + (t % kSlots) * kSlotBytes;
+    tile_math<kRowScales>(buf, lo, qf, qk_scale, g0_ok, g1_ok, min(kTile, t_end - tile0),
+                          rowbuf, a, reinterpret_cast<const float*>(buf + kTileBytes));
   }
   finish(p, b, g, c, G, o_scale, rowbuf, a);
 }
@@ -164,6 +179,13 @@ int launch_decode_gqa_mfma(const DecodeParams& p, int n_split_blocks, int batch,
                            hipStream_t stream) {
   const int64_t units = static_cast<int64_t>(n_split_blocks) * p.num_kv_heads * batch;
   if (units > 0x7FFFFFFF) return PKV_EUNSUPPORTED;
-  decode_gqa_mfma_kernel<2><<<dim3(static_cast<uint32_t>(units)), 64, 0, stream>>>(p);
+  if (p.k_row_scale) {
+    // row-scale offsets are 32-bit
+    if (static_cast<int64_t>(p.num_pages) * p.num_kv_heads * p.page_size * 4 > 0xFFFFFFFFLL)
+      return PKV_EUNSUPPORTED;
+    decode_gqa_mfma_kernel<2, true><<<dim3(static_cast<uint32_t>(units)), 64, 0, stream>>>(p);
+  } else {
+    decode_gqa_mfma_kernel<2, false><<<dim3(static_cast<uint32_t>(units)), 64, 0, stream>>>(p);
+  }
   return pkv::launch_status();
 }

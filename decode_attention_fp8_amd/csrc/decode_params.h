@@ -9,6 +9,8 @@ struct DecodeParams {
   const void* v_pool;  // == k_pool for the latent layout
   const float* k_scale;
   const float* v_scale;
+  const float* k_row_scale;  // [pages][kv heads][P] scales set at append, or NULL
+  const float* v_row_scale;
   const uint16_t* q;
   const int32_t* block_table;
   const int32_t* seq_lens;

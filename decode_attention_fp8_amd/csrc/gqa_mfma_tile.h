@@ -1,5 +1,5 @@
 // One 32-token tile of grouped-query decode on MFMA 16x16x32 (internal),
-// shared by the dispatched and the persistent e4m3 kernels.
+// the tile math of the e4m3 grouped-query kernel.
 //
 // "Smaller, faster, safer: running Kimi and GLM at scale" (Cloudflare blog),
 // section "Quantizing the KV cache": K and V are held as e4m3 and the
@@ -126,10 +126,16 @@ __device__ __forceinline__ void acc_init(Acc& a) {
 
 // QK^T, softmax and PV of the tile in buf. Group x of the tile holds valid
 // rows only if gx_ok (its page is in the pool); of the tile's 32 rows the
-// first nv are in the unit. rowbuf: 16 floats of LDS.
+// first nv are in the unit. rowbuf: 16 floats of LDS. kRowScales: the tile's
+// rows carry their own scales (set at append), in LDS at rs[t] (K) and
+// rs[64 + t] (V) for tile row t; a score is multiplied by its row's K scale
+// and a numerator by its row's V scale before PV (the denominator takes the
+// unscaled numerator), masked rows contributing nothing.
+template <bool kRowScales>
 __device__ __forceinline__ void tile_math(uint8_t* buf, const LaneOffsets& o,
                                           const bf16x8_t (&qf)[4], float qk_scale, bool g0_ok,
-                                          bool g1_ok, int nv, float* rowbuf, Acc& a) {
+                                          bool g1_ok, int nv, float* rowbuf, Acc& a,
+                                          const float* rs = nullptr) {
   const int lane = threadIdx.x;
   const int col = lane & 15, qg = lane >> 4;
   const bool full = g0_ok && g1_ok && nv == kTile;
@@ -160,12 +166,21 @@ __device__ __forceinline__ void tile_math(uint8_t* buf, const LaneOffsets& o,
     }
   }
   // s[x][i]: head col, tile row 16 x + 4 qg + i
+  float4 ks[2], vs[2];
+  if constexpr (kRowScales) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      ks[x] = *reinterpret_cast<const float4*>(rs + 16 * x + 4 * qg);
+      vs[x] = *reinterpret_cast<const float4*>(rs + 64 + 16 * x + 4 * qg);
+    }
+  }
   float tmax = -INFINITY;
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float v = s[x][i] * qk_scale;
+      if constexpr (kRowScales) v *= (&ks[x].x)[i];
       if (!full) {
         const int tt = 16 * x + 4 * qg + i;
         v = (tt < nv && (x == 0 ? g0_ok : g1_ok)) ? v : -INFINITY;
@@ -207,7 +222,12 @@ __device__ __forceinline__ void tile_math(uint8_t* buf, const LaneOffsets& o,
     for (int i = 0; i < 4; ++i) {
       const float pr = __builtin_amdgcn_exp2f(s[x][i] - a.m);
       a.l += pr;
-      pf[4 * x + i] = static_cast<_Float16>(pr);
+      if constexpr (kRowScales) {
+        // a masked row's scale may be unwritten: its numerator stays 0
+        pf[4 * x + i] = static_cast<_Float16>(s[x][i] == -INFINITY ? 0.0f : pr * (&vs[x].x)[i]);
+      } else {
+        pf[4 * x + i] = static_cast<_Float16>(pr);
+      }
     }
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {

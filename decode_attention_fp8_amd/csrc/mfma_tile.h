@@ -29,6 +29,14 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const uint8_t
                : "memory");
 }
 
+// 4 bytes per lane, global -> LDS: lane i's bytes land at lds + 4 i
+__device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, const uint8_t* base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(base)
+               : "memory");
+}
+
 // wait until at most N of this wave's vector memory loads are outstanding
 template <int N>
 __device__ __forceinline__ void wait_vm() {

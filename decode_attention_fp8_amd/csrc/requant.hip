@@ -60,6 +60,7 @@ extern "C" int pkv_requantize_pages(const pkv_cache* src, const pkv_cache* dst,
   st = pkv::check_cache(dst);
   if (st) return st;
   if (src->dtype != PKV_KV_BF16 || dst->dtype != PKV_KV_E4M3) return PKV_EINVAL;
+  if (dst->k_row_scale) return PKV_EUNSUPPORTED;  // pages of static-scale pools only
   if (src->page_size != dst->page_size || src->num_kv_heads != dst->num_kv_heads ||
       src->head_dim_k != dst->head_dim_k || src->head_dim_v != dst->head_dim_v ||
       (src->v_pool == nullptr) != (dst->v_pool == nullptr))

@@ -19,9 +19,10 @@ BF16_NAN = 0x7FC0
 
 def allocate_cache(num_pages: int, num_kv_heads: int, page_size: int, head_dim_k: int,
                    head_dim_v: int, kv_dtype: str = "fp8", latent: bool = False,
-                   device="cuda", poison: bool = True) -> Cache:
+                   device="cuda", poison: bool = True, row_scales: bool = False) -> Cache:
     """Pools filled with NaN codes (so any read of an unwritten row shows),
-    unit scales and zero tags."""
+    unit scales and zero tags. row_scales: also one scale per row, set at
+    append (e4m3 with separate pools), poisoned with NaN like the codes."""
     shape_k = (num_pages, num_kv_heads, page_size, head_dim_k)
     shape_v = (num_pages, num_kv_heads, page_size, head_dim_v)
     if kv_dtype == "fp8":
@@ -34,9 +35,16 @@ def allocate_cache(num_pages: int, num_kv_heads: int, page_size: int, head_dim_k
     k = mk(shape_k)
     v = None if latent else mk(shape_v)
     ones = lambda: torch.ones(num_kv_heads, dtype=torch.float32, device=device)
+    rows = None
+    if row_scales:
+        if kv_dtype != "fp8" or latent:
+            raise ValueError("row scales need an e4m3 cache with separate K and V pools")
+        rows = [torch.full((num_pages, num_kv_heads, page_size), float("nan") if poison else 0.0,
+                           dtype=torch.float32, device=device) for _ in range(2)]
     return Cache(k_pool=k, v_pool=v, k_scale=ones(), v_scale=ones(),
                  page_tags=torch.zeros(num_pages, dtype=torch.int32, device=device),
-                 latent_dim_v=head_dim_v if latent else None)
+                 latent_dim_v=head_dim_v if latent else None,
+                 k_row_scale=rows[0] if rows else None, v_row_scale=rows[1] if rows else None)
 
 
 class DecodeStep:

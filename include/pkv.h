@@ -90,6 +90,15 @@ typedef struct pkv_cache {
   const float* k_scale;
   const float* v_scale;
   const uint32_t* page_tags;
+  /* Scales set at append, one per cached row (e4m3, separate K and V pools
+   * only): float32 [num_pages][num_kv_heads][page_size], indexed like the
+   * rows. When both are non-NULL, pkv_append gives each new row the scale
+   * fl32(amax(row) / 448) (1 for an all-zero row), stores it here and
+   * encodes the row under it, and decode reads each row with its own
+   * scale; k_scale and v_scale are then not used. Both NULL: the static
+   * per-head scales. */
+  float* k_row_scale;
+  float* v_row_scale;
 } pkv_cache;
 
 /*

@@ -12,15 +12,15 @@ ATOL, RTOL = 2e-3, 1e-2
 
 class State:
     def __init__(self, w, kv_dtype: str, split_tokens: int | None = None, verify: bool = True,
-                 device="cuda"):
+                 device="cuda", row_scales: bool = False):
         self.w = w
         self.kv_dtype = kv_dtype
         c = pkv.allocate_cache(w.num_pages, w.num_kv_heads, w.page_size, w.head_dim_k,
-                               w.head_dim_v, kv_dtype, w.latent, device)
+                               w.head_dim_v, kv_dtype, w.latent, device, row_scales=row_scales)
         self.cache = c
         k = w.k_all(device)
         v = None if w.latent else w.v_all(device)
-        if kv_dtype == "fp8":
+        if kv_dtype == "fp8" and not row_scales:
             pkv.pkv_scales_from_amax(k, w.per_head_scales, c.k_scale)
             if w.latent:
                 c.v_scale = c.k_scale
