@@ -32,16 +32,18 @@ def _ref(lay, rows, codes=None, scales=None):
     return int4.linear(x, packed, s[:, rows])
 
 
-@pytest.mark.parametrize("batch", [1, 5, 16, 17, 33, 64])
+@pytest.mark.parametrize("batch", [1, 2, 3, 5, 8, 9, 16, 17, 33, 64])
 @pytest.mark.parametrize("n,k", [(64, 1024), (96, 2048), (32, 4096)])
 def test_small_layers_every_output(batch, n, k):
-    """One to eight groups per wave, one to four token tiles, ragged batches."""
+    """One to eight groups per wave, one to four token tiles, ragged batches;
+    up to 8 tokens with k a multiple of 2048 take the direct-to-LDS kernel
+    (x rings of 2, 4 and 8 tokens), the rest the register kernel."""
     lay = W.int4_custom(f"i4_{n}_{k}_{batch}", 40 + batch, n, k, batch)
     y = _gpu(lay)
     assert_close(y, _ref(lay, np.arange(n)), f"{lay.name}")
 
 
-@pytest.mark.parametrize("batch", [1, 64])
+@pytest.mark.parametrize("batch", [1, 8, 64])
 def test_full_size_sampled_rows(batch):
     """The benchmark's 8192 x 8192 layer: every token of 48 sampled rows
     (first and last rows of workgroups, random others)."""
@@ -53,10 +55,12 @@ def test_full_size_sampled_rows(batch):
 
 
 @pytest.mark.parametrize("byte", [0x88, 0x77, 0x0F, 0xF0])
-def test_extreme_and_mixed_sign_codes(byte):
-    """All codes -8, all 7, and alternating 0 / -1 patterns."""
-    lay = W.int4_custom("i4x", 50, 64, 1024, 16)
-    codes = torch.full((64, 512), byte, dtype=torch.uint8)
+@pytest.mark.parametrize("k,batch", [(1024, 16), (2048, 4)])
+def test_extreme_and_mixed_sign_codes(byte, k, batch):
+    """All codes -8, all 7, and alternating 0 / -1 patterns, through both
+    kernels."""
+    lay = W.int4_custom("i4x", 50, 64, k, batch)
+    codes = torch.full((64, k // 2), byte, dtype=torch.uint8)
     y = _gpu(lay, codes=codes)
     assert_close(y, _ref(lay, np.arange(64), codes=codes), f"codes 0x{byte:02x}")
 
