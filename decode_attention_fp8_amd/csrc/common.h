@@ -69,8 +69,9 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float y) {
 }
 
 // 16 bf16 values (two 16-byte words) -> 16 e4m3 codes of fl32(x / s), one
-// 16-byte word.
-__device__ __forceinline__ uint4 encode16(const uint4& w0, const uint4& w1, float s) {
+// 16-byte word: the definition step by step (correctly rounded division,
+// then the IEEE-bit encoder).
+__device__ __forceinline__ uint4 encode16_exact(const uint4& w0, const uint4& w1, float s) {
   const uint32_t in[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
   uint32_t out[4];
 #pragma unroll
@@ -85,6 +86,52 @@ __device__ __forceinline__ uint4 encode16(const uint4& w0, const uint4& w1, floa
       const uint32_t c1 = e4m3_rne_sat(__fdiv_rn(hi, s));
       word |= (c0 | (c1 << 8)) << (16 * j);
     }
+    out[k] = word;
+  }
+  return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+// fl32(x / s) clamped to +-448, for s in [2^-60, 2^60] and x not NaN, with
+// r = fl32(1 / s) and c = 512 s. Markstein's division: q0 = fl32(x r) is
+// within one ulp of x / s, the residual x - q0 s is exact in one FMA, and
+// q0 + (x - q0 s) r then rounds to the correctly rounded quotient. The scale
+// range and the clamp of x to +-c keep every step clear of overflow and
+// underflow wherever the e4m3 code depends on more than the sign (quotients
+// at or above 2^-11); the sign comes from q0, which keeps that of x even when
+// the correction returns +0 for x = -0.
+__device__ __forceinline__ float quotient_sat(float x, float s, float r, float c) {
+  const float xc = fminf(fmaxf(x, -c), c);
+  const float q0 = xc * r;
+  const float e = fmaf(-q0, s, xc);
+  const float q = copysignf(fmaf(e, r, q0), q0);
+  return fminf(fmaxf(q, -448.0f), 448.0f);
+}
+
+// encode16_exact, faster: the quotient by quotient_sat and the rounding by
+// the e4m3 conversion instruction, which rounds to nearest even on
+// [-448, 448] (the clamp gives the saturation). A word holding a NaN, or a
+// scale outside [2^-60, 2^60], takes encode16_exact.
+__device__ __forceinline__ uint4 encode16(const uint4& w0, const uint4& w1, float s) {
+  const uint32_t in[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  // a bf16 half h is NaN iff (h & 0x7FFF) > 0x7F80, iff adding 0x7F to it
+  // sets its bit 15 (no carry leaves the half)
+  uint32_t nan = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) nan |= (in[i] & 0x7FFF7FFFu) + 0x007F007Fu;
+  if ((nan & 0x80008000u) != 0 || !(s >= 0x1p-60f && s <= 0x1p60f))
+    return encode16_exact(w0, w1, s);
+  const float r = __fdiv_rn(1.0f, s), c = 512.0f * s;
+  uint32_t out[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t p0 = in[2 * k], p1 = in[2 * k + 1];
+    const float y0 = quotient_sat(__uint_as_float(p0 << 16), s, r, c);
+    const float y1 = quotient_sat(__uint_as_float(p0 & 0xFFFF0000u), s, r, c);
+    const float y2 = quotient_sat(__uint_as_float(p1 << 16), s, r, c);
+    const float y3 = quotient_sat(__uint_as_float(p1 & 0xFFFF0000u), s, r, c);
+    uint32_t word = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false));
+    word = static_cast<uint32_t>(
+        __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, static_cast<int>(word), true));
     out[k] = word;
   }
   return make_uint4(out[0], out[1], out[2], out[3]);

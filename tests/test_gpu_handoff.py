@@ -125,3 +125,99 @@ def test_handoff_rejects_bad_arguments():
     other = pkv.allocate_cache(w.num_pages, 1, 32, 64, 64, "fp8", False, dev)
     with pytest.raises(pkv.PkvError):
         pkv.pkv_requantize_pages(src, other, pages, pages)    # page sizes differ
+
+
+def _special_bf16_pool(rng, pages, heads, page, dim, scales):
+    """bf16 bit patterns [pages, heads, page, dim]: random values, then per
+    16-value chunk a set of special values (NaN of both signs, quiet and
+    signalling; infinities; signed zeros; the largest bf16; subnormals;
+    exact e4m3 ties and the saturation edge under each head's scale)."""
+    vals = rng.standard_normal((pages, heads, page, dim)).astype(np.float32) * 3.0
+    bits = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    specials_common = [0x7F80, 0xFF80, 0x0000, 0x8000, 0x7F7F, 0xFF7F, 0x0001, 0x8001, 0x007F]
+    nans = [0x7FC0, 0xFFC0, 0x7F81, 0xFF81]
+
+    def bf16_bits(x):
+        return int((np.array([x], dtype=np.float32).view(np.uint32)[0] >> 16) & 0xFFFF)
+
+    for h in range(heads):
+        s = float(scales[h])
+        # e4m3 midpoints (between 1 and 1.125, 2 and 2.25, the two smallest
+        # subnormals) and the saturation edge, times s: exact when s is a power of two
+        edge = [1.0625 * s, -1.0625 * s, 2.125 * s, 0.5 * 2.0 ** -9 * s, 1.5 * 2.0 ** -9 * s,
+                448.0 * s, -448.0 * s, 464.0 * s, 447.0 * s, 480.0 * s]
+        extra = [bf16_bits(e) for e in edge]
+        flat = bits[:, h].reshape(-1)
+        chunks = flat.size // 16
+        for c in range(chunks):
+            base = 16 * c
+            if c % 3 == 0:     # a chunk holding a NaN
+                flat[base + c % 16] = nans[c % len(nans)]
+            pool = specials_common + extra
+            for j in range(4):
+                flat[base + (3 * j + c) % 16] = pool[(c * 4 + j) % len(pool)]
+        bits[:, h] = flat.reshape(bits[:, h].shape)
+    return bits
+
+
+@pytest.mark.parametrize("scales", [(0.125, 2.0 ** -70), (0.0371, 2.0 ** 61), (2.0 ** -60, 2.0 ** 60)])
+def test_handoff_special_values_bit_exact(scales):
+    """NaN, infinities, signed zeros, bf16 extremes and subnormals, e4m3 ties
+    and the saturation edge, under scales inside and outside [2^-60, 2^60]:
+    every code equals the oracle's."""
+    pages, H, P, D = 3, 2, 16, 128
+    rng = np.random.default_rng(61)
+    s32 = np.array(scales, dtype=np.float32)
+    kb = _special_bf16_pool(rng, pages, H, P, D, s32)
+    vb = _special_bf16_pool(rng, pages, H, P, D, s32[::-1].copy())
+    src = pkv.allocate_cache(pages, H, P, D, D, "bf16", False, dev, poison=False)
+    src.k_pool.copy_(torch.from_numpy(kb.view(np.int16)).to(dev).view(torch.bfloat16))
+    src.v_pool.copy_(torch.from_numpy(vb.view(np.int16)).to(dev).view(torch.bfloat16))
+    dst = pkv.allocate_cache(pages, H, P, D, D, "fp8", False, dev)
+    dst.k_scale.copy_(torch.from_numpy(s32).to(dev))
+    dst.v_scale.copy_(torch.from_numpy(s32[::-1].copy()).to(dev))
+    pg = torch.arange(pages, dtype=torch.int32, device=dev)
+    k0 = dst.k_pool.cpu().numpy()
+    v0 = dst.v_pool.cpu().numpy()
+    pkv.pkv_requantize_pages(src, dst, pg, pg)
+    torch.cuda.synchronize()
+    kv = (kb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    vv = (vb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    kc, _ = handoff.requantize_pages(kv, k0, None, list(range(pages)), list(range(pages)), s32)
+    vc, _ = handoff.requantize_pages(vv, v0, None, list(range(pages)), list(range(pages)),
+                                     s32[::-1].copy())
+    got_k, got_v = dst.k_pool.cpu().numpy(), dst.v_pool.cpu().numpy()
+    bad = np.argwhere(got_k != kc)
+    assert bad.size == 0, f"K codes differ at {bad[:4].tolist()}: {got_k[tuple(bad[0])]:#x} vs {kc[tuple(bad[0])]:#x}"
+    bad = np.argwhere(got_v != vc)
+    assert bad.size == 0, f"V codes differ at {bad[:4].tolist()}: {got_v[tuple(bad[0])]:#x} vs {vc[tuple(bad[0])]:#x}"
+
+
+def test_handoff_every_bf16_value_bit_exact():
+    """All 65536 bf16 bit patterns under six scales (one per kv head: powers
+    of two, amax-style values and both ends of [2^-60, 2^60]): every code
+    equals the oracle's."""
+    H, P, D = 6, 16, 128
+    pages = 65536 // (P * D)
+    rng = np.random.default_rng(62)
+    bits = np.empty((pages, H, P, D), dtype=np.uint16)
+    for h in range(H):
+        bits[:, h] = rng.permutation(65536).astype(np.uint16).reshape(pages, P, D)
+    s32 = np.array([1.0, 0.125, 0.0371, 3.7 / 448.0, 2.0 ** -60, 2.0 ** 60], dtype=np.float32)
+    src = pkv.allocate_cache(pages, H, P, D, D, "bf16", False, dev, poison=False)
+    src.k_pool.copy_(torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16))
+    src.v_pool.copy_(src.k_pool)
+    dst = pkv.allocate_cache(pages, H, P, D, D, "fp8", False, dev)
+    dst.k_scale.copy_(torch.from_numpy(s32).to(dev))
+    dst.v_scale.copy_(torch.from_numpy(s32[::-1].copy()).to(dev))
+    pg = torch.arange(pages, dtype=torch.int32, device=dev)
+    pkv.pkv_requantize_pages(src, dst, pg, pg)
+    torch.cuda.synchronize()
+    vals = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for pool, sc in ((dst.k_pool, s32), (dst.v_pool, s32[::-1].copy())):
+        got = pool.cpu().numpy()
+        for h in range(H):
+            want = quant.quantize(vals[:, h], sc[h])
+            bad = np.argwhere(got[:, h] != want)
+            assert bad.size == 0, (f"scale {sc[h]!r}: {len(bad)} codes differ, first x = "
+                                   f"{vals[:, h][tuple(bad[0])]!r}")
