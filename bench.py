@@ -306,10 +306,11 @@ def time_int4(steps: int, warmup: int, layers: int = 16, n: int = 8192, k: int =
     for B in (1, 8, 16, 32, 64):
         x = lays[0].x("cuda")[:B].contiguous()
         y = torch.empty((B, n), dtype=torch.bfloat16, device="cuda")
+        ws = pkv.int4_workspace(B, n, k, "cuda")
 
         def step_int4():
             for i in range(layers):
-                pkv.pkv_int4_linear(x, codes[i], scales[i], y)
+                pkv.pkv_int4_linear(x, codes[i], scales[i], y, ws)
 
         def step_bf16():
             for i in range(layers):
@@ -349,7 +350,9 @@ def time_int4(steps: int, warmup: int, layers: int = 16, n: int = 8192, k: int =
     del codes, scales, wbf
     torch.cuda.empty_cache()
     return {"layer": f"{n}x{k} INT4 (group 128, bf16 scales), {layers} distinct layers per step",
-            "bytes_per_layer": w_bytes // layers, "kernel": "int4_linear_kernel", "rows": rows}
+            "bytes_per_layer": w_bytes // layers,
+            "kernel": "int4_lds_kernel (batch <= 8), int4_split_kernel + int4_sum_kernel (above)",
+            "rows": rows}
 
 
 def cpu_baseline(w, budget_s: float = 12.0):

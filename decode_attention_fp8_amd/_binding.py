@@ -21,6 +21,7 @@ PKV_KV_E4M3, PKV_KV_BF16 = 1, 2
 
 EXPORTS = ("pkv_scales_from_amax", "pkv_append", "pkv_verify", "pkv_decode_attn",
            "pkv_combine", "pkv_decode_attn_drafts", "pkv_requantize_pages", "pkv_int4_linear",
+           "pkv_int4_linear_workspace",
            "pkv_suggest_split", "pkv_strerror", "pkv_version")
 
 
@@ -56,7 +57,8 @@ def _load() -> ctypes.CDLL:
         "pkv_decode_attn_drafts": (I32, [CP, P, I32, I32, P, P, I32, I32, I32, P, F, I32, I32, P,
                                          P, P]),
         "pkv_requantize_pages": (I32, [CP, CP, P, P, P, P, I32, P]),
-        "pkv_int4_linear": (I32, [P, P, P, I32, I32, I32, P, P]),
+        "pkv_int4_linear": (I32, [P, P, P, I32, I32, I32, P, P, P]),
+        "pkv_int4_linear_workspace": (I64, [I32, I32, I32]),
         "pkv_suggest_split": (I32, [CP, I32, I32, I64, I32]),
         "pkv_strerror": (ctypes.c_char_p, [I32]),
         "pkv_version": (I32, []),
@@ -231,9 +233,10 @@ def pkv_decode_attn_drafts(cache: Cache, q: torch.Tensor, block_table: torch.Ten
 
 
 def pkv_int4_linear(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor, y: torch.Tensor,
-                    stream=None) -> None:
+                    workspace: torch.Tensor | None = None, stream=None) -> None:
     """y bf16 [B, n] = x bf16 [B, k] times the INT4 weights w uint8 [n, k/2]
-    with bf16 group scales [k/128, n]."""
+    with bf16 group scales [k/128, n]; workspace: a uint8 device tensor of at
+    least pkv_int4_linear_workspace(B, n, k) bytes, or None."""
     _need(x, torch.bfloat16, "x")
     _need(scales, torch.bfloat16, "scales")
     _need(y, torch.bfloat16, "y")
@@ -243,8 +246,30 @@ def pkv_int4_linear(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor, y: t
     n = w.shape[0]
     if w.shape[1] * 2 != k or tuple(scales.shape) != (k // 128, n) or tuple(y.shape) != (B, n):
         raise ValueError("pkv_int4_linear: shapes x [B, k], w [n, k/2], scales [k/128, n], y [B, n]")
+    ws = None
+    if workspace is not None:
+        need = pkv_int4_linear_workspace(B, n, k)
+        if workspace.device != x.device or workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace: at least {need} bytes on {x.device}")
+        ws = _ptr(workspace)
     _check("pkv_int4_linear", _lib.pkv_int4_linear(_ptr(x), _ptr(w), _ptr(scales), B, n, k,
-                                                   _ptr(y), _stream(stream)))
+                                                   _ptr(y), ws, _stream(stream)))
+
+
+def pkv_int4_linear_workspace(batch: int, n: int, k: int) -> int:
+    """Bytes of workspace pkv_int4_linear wants (0: none)."""
+    r = int(_lib.pkv_int4_linear_workspace(batch, n, k))
+    if r < 0:
+        _check("pkv_int4_linear_workspace", r)
+    return r
+
+
+def int4_workspace(max_batch: int, n: int, k: int, device) -> torch.Tensor | None:
+    """A workspace for pkv_int4_linear calls of up to max_batch tokens on an
+    n x k layer (None if they need none); reusable across calls and shapes
+    that fit it."""
+    need = max(pkv_int4_linear_workspace(b, n, k) for b in range(1, max_batch + 1))
+    return torch.zeros((need,), dtype=torch.uint8, device=device) if need else None
 
 
 def pkv_requantize_pages(src: Cache, dst: Cache, src_pages: torch.Tensor, dst_pages: torch.Tensor,

@@ -70,10 +70,10 @@ __device__ __forceinline__ bf16x8_t neg136() {
 // one 128-input group of kM row tiles against T token tiles: xv the B
 // operands, c the codes of row 16 m + col, sq the scales of rows 16 m + 4 qg
 // .. + 3
-template <int T>
-__device__ __forceinline__ void group_math(const bf16x8_t (&xv)[T][4], const uint4 (&c)[kM],
-                                           const uint2 (&sq)[kM], bf16x8_t neg, uint32_t mask,
-                                           uint32_t expo, floatx4_t (&acc)[kM][T]) {
+template <int T, int M = kM>
+__device__ __forceinline__ void group_math(const bf16x8_t (&xv)[T][4], const uint4 (&c)[M],
+                                           const uint2 (&sq)[M], bf16x8_t neg, uint32_t mask,
+                                           uint32_t expo, floatx4_t (&acc)[M][T]) {
   floatx4_t dn[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
@@ -83,7 +83,7 @@ __device__ __forceinline__ void group_math(const bf16x8_t (&xv)[T][4], const uin
       dn[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg, xv[t][s], dn[t], 0, 0, 0);
   }
 #pragma unroll
-  for (int m = 0; m < kM; ++m) {
+  for (int m = 0; m < M; ++m) {
     const bf16x8_t a0 = codes_to_bf16(c[m].x ^ 0x88888888u, mask, expo),
                    a1 = codes_to_bf16(c[m].y ^ 0x88888888u, mask, expo),
                    a2 = codes_to_bf16(c[m].z ^ 0x88888888u, mask, expo),
@@ -304,6 +304,163 @@ __global__ void __launch_bounds__(64 * kWaves)
   reduce_store<T>(red, acc, wv, lane, r0, batch, N, y);
 }
 
+// ---------------------------------------------------------------------------
+// Above 8 tokens, with a workspace: the 8 waves of a workgroup take 16 rows
+// each of a 128-row block over the same slice of the inputs, so the x tile
+// (16 TT token rows x 256 inputs) is staged once through LDS for all of
+// them. When there are too few row blocks to fill the chip, the inputs are
+// split over KS workgroups of a block, which write fp32 partial sums to the
+// workspace; int4_sum_kernel then adds the KS partials of each output in
+// slice order and rounds to bf16. (The last workgroup of a block could add
+// them itself, but making the partials of other XCDs visible to it takes a
+// write-back of each XCD's L2 per workgroup, which costs more than the
+// second launch.) Each tile: per wave 2 direct-to-LDS loads of
+// codes (16 rows x 128 bytes, the same swizzle as above), one of scales and
+// TT of x (each 1 KB: two token rows, 16-byte chunk p of row t at
+// p ^ (t & 15)); three slots, two tiles in flight while one is computed.
+constexpr int kBlockRows = 16 * kWaves;  // rows per workgroup
+
+template <int TT>
+__global__ void __launch_bounds__(64 * kWaves)
+    int4_split_kernel(const uint16_t* x, const uint8_t* w, const uint16_t* scales, int batch,
+                      int N, int K, int KC, float* part, uint16_t* y) {
+  constexpr int kSlots = 3;
+  constexpr int kXRowB = 512;                   // 256 inputs of one token
+  constexpr int kXB = 16 * TT * kXRowB;         // x tile
+  constexpr int kCodeB = 16 * 128, kScB = 256;  // one wave's codes and scales
+  constexpr int kCSlot = kCodeB + kScB;
+  constexpr int kLoads = 2 + 1 + TT;  // loads per wave and tile
+  __shared__ __attribute__((aligned(16))) uint8_t xring[kSlots * kXB];
+  __shared__ __attribute__((aligned(16))) uint8_t cring[kWaves * kSlots * kCSlot];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int col = lane & 15, qg = lane >> 4;
+  const int r0 = blockIdx.x * kBlockRows + 16 * wv;  // this wave's 16 rows
+  const int kc = blockIdx.y;
+  const int kb = kc * KC, tiles = KC / 256;
+  const uint32_t half = static_cast<uint32_t>(K) / 2;
+  const uint8_t* wring = cring + wv * kSlots * kCSlot;
+  const uint32_t cbase = __builtin_amdgcn_readfirstlane(lds_addr(wring));
+  const uint32_t xbase = lds_addr(xring);
+
+  uint32_t cvoff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 8 * j + (lane >> 3);
+    cvoff[j] = (r0 + row) * half + kb / 2 + 16 * ((lane & 7) ^ ((row >> 1) & 7));
+  }
+  // lanes 0 .. 7: rows 2 p, 2 p + 1 of the tile's first group, 8 .. 15 the
+  // second (the other lanes repeat them)
+  const uint32_t svoff = ((kb / kGroup + ((lane >> 3) & 1)) * N + r0 + 2 * (lane & 7)) * 2;
+  // x: this wave's instructions wv + 8 i cover token rows 2 (wv + 8 i) + 0, 1
+  uint32_t xvoff[TT];
+#pragma unroll
+  for (int i = 0; i < TT; ++i) {
+    const int row = 2 * (wv + 8 * i) + (lane >> 5);
+    const int tok = min(row, batch - 1);
+    xvoff[i] = (tok * K + kb) * 2 + 16 * ((lane & 31) ^ (row & 15));
+  }
+  const bf16x8_t neg = neg136();
+  uint32_t mask = 0x000F000Fu, expo = 0x43004300u;
+  asm volatile("" : "+v"(mask), "+v"(expo));
+  floatx4_t acc[1][TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) acc[0][tt] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const uint32_t cs = __builtin_amdgcn_readfirstlane(cbase + (t % kSlots) * kCSlot);
+    dma16(cs, cvoff[0] + 128 * t, w);
+    dma16(cs + 1024, cvoff[1] + 128 * t, w);
+    dma4(cs + kCodeB, svoff + 4 * N * t, reinterpret_cast<const uint8_t*>(scales));
+    const uint32_t xs = __builtin_amdgcn_readfirstlane(xbase + (t % kSlots) * kXB);
+#pragma unroll
+    for (int i = 0; i < TT; ++i)
+      dma16(xs + 1024 * (wv + 8 * i), xvoff[i] + kXRowB * t, reinterpret_cast<const uint8_t*>(x));
+  };
+  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+  issue(0);
+  if (tiles > 1) issue(1);
+  for (int t = 0; t < tiles; ++t) {
+    if (t + 1 < tiles) {
+      wait_vm<kLoads>();
+    } else {
+      wait_vm<0>();
+    }
+    // every wave's part of tile t has landed, and every wave is done with
+    // tile t - 1, whose slots tile t + 2 takes next
+    __syncthreads();
+    if (t + 2 < tiles) issue(t + 2);
+    const uint8_t* cbuf = wring + (t % kSlots) * kCSlot;
+    const uint8_t* xbuf = xring + (t % kSlots) * kXB;
+#pragma unroll
+    for (int gh = 0; gh < 2; ++gh) {
+      uint4 c[1];
+      uint2 sq[1];
+      c[0] = *reinterpret_cast<const uint4*>(cbuf + 128 * col +
+                                             16 * ((4 * gh + qg) ^ ((col >> 1) & 7)));
+      sq[0] = *reinterpret_cast<const uint2*>(cbuf + kCodeB + 32 * gh + 8 * qg);
+      bf16x8_t xv[TT][4];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const int row = 16 * tt + col;
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          xv[tt][s4] = *reinterpret_cast<const bf16x8_t*>(
+              xbuf + kXRowB * row + 16 * ((16 * gh + 4 * qg + s4) ^ (row & 15)));
+      }
+      group_math<TT, 1>(xv, c, sq, neg, mask, expo, acc);
+    }
+  }
+  // rows r0 + 4 qg + i, tokens 16 tt + col
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    const int token = 16 * tt + col;
+    if (token >= batch) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t o = static_cast<size_t>(token) * N + r0 + 4 * qg + i;
+      if (part) {
+        part[static_cast<size_t>(kc) * batch * N + o] = acc[0][tt][i];
+      } else {
+        y[o] = pkv::f32_to_bf16_rne(acc[0][tt][i]);
+      }
+    }
+  }
+}
+
+// y = bf16(sum over the KS input slices of the partials, in slice order),
+// 4 outputs a thread
+__global__ void __launch_bounds__(256) int4_sum_kernel(const float* part, int KS, size_t count,
+                                                       uint16_t* y) {
+  const size_t i = (static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= count) return;
+  float4 v = *reinterpret_cast<const float4*>(part + i);
+  for (int s = 1; s < KS; ++s) {
+    const float4 u = *reinterpret_cast<const float4*>(part + static_cast<size_t>(s) * count + i);
+    v.x += u.x;
+    v.y += u.y;
+    v.z += u.z;
+    v.w += u.w;
+  }
+  y[i] = pkv::f32_to_bf16_rne(v.x);
+  y[i + 1] = pkv::f32_to_bf16_rne(v.y);
+  y[i + 2] = pkv::f32_to_bf16_rne(v.z);
+  y[i + 3] = pkv::f32_to_bf16_rne(v.w);
+}
+
+// input slices per row block for the split kernel: enough workgroups to fill
+// the chip (about 192 or more), each slice whole tiles; 0 if the split kernel
+// does not apply
+int split_slices(int batch, int n, int k) {
+  if (batch <= 8 || n % kBlockRows) return 0;
+  if (static_cast<int64_t>(n) * k / 2 > 0xFFFFFFFFLL || static_cast<int64_t>(batch) * k * 2 > 0xFFFFFFFFLL)
+    return 0;
+  const int blocks = n / kBlockRows;
+  int ks = 1;
+  while (blocks * ks < 192 && ks < 8 && k % (256 * ks * 2) == 0) ks *= 2;
+  return k % (256 * ks) == 0 ? ks : 0;
+}
+
 template <int T>
 int launch_reg(const uint16_t* x, const uint8_t* w, const uint16_t* s, int batch, int n, int k,
                uint16_t* y, hipStream_t stream) {
@@ -318,16 +475,39 @@ int launch_lds(const uint16_t* x, const uint8_t* w, const uint16_t* s, int batch
   return pkv::launch_status();
 }
 
+// workspace: fp32 partials [ks][batch][n]
+int64_t partial_bytes(int ks, int batch, int n) { return static_cast<int64_t>(ks) * batch * n * 4; }
+
+template <int TT>
+int launch_split(const uint16_t* x, const uint8_t* w, const uint16_t* s, int batch, int n, int k,
+                 int ks, void* workspace, uint16_t* y, hipStream_t stream) {
+  float* part = ks > 1 ? static_cast<float*>(workspace) : nullptr;
+  int4_split_kernel<TT><<<dim3(n / kBlockRows, ks), 64 * kWaves, 0, stream>>>(
+      x, w, s, batch, n, k, k / ks, part, y);
+  int st = pkv::launch_status();
+  if (st || ks == 1) return st;
+  const size_t count = static_cast<size_t>(batch) * n;
+  int4_sum_kernel<<<dim3(static_cast<uint32_t>((count / 4 + 255) / 256)), 256, 0, stream>>>(
+      part, ks, count, y);
+  return pkv::launch_status();
+}
+
 }  // namespace
 
+extern "C" int64_t pkv_int4_linear_workspace(int32_t batch, int32_t n, int32_t k) {
+  if (batch < 1 || batch > 64 || n < 1 || k < 1) return PKV_EINVAL;
+  const int ks = split_slices(batch, n, k);
+  return ks > 1 ? partial_bytes(ks, batch, n) : 0;
+}
+
 extern "C" int pkv_int4_linear(const void* x, const uint8_t* w, const void* scales,
-                               int32_t batch, int32_t n, int32_t k, void* y,
+                               int32_t batch, int32_t n, int32_t k, void* y, void* workspace,
                                hipStream_t stream) {
   if (!x || !w || !scales || !y) return PKV_EINVAL;
   if (batch < 1 || batch > 64 || n < 1 || k < 1) return PKV_EINVAL;
   if (n % (16 * kM) || k % (kWaves * kGroup)) return PKV_EINVAL;
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) |
-       reinterpret_cast<uintptr_t>(scales)) & 15)
+       reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(workspace)) & 15)
     return PKV_EINVAL;
   const auto* xs = static_cast<const uint16_t*>(x);
   const auto* ss = static_cast<const uint16_t*>(scales);
@@ -340,6 +520,15 @@ extern "C" int pkv_int4_linear(const void* x, const uint8_t* w, const void* scal
     if (batch <= 2) return launch_lds<1>(xs, w, ss, batch, n, k, ys, stream);
     if (batch <= 4) return launch_lds<2>(xs, w, ss, batch, n, k, ys, stream);
     return launch_lds<4>(xs, w, ss, batch, n, k, ys, stream);
+  }
+  const int ks = split_slices(batch, n, k);
+  if (ks == 1 || (ks > 1 && workspace)) {
+    switch ((batch + 15) / 16) {
+      case 1: return launch_split<1>(xs, w, ss, batch, n, k, ks, workspace, ys, stream);
+      case 2: return launch_split<2>(xs, w, ss, batch, n, k, ks, workspace, ys, stream);
+      case 3: return launch_split<3>(xs, w, ss, batch, n, k, ks, workspace, ys, stream);
+      default: return launch_split<4>(xs, w, ss, batch, n, k, ks, workspace, ys, stream);
+    }
   }
   switch ((batch + 15) / 16) {
     case 1: return launch_reg<1>(xs, w, ss, batch, n, k, ys, stream);

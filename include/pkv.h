@@ -305,12 +305,26 @@ int pkv_requantize_pages(const pkv_cache* src, const pkv_cache* dst,
  *   scales: bf16 [k / 128][n] (group-major: one group's scales of
  *           consecutive rows are contiguous)
  *   y:      bf16 [batch][n], fully written
- * Accumulation is fp32. Device pointers, caller-owned; x, w and scales
- * 16-byte aligned. EINVAL: NULL pointers, batch outside [1, 64], n not a
- * multiple of 32, k not a multiple of 1024, misaligned pointers.
+ *   workspace: device scratch of at least pkv_int4_linear_workspace(batch,
+ *           n, k) bytes, 16-byte aligned, or NULL. Above 8 tokens, when the
+ *           rows alone give too few workgroups, the inputs are split over
+ *           several workgroups that leave fp32 partial sums here, and a
+ *           second kernel adds them up. Overwritten; nothing is kept between
+ *           calls, but calls sharing a workspace must not overlap in time.
+ *           Without a workspace such a call takes a slower kernel.
+ * Accumulation is fp32. Device pointers, caller-owned; x, w, scales and
+ * workspace 16-byte aligned. EINVAL: NULL pointers, batch outside [1, 64],
+ * n not a multiple of 32, k not a multiple of 1024, misaligned pointers.
  */
 int pkv_int4_linear(const void* x, const uint8_t* w, const void* scales, int32_t batch,
-                    int32_t n, int32_t k, void* y, hipStream_t stream);
+                    int32_t n, int32_t k, void* y, void* workspace, hipStream_t stream);
+
+/*
+ * Bytes of workspace pkv_int4_linear wants for this layer and batch (0: it
+ * needs none): the fp32 partial sums. EINVAL for batch outside [1, 64] or
+ * n, k < 1.
+ */
+int64_t pkv_int4_linear_workspace(int32_t batch, int32_t n, int32_t k);
 
 /*
  * Host helper: a split size for pkv_decode_attn on this cache and batch.

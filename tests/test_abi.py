@@ -110,13 +110,24 @@ def test_invalid_arguments_rejected_on_host():
     assert lib.pkv_combine(P, P, P, 1, 1, 64, 16, 3, 64, None, P, None, None) == E
     assert lib.pkv_combine(P, P, P, 1, 1, 60, 16, 4, 64, None, P, None, None) == E
     # INT4 linear: NULL, batch outside [1, 64], n not a multiple of 32, k not a
-    # multiple of 1024, misaligned pointers
-    assert lib.pkv_int4_linear(None, P, P, 1, 32, 1024, P, None) == E
-    assert lib.pkv_int4_linear(P, P, P, 0, 32, 1024, P, None) == E
-    assert lib.pkv_int4_linear(P, P, P, 65, 32, 1024, P, None) == E
-    assert lib.pkv_int4_linear(P, P, P, 1, 48, 1024, P, None) == E
-    assert lib.pkv_int4_linear(P, P, P, 1, 32, 1536, P, None) == E
-    assert lib.pkv_int4_linear(P + 8, P, P, 1, 32, 1024, P, None) == E
+    # multiple of 1024, misaligned pointers (the workspace too)
+    assert lib.pkv_int4_linear(None, P, P, 1, 32, 1024, P, None, None) == E
+    assert lib.pkv_int4_linear(P, P, P, 0, 32, 1024, P, None, None) == E
+    assert lib.pkv_int4_linear(P, P, P, 65, 32, 1024, P, None, None) == E
+    assert lib.pkv_int4_linear(P, P, P, 1, 48, 1024, P, None, None) == E
+    assert lib.pkv_int4_linear(P, P, P, 1, 32, 1536, P, None, None) == E
+    assert lib.pkv_int4_linear(P + 8, P, P, 1, 32, 1024, P, None, None) == E
+    assert lib.pkv_int4_linear(P, P, P, 16, 8192, 8192, P, P + 4, None) == E
+    # workspace: none up to 8 tokens or when the row blocks fill the chip; above,
+    # one fp32 partial per input slice (8192 rows: 64 blocks of 128, 4 slices)
+    ws = lib.pkv_int4_linear_workspace
+    assert ws(8, 8192, 8192) == 0
+    assert ws(16, 8192, 8192) == 4 * 16 * 8192 * 4
+    assert ws(64, 8192, 8192) == 4 * 64 * 8192 * 4
+    assert ws(64, 28672, 8192) == 0
+    assert ws(9, 128, 2048) == 8 * 9 * 128 * 4
+    assert ws(33, 96, 2048) == 0          # rows not a multiple of 128: no split
+    assert ws(0, 8192, 8192) == E and ws(65, 8192, 8192) == E
 
 
 def test_binding_refuses_host_tensors():

@@ -15,12 +15,17 @@ pytestmark = pytest.mark.gpu
 dev = "cuda"
 
 
-def _gpu(lay, codes=None, scales=None):
+def _gpu(lay, codes=None, scales=None, workspace=True):
     x = lay.x(dev)
     w = lay.codes(dev) if codes is None else codes.to(dev)
     s = lay.scales(dev) if scales is None else scales.to(dev)
     y = torch.full((lay.batch, lay.n), float("nan"), dtype=torch.bfloat16, device=dev)
-    pkv.pkv_int4_linear(x, w, s, y)
+    ws = None
+    need = pkv.pkv_int4_linear_workspace(lay.batch, lay.n, lay.k)
+    if workspace and need:
+        # stale partials from an earlier use must not leak into y
+        ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=dev)
+    pkv.pkv_int4_linear(x, w, s, y, ws)
     torch.cuda.synchronize()
     return y.float().cpu().numpy()
 
@@ -43,7 +48,44 @@ def test_small_layers_every_output(batch, n, k):
     assert_close(y, _ref(lay, np.arange(n)), f"{lay.name}")
 
 
-@pytest.mark.parametrize("batch", [1, 8, 64])
+@pytest.mark.parametrize("batch", [9, 16, 17, 33, 64])
+@pytest.mark.parametrize("n,k", [(128, 2048), (256, 1024), (384, 4096)])
+@pytest.mark.parametrize("workspace", [True, False])
+def test_split_inputs_every_output(batch, n, k, workspace):
+    """Above 8 tokens with rows in blocks of 128: inputs split over 4 or 8
+    workgroups per block (1, 2 or 8 tiles each) through the workspace, and
+    the same calls without one (the register kernel)."""
+    lay = W.int4_custom(f"i4s_{n}_{k}_{batch}", 70 + batch, n, k, batch)
+    y = _gpu(lay, workspace=workspace)
+    assert_close(y, _ref(lay, np.arange(n)), f"{lay.name} workspace={workspace}")
+
+
+def test_workspace_reused_across_calls_and_shapes():
+    """One workspace through successive calls of different batches and
+    shapes: nothing carries over from one call to the next."""
+    ws = pkv.int4_workspace(64, 384, 4096, dev)
+    for i, (n, k, batch) in enumerate([(384, 4096, 64), (128, 2048, 9), (384, 4096, 33),
+                                       (256, 1024, 64), (384, 4096, 64)]):
+        lay = W.int4_custom(f"i4r_{i}", 110 + i, n, k, batch)
+        y = torch.full((batch, n), float("nan"), dtype=torch.bfloat16, device=dev)
+        pkv.pkv_int4_linear(lay.x(dev), lay.codes(dev), lay.scales(dev), y, ws)
+        torch.cuda.synchronize()
+        assert_close(y.float().cpu().numpy(), _ref(lay, np.arange(n)), f"call {i} {lay.name}")
+
+
+@pytest.mark.parametrize("batch", [12, 64])
+def test_split_kernel_unsplit_rows_sampled(batch):
+    """24576 rows fill the chip: one input slice, y written directly, no
+    workspace wanted. Every token of 40 sampled rows."""
+    lay = W.int4_custom(f"i4u_{batch}", 90 + batch, 24576, 1024, batch)
+    assert pkv.pkv_int4_linear_workspace(batch, 24576, 1024) == 0
+    y = _gpu(lay)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 127, 128, 24575], rng.integers(0, lay.n, 36)]))
+    assert_close(y[:, rows], _ref(lay, rows), f"{lay.name} sampled rows")
+
+
+@pytest.mark.parametrize("batch", [1, 8, 16, 64])
 def test_full_size_sampled_rows(batch):
     """The benchmark's 8192 x 8192 layer: every token of 48 sampled rows
     (first and last rows of workgroups, random others)."""
