@@ -69,6 +69,17 @@ def test_sweep_b64_full_size_sampled():
     _check_requests(st, [0, 31, 63], kv_heads=[3])
 
 
+def test_short_splits_on_long_ragged_requests():
+    """Splits of 128 tokens on 8 long requests (up to 128 partials each for
+    the combine): ragged lengths, one request shorter than a split; every
+    request, two kv heads."""
+    lens = [16384, 16307, 16000, 15999, 130, 16384, 9000, 16383]
+    w = W.custom("units2", 77, lens, hq=64, hkv=8, dk=128, dv=128, page=16, split=128)
+    st = State(w, "fp8")
+    assert st.step.split_tokens == 128
+    _check_requests(st, list(range(8)), kv_heads=[0, 7])
+
+
 def test_long_context_split256_sampled():
     st = State(W.long_context(), "fp8")
     assert st.step.split_tokens == 256 and st.step.max_splits == 512
