@@ -244,7 +244,8 @@ def time_drafts(run, T: int, steps: int, warmup: int, read, dec_ms: float):
     q = torch.randn((w.batch, T, w.num_q_heads, w.head_dim_k), generator=g, device="cuda")
     q = q.to(torch.bfloat16)
     L = s.max_seq_len
-    split = s.split_tokens
+    # the drafts kernel takes up to 64 pages per unit
+    split = min(s.split_tokens, 64 * w.page_size)
     n_split = -(-L // split)
     o_part = torch.empty((w.batch, T * w.num_q_heads, n_split, w.head_dim_v),
                          dtype=torch.float32, device="cuda")
@@ -279,7 +280,8 @@ def time_drafts(run, T: int, steps: int, warmup: int, read, dec_ms: float):
     tokens = int(w.seq_lens[read].sum()) if read is not None else w.total_tokens
     flop = 2 * T * w.num_q_heads * (w.head_dim_k + w.head_dim_v) * tokens
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"q_len": T, "decode_ms": round(ms, 5), "eager_ms_per_step": round((t1 - t0) * 1e3 / steps, 5),
+    return {"q_len": T, "split_tokens": split, "decode_ms": round(ms, 5),
+            "eager_ms_per_step": round((t1 - t0) * 1e3 / steps, 5),
             "kv_gbs": round(gbs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
             "vs_q_len_single_token_decodes": round(T * dec_ms / ms, 3),

@@ -61,14 +61,24 @@ __device__ __forceinline__ uint32_t vswz(uint32_t t) {
   return (((t >> 1) & 1u) << 1) | (((t >> 3) & 1u) << 2);
 }
 
-__global__ void __launch_bounds__(64) decode_drafts_kernel(DecodeParams p, int row_groups) {
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kSlots * kTileBytes];
-  __shared__ float rowbuf[2][32];
-  const int lane = threadIdx.x;
+// W waves per workgroup, one group of 32 query rows each, share every tile:
+// each wave issues 8 / W of the tile's loads, one barrier per tile makes the
+// whole tile visible and frees the slot two tiles ahead (three slots). With
+// W = 1 the wave runs its own two-slot ring without barriers.
+template <int W>
+__global__ void __launch_bounds__(64 * W) decode_drafts_kernel(DecodeParams p, int row_groups) {
+  constexpr int kRing = W == 1 ? kSlots : 3;
+  constexpr int kMine = 8 / W;  // loads per tile issued by each wave
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kTileBytes];
+  __shared__ float rowbufs[W][2][32];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  float (*rowbuf)[32] = rowbufs[wv];
   const int col = lane & 31, hl = lane >> 5;
-  const int rg = static_cast<int>(blockIdx.x) % row_groups;
+  const int parts = (row_groups + W - 1) / W;
+  const int rg = (static_cast<int>(blockIdx.x) % parts) * W + wv;
   int b, g, c, L;
-  if (!pkv::find_unit(p, static_cast<int>(blockIdx.x) / row_groups, b, g, c, L)) return;
+  if (!pkv::find_unit(p, static_cast<int>(blockIdx.x) / parts, b, g, c, L)) return;
   const int G = p.num_q_heads / p.num_kv_heads;
   const int T = p.q_len;
   const int rows = T * G;
@@ -78,9 +88,10 @@ __global__ void __launch_bounds__(64) decode_drafts_kernel(DecodeParams p, int r
   const int P = p.page_size;
   const int log2P = P == 16 ? 4 : (P == 32 ? 5 : 6);
 
-  // this lane's query row (S^T column): position j, head g*G + hh
+  // this lane's query row (S^T column): position j, head g*G + hh (a wave
+  // past the last row group only helps with the loads)
   const int r_mine = 32 * rg + col;
-  const bool row_ok = r_mine < rows;
+  const bool row_ok = rg < row_groups && r_mine < rows;
   const int j_mine = row_ok ? r_mine / G : 0;
   // tokens this row may see inside the unit: [t_begin, lim)
   const int lim = row_ok ? min(t_end, L - T + j_mine + 1) : t_begin;
@@ -140,17 +151,21 @@ __global__ void __launch_bounds__(64) decode_drafts_kernel(DecodeParams p, int r
     return off + static_cast<uint32_t>(((gg << 4) & (P - 1)) * kD);
   };
   // 8 loads per tile, always: a 16-token group past the unit's end loads the
-  // tile's first group again (its rows are masked and their V zeroed)
+  // tile's first group again (its rows are masked and their V zeroed). Load
+  // j = 4 x + kind: group x of the tile, kind 0 / 1 the K rows 0..7 / 8..15,
+  // 2 / 3 the V rows; wave wv issues j = wv, wv + W, ...
   auto issue = [&](int t) __attribute__((always_inline)) {
-    const uint32_t slot = ring0 + (t % kSlots) * kTileBytes;
+    const uint32_t slot = ring0 + (t % kRing) * kTileBytes;
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
+    for (int i = 0; i < kMine; ++i) {
+      const int j = wv + W * i;
+      const int x = j >> 2, kind = j & 3;
       const int gg = (t_begin + kTile * t + 16 * x < t_end) ? 2 * t + x : 2 * t;
       const uint64_t off = group_base(gg);
-      dma16(slot + 2048 * x, koff0, kpool + off);
-      dma16(slot + 2048 * x + 1024, koff1, kpool + off);
-      dma16(slot + kHalf + 2048 * x, voff0, vpool + off);
-      dma16(slot + kHalf + 2048 * x + 1024, voff1, vpool + off);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          slot + (kind >= 2 ? kHalf : 0) + 2048 * x + 1024 * (kind & 1));
+      const uint32_t src = kind == 0 ? koff0 : (kind == 1 ? koff1 : (kind == 2 ? voff0 : voff1));
+      dma16(dst, src, (kind < 2 ? kpool : vpool) + off);
     }
   };
 
@@ -184,16 +199,28 @@ __global__ void __launch_bounds__(64) decode_drafts_kernel(DecodeParams p, int r
   float l = 0.0f;     // this lane's part of row col's denominator
 
 #pragma unroll
-  for (int k = 0; k < kSlots - 1; ++k)
+  for (int k = 0; k < kRing - 1; ++k)
     if (k < n_tiles) issue(k);
   for (int t = 0; t < n_tiles; ++t) {
-    if (t + kSlots - 1 < n_tiles) {
-      issue(t + kSlots - 1);
-      wait_vm<8 * (kSlots - 1)>();
+    if constexpr (W == 1) {
+      if (t + kSlots - 1 < n_tiles) {
+        issue(t + kSlots - 1);
+        wait_vm<8 * (kSlots - 1)>();
+      } else {
+        wait_vm<0>();
+      }
     } else {
-      wait_vm<0>();
+      if (t + 1 < n_tiles) {
+        wait_vm<kMine>();
+      } else {
+        wait_vm<0>();
+      }
+      // every wave's share of tile t has landed, and every wave is done with
+      // tile t - 1, whose slot tile t + 2 takes
+      __syncthreads();
+      if (t + 2 < n_tiles) issue(t + 2);
     }
-    uint8_t* buf = ring + (t % kSlots) * kTileBytes;
+    uint8_t* buf = ring + (t % kRing) * kTileBytes;
     const int tile0 = t_begin + kTile * t;
     // rows past the unit or of a page outside the pool: V to zero (their
     // scores are masked, and 0 * NaN must not reach the accumulators)
@@ -201,12 +228,16 @@ __global__ void __launch_bounds__(64) decode_drafts_kernel(DecodeParams p, int r
     const bool g1_ok = tile0 + 16 < t_end && ((valid >> (((2 * t + 1) << 4) >> log2P)) & 1u) != 0;
     const int nv = min(kTile, t_end - tile0);
     if (!g0_ok || !g1_ok || nv < kTile) {
-      for (int q = lane; q < kTile * (kD / 16); q += 64) {
+      for (int q = static_cast<int>(threadIdx.x); q < kTile * (kD / 16); q += 64 * W) {
         const int row = q >> 3;
         const bool keep = row < nv && (row < 16 ? g0_ok : g1_ok);
         if (!keep) *reinterpret_cast<uint4*>(buf + kHalf + 16 * q) = make_uint4(0u, 0u, 0u, 0u);
       }
-      __builtin_amdgcn_wave_barrier();
+      if constexpr (W == 1) {
+        __builtin_amdgcn_wave_barrier();
+      } else {
+        __syncthreads();  // the same condition in every wave of the unit
+      }
     }
 
     // ---- S^T = K Q^T for the tile
@@ -303,12 +334,21 @@ bool drafts_path_supported(int dk, int dv, bool latent, bool e4m3) {
   return e4m3 && !latent && dk == kD && dv == kD;
 }
 
+template <int W>
+int launch_w(const DecodeParams& p, int64_t units, int row_groups, hipStream_t stream) {
+  const int64_t blocks = units * ((row_groups + W - 1) / W);
+  if (blocks > 0x7FFFFFFF) return PKV_EUNSUPPORTED;
+  decode_drafts_kernel<W><<<dim3(static_cast<uint32_t>(blocks)), 64 * W, 0, stream>>>(p, row_groups);
+  return pkv::launch_status();
+}
+
 int launch_decode_drafts(const DecodeParams& p, int n_split_blocks, int batch, int row_groups,
                          hipStream_t stream) {
   if (p.split_tokens > kMaxUnitPages * p.page_size) return PKV_EUNSUPPORTED;
-  const int64_t units =
-      static_cast<int64_t>(n_split_blocks) * p.num_kv_heads * batch * row_groups;
-  if (units > 0x7FFFFFFF) return PKV_EUNSUPPORTED;
-  decode_drafts_kernel<<<dim3(static_cast<uint32_t>(units)), 64, 0, stream>>>(p, row_groups);
-  return pkv::launch_status();
+  const int64_t units = static_cast<int64_t>(n_split_blocks) * p.num_kv_heads * batch;
+  // the row groups of a unit share its tiles, up to 8 waves a workgroup
+  if (row_groups == 1) return launch_w<1>(p, units, row_groups, stream);
+  if (row_groups == 2) return launch_w<2>(p, units, row_groups, stream);
+  if (row_groups <= 4) return launch_w<4>(p, units, row_groups, stream);
+  return launch_w<8>(p, units, row_groups, stream);
 }

@@ -7,7 +7,7 @@ namespace pkv {
 
 // Inclusive prefix sum over the wave.
 __device__ __forceinline__ int wave_scan(int x) {
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int y = __shfl_up(x, off);
@@ -25,7 +25,7 @@ __device__ __forceinline__ int wave_scan(int x) {
 // Aborted requests and empty or over-long contexts have no units.
 __device__ __forceinline__ bool find_unit(const DecodeParams& p, int u, int& b_out, int& g_out, int& c_out,
                           int& L_out) {
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int S = p.split_tokens, H = p.num_kv_heads;
   int L = 0;
   auto splits = [&](int j) __attribute__((always_inline)) {
