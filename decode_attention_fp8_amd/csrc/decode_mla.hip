@@ -564,7 +564,6 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
       if (j + kKAhead < 18) kq[j % kKAhead] = k_read(j + kKAhead);
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(cur.x, cur.y), qf[2 * j], st, 0, 0, 0);
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(cur.z, cur.w), qf[2 * j + 1], st, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
     }
     // scores: st[i] is token 32mb + 8(i/4) + 4hh + i%4 of head h_base + col
     float lm = -INFINITY;
@@ -610,7 +609,6 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
         const uint2 cur = vq[nb % kVAhead];
         if (nb + kVAhead < 16) vq[nb % kVAhead] = v_read(nb + kVAhead);
         O[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf, fp8x8_to_bf16(cur.x, cur.y), O[nb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
