@@ -119,3 +119,19 @@ def test_bad_arguments_raise():
     with pytest.raises(pkv.PkvError):
         pkv.pkv_int4_linear(big.x(dev), w, s, torch.empty((65, 32), dtype=torch.bfloat16,
                                                           device=dev))
+
+
+@pytest.mark.parametrize("batch", [2, 20])
+def test_codes_above_4gib_sampled_rows(batch):
+    """A 32768 x 262144 layer holds 4 GiB of codes, past the 32-bit byte
+    offsets of the direct-to-LDS kernels, so the register kernel (64-bit
+    offsets) runs at every batch. Every token of 24 sampled rows."""
+    n, k = 32768, 262144
+    assert n * k // 2 > 0xFFFFFFFF
+    assert pkv.pkv_int4_linear_workspace(batch, n, k) == 0
+    lay = W.int4_custom(f"i4big_{batch}", 130 + batch, n, k, batch)
+    y = _gpu(lay)
+    torch.cuda.empty_cache()
+    rng = np.random.default_rng(13)
+    rows = np.unique(np.concatenate([[0, 31, 16384, n - 1], rng.integers(0, n, 20)]))
+    assert_close(y[:, rows], _ref(lay, rows), f"{lay.name} sampled rows")
