@@ -80,6 +80,20 @@ def test_short_splits_on_long_ragged_requests():
     _check_requests(st, list(range(8)), kv_heads=[0, 7])
 
 
+def test_pages_past_4gib_of_pool():
+    """Four requests' pages scattered over a 600,000-page pool (9.8 GB per
+    pool): about half of them start past 4 GiB, so every page offset takes
+    64 bits. Every request, two kv heads."""
+    w = W.custom("bigpool", 88, [2000, 1500, 777, 3000], hq=64, hkv=8, dk=128, dv=128,
+                 page=16, pool_pages=600000)
+    page_bytes = 8 * 16 * 128
+    assert int(w.block_table.max()) * page_bytes > 2 ** 32
+    st = State(w, "fp8")
+    _check_requests(st, [0, 1, 2, 3], kv_heads=[0, 7])
+    del st
+    torch.cuda.empty_cache()
+
+
 def test_long_context_split256_sampled():
     st = State(W.long_context(), "fp8")
     assert st.step.split_tokens == 256 and st.step.max_splits == 512
