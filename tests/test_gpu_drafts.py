@@ -72,6 +72,15 @@ def test_drafts_row_groups_and_group_sizes(T, hq, hkv):
     _check(w, T, 64)
 
 
+@pytest.mark.parametrize("T,hq,hkv", [(16, 64, 8), (40, 64, 8), (64, 64, 8)])
+def test_drafts_many_row_groups_share_tiles(T, hq, hkv):
+    """4, 10 and 16 row groups of 32 query rows per kv head: one workgroup of
+    4 waves, then two workgroups of 8 (the second with idle waves that still
+    load their share of every tile)."""
+    w = W.custom(f"drm{T}", 95, [300, 129, 77], hq=hq, hkv=hkv, dk=128, dv=128, page=16)
+    _check(w, T, 128)
+
+
 @pytest.mark.parametrize("lens,P,split", [([1, 2, 3, 4], 16, 16), ([33, 31, 32, 47], 16, 32),
                                           ([129, 64, 65], 64, 64), ([4096 + 3], 32, 512)])
 def test_drafts_ragged_lengths_splits_and_short_requests(lens, P, split):
