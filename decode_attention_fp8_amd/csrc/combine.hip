@@ -46,6 +46,20 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   __shared__ float den_s[kP];
   __shared__ float4 acc_s[kP][kC];
 
+  // this thread's first two split rows load now, independent of the max
+  // they are weighted by, so their latency overlaps the max's
+  const int c0 = sg, c1 = sg + kP;
+  float4 v0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), v1 = v0;
+  float l0 = -INFINITY, l1 = -INFINITY;
+  if (c0 < n) {
+    v0 = op[static_cast<int64_t>(c0) * kC + ch];
+    l0 = lse[c0];
+  }
+  if (c1 < n) {
+    v1 = op[static_cast<int64_t>(c1) * kC + ch];
+    l1 = lse[c1];
+  }
+
   float mx = -INFINITY;
   for (int c = t; c < n; c += 256) mx = fmaxf(mx, lse[c]);
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
@@ -57,8 +71,24 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float den = 0.0f;
   if (!empty) {
+    if (c0 < n) {
+      const float w = exp2f((l0 - M) * kLog2e);
+      den += w;
+      acc.x += w * v0.x;
+      acc.y += w * v0.y;
+      acc.z += w * v0.z;
+      acc.w += w * v0.w;
+    }
+    if (c1 < n) {
+      const float w = exp2f((l1 - M) * kLog2e);
+      den += w;
+      acc.x += w * v1.x;
+      acc.y += w * v1.y;
+      acc.z += w * v1.z;
+      acc.w += w * v1.w;
+    }
 #pragma unroll 4
-    for (int c = sg; c < n; c += kP) {
+    for (int c = sg + 2 * kP; c < n; c += kP) {
       const float w = exp2f((lse[c] - M) * kLog2e);
       const float4 v = op[static_cast<int64_t>(c) * kC + ch];
       den += w;
