@@ -33,13 +33,13 @@ MFMA_BF16_PEAK = 2500.0  # TFLOP/s, dense
 # HBM traffic of the decode kernel from rocprofv3 --pmc runs of this same
 # command (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, mean over the
 # dispatches), keyed by (workload, split, sha256 prefix of the kernel source
-# the counters were taken on). A plain 1 GiB device copy reads as 524,300 KiB
+# and every header beside it, as the counters were taken on). A plain 1 GiB device copy reads as 524,300 KiB
 # FETCH_SIZE and 1,048,576 KiB WRITE_SIZE, so FETCH_SIZE counts in units of 2 KiB
 # here and WRITE_SIZE in KiB. Entries stop matching once the kernel changes.
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 TRAFFIC_KIB = {
-    ("sweep_b64", 2048, "decode_gqa_mfma.hip", "e3b96c7b76b468a9"): (1197411.4, 20421.8),
-    ("mla_b64", 4096, "decode_mla.hip", "2764739f88392a1d"): (178399.9, 44200.0),
+    ("sweep_b64", 2048, "decode_gqa_mfma.hip", "3ff62c8502dd9713"): (1196882.7, 20023.1),
+    ("mla_b64", 4096, "decode_mla.hip", "f4fc24c1d6ae8f33"): (178171.6, 44204.1),
 }
 
 
@@ -73,14 +73,23 @@ def parse():
     return ap.parse_args()
 
 
+def kernel_digest(src: str) -> str:
+    """sha256 prefix over a kernel source and the csrc headers (any of which
+    the kernel may include), in a fixed order."""
+    import glob
+    import hashlib
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "decode_attention_fp8_amd", "csrc")
+    h = hashlib.sha256()
+    for path in [os.path.join(d, src)] + sorted(glob.glob(os.path.join(d, "*.h"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(w, split: int):
     """Scaled HBM bytes per decode launch, or None if no counters match."""
-    import hashlib
     src = "decode_mla.hip" if w.latent else "decode_gqa_mfma.hip"
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "decode_attention_fp8_amd",
-                        "csrc", src)
-    with open(path, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()[:16]
+    digest = kernel_digest(src)
     kib = TRAFFIC_KIB.get((w.name, split, src, digest))
     if kib is None:
         return None

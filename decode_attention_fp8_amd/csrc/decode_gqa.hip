@@ -34,8 +34,11 @@
 // (t, t+4) are interleaved with a byte permute so one packed dot product
 // takes p and v of both tokens. p reaches these lanes through 256 bytes of
 // LDS.
+#include <type_traits>
+
 #include "common.h"
 #include "decode_params.h"
+#include "unit_order.h"
 
 namespace {
 
@@ -72,12 +75,20 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // 16 bytes per lane from base + voff into LDS at lds + 16 * lane (the
 // instruction's immediate offset would move both addresses, so it stays 0).
-// m0 is not otherwise used by this kernel.
+// m0 is not otherwise used by this kernel. kNt selects the non-temporal
+// form, for launches whose cache would not stay resident.
+template <bool kNt>
 __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const uint8_t* base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds), "v"(voff), "s"(base)
-               : "memory");
+  if constexpr (kNt)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :
+                 : "s"(lds), "v"(voff), "s"(base)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds), "v"(voff), "s"(base)
+                 : "memory");
 }
 
 template <int N>
@@ -177,6 +188,10 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) de
   const int n_unit_pages = (t_end - t_begin + P - 1) >> log2P;
   int pg = -1;
   if (lane < n_unit_pages) pg = bt[first_page + lane];
+  // the launch's footprint; up to 64 requests its loads join the ones above
+  const int64_t tokens = p.batch <= 64 ? pkv::wave_sum(pkv::footprint_len(pkv::unit_len(p, lane)))
+                                       : pkv::launch_tokens(p);
+  const bool stream = pkv::stream_cache(tokens * p.num_kv_heads * 2 * kRow);
   if (lane < kG) lds.m[lane] = kMInit;
   // Every compiler-issued load must be complete before the first DMA, or its
   // own wait for them would also wait for the ring.
@@ -186,7 +201,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) de
     for (int k = 0; k < 16; k += 8)
       asm volatile("" : : "v"(qr[h][k]), "v"(qr[h][k + 1]), "v"(qr[h][k + 2]), "v"(qr[h][k + 3]),
                    "v"(qr[h][k + 4]), "v"(qr[h][k + 5]), "v"(qr[h][k + 6]), "v"(qr[h][k + 7]));
-  asm volatile("" : : "v"(qk_scale), "v"(o_scale), "v"(pg));
+  asm volatile("" : : "v"(qk_scale), "v"(o_scale), "v"(pg), "s"(static_cast<int>(stream)));
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" : : : "memory");
   const bool pg_ok = pg >= 0 && pg < p.num_pages;
   const uint64_t valid = __ballot(pg_ok);
@@ -230,21 +245,29 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) de
     const uint8_t* kb = kpool + off + row_off;
     const uint8_t* vb = vpool + off + row_off;
     const uint32_t slot = ring0 + (gi % R::kSlots) * R::kGroupBytes;
-    if constexpr (kE4M3) {
-      dma16(slot, koff0, kb);
-      dma16(slot + 1024, koff0, kb + 1024);
-      dma16(slot + 2048, voff, vb);
-      dma16(slot + 3072, voff, vb + 1024);
-    } else {
-      dma16(slot, koff0, kb);
-      dma16(slot + 1024, koff1, kb);
-      dma16(slot + 2048, koff0, kb + 2048);
-      dma16(slot + 3072, koff1, kb + 2048);
-      dma16(slot + 4096, voff, vb);
-      dma16(slot + 5120, voff, vb + 1024);
-      dma16(slot + 6144, voff, vb + 2048);
-      dma16(slot + 7168, voff, vb + 3072);
-    }
+    // one branch per group selects the load form for all of its loads
+    auto dmas = [&](auto nt) __attribute__((always_inline)) {
+      constexpr bool kNt = decltype(nt)::value;
+      if constexpr (kE4M3) {
+        dma16<kNt>(slot, koff0, kb);
+        dma16<kNt>(slot + 1024, koff0, kb + 1024);
+        dma16<kNt>(slot + 2048, voff, vb);
+        dma16<kNt>(slot + 3072, voff, vb + 1024);
+      } else {
+        dma16<kNt>(slot, koff0, kb);
+        dma16<kNt>(slot + 1024, koff1, kb);
+        dma16<kNt>(slot + 2048, koff0, kb + 2048);
+        dma16<kNt>(slot + 3072, koff1, kb + 2048);
+        dma16<kNt>(slot + 4096, voff, vb);
+        dma16<kNt>(slot + 5120, voff, vb + 1024);
+        dma16<kNt>(slot + 6144, voff, vb + 2048);
+        dma16<kNt>(slot + 7168, voff, vb + 3072);
+      }
+    };
+    if (stream)
+      dmas(std::true_type{});
+    else
+      dmas(std::false_type{});
   };
 
   // V rows tg + 4j, dims [8dg, 8dg+8) of group gi; rows past the context

@@ -76,9 +76,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // 16 bytes per lane from base + voff into LDS at lds + 16 * lane (m0 is not
 // otherwise used by this kernel; the immediate offset stays 0 because it
-// would move both addresses).
+// would move both addresses). Marked non-temporal: a step reads each cache
+// byte once, so its lines are not kept for reuse.
 __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const uint8_t* base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
                :
                : "s"(lds), "v"(voff), "s"(base)
                : "memory");

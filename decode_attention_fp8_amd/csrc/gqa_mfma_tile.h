@@ -100,13 +100,22 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
   return o;
 }
 
-// DMA of one 16-token group (K and V, 2 KB each) into half x of a slot.
+// DMA of one 16-token group (K and V, 2 KB each) into half x of a slot;
+// `stream` (wave-uniform) selects the non-temporal form.
 __device__ __forceinline__ void dma_group(uint32_t slot, int x, const LaneOffsets& o,
-                                          const uint8_t* kgroup, const uint8_t* vgroup) {
-  dma16(slot + 2048 * x, o.kdma0, kgroup);
-  dma16(slot + 2048 * x + 1024, o.kdma1, kgroup);
-  dma16(slot + kHalf + 2048 * x, o.vdma[x][0], vgroup);
-  dma16(slot + kHalf + 2048 * x + 1024, o.vdma[x][1], vgroup);
+                                          const uint8_t* kgroup, const uint8_t* vgroup,
+                                          bool stream) {
+  if (stream) {
+    dma16_stream(slot + 2048 * x, o.kdma0, kgroup);
+    dma16_stream(slot + 2048 * x + 1024, o.kdma1, kgroup);
+    dma16_stream(slot + kHalf + 2048 * x, o.vdma[x][0], vgroup);
+    dma16_stream(slot + kHalf + 2048 * x + 1024, o.vdma[x][1], vgroup);
+  } else {
+    dma16(slot + 2048 * x, o.kdma0, kgroup);
+    dma16(slot + 2048 * x + 1024, o.kdma1, kgroup);
+    dma16(slot + kHalf + 2048 * x, o.vdma[x][0], vgroup);
+    dma16(slot + kHalf + 2048 * x + 1024, o.vdma[x][1], vgroup);
+  }
 }
 
 struct Acc {

@@ -192,7 +192,7 @@ __global__ void __launch_bounds__(64 * kWaves)
   auto issue = [&](int t) __attribute__((always_inline)) {
     const uint32_t slot = base + (t % kSlots) * kSlot;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(slot + 1024 * j, cvoff[j] + 128 * t, w);
+    for (int j = 0; j < 4; ++j) dma16_stream(slot + 1024 * j, cvoff[j] + 128 * t, w);
     dma4(slot + kCodeB, svoff + 4 * N * t, reinterpret_cast<const uint8_t*>(scales));
 #pragma unroll
     for (int j = 0; j < XB; ++j)
@@ -369,8 +369,15 @@ __global__ void __launch_bounds__(64 * kWaves)
 
   auto issue = [&](int t) __attribute__((always_inline)) {
     const uint32_t cs = __builtin_amdgcn_readfirstlane(cbase + (t % kSlots) * kCSlot);
-    dma16(cs, cvoff[0] + 128 * t, w);
-    dma16(cs + 1024, cvoff[1] + 128 * t, w);
+    // codes are read once; the non-temporal hint pays with one token tile
+    // and was measured slower with two or more
+    if constexpr (TT == 1) {
+      dma16_stream(cs, cvoff[0] + 128 * t, w);
+      dma16_stream(cs + 1024, cvoff[1] + 128 * t, w);
+    } else {
+      dma16(cs, cvoff[0] + 128 * t, w);
+      dma16(cs + 1024, cvoff[1] + 128 * t, w);
+    }
     dma4(cs + kCodeB, svoff + 4 * N * t, reinterpret_cast<const uint8_t*>(scales));
     const uint32_t xs = __builtin_amdgcn_readfirstlane(xbase + (t % kSlots) * kXB);
 #pragma unroll

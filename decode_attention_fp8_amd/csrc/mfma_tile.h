@@ -37,6 +37,23 @@ __device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, const uint8_t*
                : "memory");
 }
 
+// The same two loads marked non-temporal, for bytes a launch reads once (the
+// KV stream): the line is not kept in the caches for reuse. On random 2 KB
+// blocks this lifts the read rate from about 6.0 to about 6.7 TB/s.
+__device__ __forceinline__ void dma16_stream(uint32_t lds, uint32_t voff, const uint8_t* base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+               :
+               : "s"(lds), "v"(voff), "s"(base)
+               : "memory");
+}
+
+__device__ __forceinline__ void dma4_stream(uint32_t lds, uint32_t voff, const uint8_t* base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2 nt"
+               :
+               : "s"(lds), "v"(voff), "s"(base)
+               : "memory");
+}
+
 // wait until at most N of this wave's vector memory loads are outstanding
 template <int N>
 __device__ __forceinline__ void wait_vm() {

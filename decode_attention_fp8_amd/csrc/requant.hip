@@ -40,9 +40,18 @@ __global__ void __launch_bounds__(256) requant_kernel(RequantArgs k, RequantArgs
   const int64_t page_vals = static_cast<int64_t>(heads) * page_size * a.row;
   const uint4* src = reinterpret_cast<const uint4*>(a.src + sp * page_vals);
   uint4* dst = reinterpret_cast<uint4*>(a.dst + dp * page_vals);
+  // both pages are touched once: non-temporal loads and stores keep them out
+  // of the caches' reuse
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
+  u32x4* dst4 = reinterpret_cast<u32x4*>(dst);
   for (int c = threadIdx.x; c < total; c += blockDim.x) {
     const int h = c / per_head;
-    dst[c] = pkv::encode16(src[2 * c], src[2 * c + 1], a.scale[h]);
+    const u32x4 w0 = __builtin_nontemporal_load(src4 + 2 * c);
+    const u32x4 w1 = __builtin_nontemporal_load(src4 + 2 * c + 1);
+    const uint4 e = pkv::encode16(make_uint4(w0.x, w0.y, w0.z, w0.w),
+                                  make_uint4(w1.x, w1.y, w1.z, w1.w), a.scale[h]);
+    __builtin_nontemporal_store(u32x4{e.x, e.y, e.z, e.w}, dst4 + c);
   }
   if (blockIdx.y == 0 && threadIdx.x == 0 && new_tags) dst_tags[dp] = new_tags[i];
 }

@@ -129,3 +129,12 @@ def test_drafts_score_jump_rescales():
     v_hat = (e4m3.DECODE[vc] * np.float64(vs))[:, None, :]
     o_ref, _ = attention.attend_drafts(qb[0].double().numpy(), k_hat, v_hat, st.w.sm_scale)
     assert_close(out[0], o_ref, "drafts score jump")
+
+
+def test_drafts_footprint_above_cache_sampled():
+    """The batch-16 sweep cache (285,175 tokens, 584 MB of codes) is read with
+    non-temporal loads, the small caches above with plain ones: three
+    requests of a q_len-4 launch."""
+    w = W.sweep(16)
+    assert w.total_tokens * w.num_kv_heads * 2 * 128 > 384 << 20
+    _check(w, 4, 1024, seed=5, requests=[0, 9, 15])

@@ -96,3 +96,11 @@ def test_row_scales_unsupported_paths_refuse():
     with pytest.raises(pkv.PkvError):
         pkv.pkv_decode_attn_drafts(st2.cache, q, st2.block_table, st2.seq_lens, 100, None,
                                    w2.sm_scale, 128, o_part, lse)
+
+
+def test_decode_sweep_b16_row_scales():
+    """Codes and row scales of the batch-16 sweep (about 600 MB) are read
+    with non-temporal loads; the batch-8 case above reads plainly."""
+    w = W.sweep(16)
+    assert w.total_tokens * w.num_kv_heads * (2 * 128 + 8) > 384 << 20
+    _decode_check(w, None, requests=[0, 15])
