@@ -24,7 +24,8 @@ Modules:
   handoff  prefill -> decode page handoff: BF16 pages re-encoded, tags set
   int4     INT4 weight-only linear layer of the decode phase
 
-Parity status: every function is pinned by tests/test_oracle_*.py; the only
+Parity status: every function is pinned by tests/test_oracle_*.py (the step
+composition by hand-worked steps in tests/golden/step_hand_worked.json); the only
 unpinned quantity is the accuracy of FP8 against BF16 attention (the pages'
 evidence for it is model-level benchmark scores), which is reported, never
 asserted.

@@ -27,8 +27,18 @@ def scale_from_amax(amax: float) -> np.float32:
 
 
 def quotient(x, s) -> np.ndarray:
-    """fl32(x / s) for float32-representable x (bf16 inputs) and float32 s."""
-    return (np.asarray(x, dtype=np.float64) / np.float64(np.float32(s))).astype(np.float32)
+    """fl32(x / s) for float32-representable x (bf16 inputs) and float32 s.
+
+    A NaN that the division itself creates from non-NaN operands (an infinity
+    over an infinite scale) is taken as the positive default NaN, as the GPU's
+    arithmetic units produce it; an input NaN keeps its sign."""
+    xa = np.asarray(x, dtype=np.float64)
+    with np.errstate(invalid="ignore"):
+        q = (xa / np.float64(np.float32(s))).astype(np.float32)
+    made = np.isnan(q) & ~np.isnan(xa)
+    if np.any(made):
+        q = np.where(made, np.float32(np.nan), q)
+    return q
 
 
 def quantize(x, s) -> np.ndarray:
@@ -47,7 +57,17 @@ def dequantize(codes, s) -> np.ndarray:
 # The pages give no scale granularity. The finer reading taken here: every
 # appended row (one token of one kv head, K and V separately) gets its own
 # scale from its own largest magnitude, by the same rule as the static
-# scales, and is encoded under it.
+# scales, and is encoded under it. A NaN in a row is no magnitude: it takes
+# no part in the row's largest magnitude (an all-NaN row counts as all
+# zero, scale 1) and is itself encoded as a NaN code, so it spoils no other
+# value of its row.
+
+
+def row_amax(row) -> float:
+    """Largest |value| of a row, NaNs left out (0 for an empty or all-NaN row)."""
+    a = np.abs(np.asarray(row, dtype=np.float64))
+    a = a[~np.isnan(a)]
+    return float(a.max()) if a.size else 0.0
 
 
 def quantize_rows(x):
@@ -58,7 +78,7 @@ def quantize_rows(x):
     codes = np.empty(flat.shape, dtype=np.uint8)
     scales = np.empty(flat.shape[0], dtype=np.float32)
     for i, row in enumerate(flat):
-        s = scale_from_amax(np.abs(row).max() if row.size else 0.0)
+        s = scale_from_amax(row_amax(row))
         scales[i] = s
         codes[i] = quantize(row, s)
     return codes.reshape(a.shape), scales.reshape(a.shape[:-1])

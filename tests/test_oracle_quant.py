@@ -120,3 +120,34 @@ def test_row_scale_zero_row_and_exact_grid_rows():
     row = vals * 2.0 ** -7
     c, s = quant.quantize_rows(row[None, :])
     assert np.array_equal(quant.dequantize_rows(c, s)[0], row)
+
+
+def test_row_scale_leaves_nan_out_of_the_row_amax():
+    """A NaN takes no part in its row's largest magnitude and becomes a NaN
+    code with its sign; the rest of the row is encoded as if it were absent.
+    An all-NaN row gets scale 1 (no magnitude, as an all-zero row)."""
+    row = np.array([np.nan, 224.0, -112.0, 1.0, -np.nan, 0.0], dtype=np.float64)
+    c, s = quant.quantize_rows(row[None, :])
+    assert s[0] == np.float32(0.5)  # 224 / 448
+    assert c[0, 0] == 0x7F and c[0, 4] == 0xFF
+    assert c[0, 1] == 0x7E and c[0, 2] == 0xF6 and c[0, 3] == 0x40 and c[0, 5] == 0x00
+    c2, s2 = quant.quantize_rows(np.full((1, 4), np.nan))
+    assert s2[0] == 1.0 and np.all(c2 == 0x7F)
+    # an infinity is a magnitude: scale inf, finite values encode as zero codes and
+    # inf / inf is the positive default NaN
+    c3, s3 = quant.quantize_rows(np.array([[np.inf, 3.0, -3.0]]))
+    assert np.isinf(s3[0]) and c3[0, 0] == 0x7F and c3[0, 1] == 0x00 and c3[0, 2] == 0x80
+
+
+def test_scale_from_amax_subnormal_results():
+    """Scales that land among float32 subnormals (multiples of 2^-149) still
+    round to nearest: the smallest bf16 magnitude 2^-133 gives
+    2^-133 / 448 = 2^-139 / 7 = (1024 / 7) * 2^-149 = 146.29 * 2^-149, so
+    s = 146 * 2^-149; and the amax value itself then sits at
+    2^16 / 146 = 448.9 scale units, above 448, so it saturates to 0x7E."""
+    tiny = 2.0 ** -133
+    s = quant.scale_from_amax(tiny)
+    assert s == np.float32(146 * 2.0 ** -149)
+    assert quant.quantize(np.array([tiny, -tiny]), s).tolist() == [0x7E, 0xFE]
+    # a float32-normal but small amax: 2^-100 / 448 = 2^-106 / 7, normal
+    assert quant.scale_from_amax(2.0 ** -100) == _round_f32(Fraction(2) ** -100 / 448)

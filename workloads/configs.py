@@ -134,6 +134,17 @@ class Workload:
         return hashgen.bf16_block(self._keys(S_Q), n, device).view(
             self.batch, self.num_q_heads, self.head_dim_k)
 
+    # The same values as raw bf16 bit patterns in NumPy uint16 arrays (for
+    # consumers that take no torch tensors).
+    def k_bits(self, b: int, heads=None, tokens=None) -> np.ndarray:
+        return _bits(self.k_values(b, heads=heads, tokens=tokens))
+
+    def v_bits(self, b: int, heads=None, tokens=None) -> np.ndarray:
+        return _bits(self.v_values(b, heads=heads, tokens=tokens))
+
+    def q_bits(self) -> np.ndarray:
+        return _bits(self.q_values())
+
     # ---------------------------------------------------------------- amax
     def amax(self, which: str, head: int | None = None) -> float:
         """Exact max |x| over every K (or V) value of every request, or of one
@@ -158,6 +169,11 @@ class Workload:
 # ----------------------------------------------------------------------------
 # construction helpers
 # ----------------------------------------------------------------------------
+def _bits(t: torch.Tensor) -> np.ndarray:
+    """uint16 bit patterns of a CPU bf16 tensor."""
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
 def _rng(seed: int, stream: int) -> np.random.Generator:
     return np.random.default_rng([seed, stream, 7919])
 
