@@ -175,7 +175,8 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
     tile_math<kRowScales>(buf, lo, qf, qk_scale, g0_ok, g1_ok, min(kTile, t_end - tile0),
                           rowbuf, a, reinterpret_cast<const float*>(buf + kTileBytes));
   }
-  finish(p, b, g, c, G, o_scale, rowbuf, a);
+  // scales set at append: O is relative to the unit's V reference scale
+  finish(p, b, g, c, G, kRowScales ? a.vref : o_scale, rowbuf, a);
 }
 
 }  // namespace

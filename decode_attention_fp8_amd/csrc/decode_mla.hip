@@ -574,8 +574,11 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
       st[i] = (32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3) < nv) ? v : -INFINITY;
       lm = fmaxf(lm, st[i]);
     }
+    // the lanes col and col + 32 hold the two token halves of one head and
+    // feed the same A row of PV: both take the head's maximum, so their m
+    // (and the numerators summed into one l) always agree
+    lm = fmaxf(lm, __shfl_xor(lm, 32));
     if (m == kMInit) {  // first scores of the unit set the reference max
-      lm = fmaxf(lm, __shfl_xor(lm, 32));
       m = lm > -INFINITY ? lm : kMInit;
     } else if (lm > m + kWideTau) {
       jump = true;

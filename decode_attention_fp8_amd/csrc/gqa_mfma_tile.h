@@ -122,6 +122,10 @@ struct Acc {
   floatx4_t O[8];  // head 4 qg + i, dim 16 nb + col
   float m;         // reference max of head col (its four lanes agree)
   float l;         // this lane's part of head col's denominator
+  // scales set at append: O holds sum p * code * (v_scale / vref), vref a
+  // power of two at or above every V row scale seen so far (0 = none yet),
+  // so that f16 numerators p * v_scale / vref stay at most 2^kTau
+  float vref;
 };
 
 __device__ __forceinline__ void acc_init(Acc& a) {
@@ -131,6 +135,13 @@ __device__ __forceinline__ void acc_init(Acc& a) {
     for (int i = 0; i < 4; ++i) a.O[nb][i] = 0.0f;
   a.m = kMUnset;
   a.l = 0.0f;
+  a.vref = 0.0f;
+}
+
+// Smallest power of two at or above a positive float (2^-126 for any
+// subnormal; infinity above 2^127).
+__device__ __forceinline__ float pow2_at_or_above(float x) {
+  return __uint_as_float((__float_as_uint(x) + 0x7FFFFFu) & 0xFF800000u);
 }
 
 // QK^T, softmax and PV of the tile in buf. Group x of the tile holds valid
@@ -138,8 +149,9 @@ __device__ __forceinline__ void acc_init(Acc& a) {
 // first nv are in the unit. rowbuf: 16 floats of LDS. kRowScales: the tile's
 // rows carry their own scales (set at append), in LDS at rs[t] (K) and
 // rs[64 + t] (V) for tile row t; a score is multiplied by its row's K scale
-// and a numerator by its row's V scale before PV (the denominator takes the
-// unscaled numerator), masked rows contributing nothing.
+// and a numerator by its row's V scale over the unit's V reference a.vref
+// before PV (the denominator takes the unscaled numerator), masked rows
+// contributing nothing.
 template <bool kRowScales>
 __device__ __forceinline__ void tile_math(uint8_t* buf, const LaneOffsets& o,
                                           const bf16x8_t (&qf)[4], float qk_scale, bool g0_ok,
@@ -223,6 +235,35 @@ __device__ __forceinline__ void tile_math(uint8_t* buf, const LaneOffsets& o,
     __builtin_amdgcn_wave_barrier();
   }
 
+  float vinv = 1.0f;
+  if constexpr (kRowScales) {
+    // V row scales relative to vref: a tile with a larger scale (always the
+    // unit's first valid tile) raises vref and rescales O in a uniform
+    // branch. A masked row's scale may be unwritten and takes no part.
+    bool up = false;
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) up |= s[x][i] != -INFINITY && (&vs[x].x)[i] > a.vref;
+    if (__any(up)) {
+      float vm = 0.0f;
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (s[x][i] != -INFINITY) vm = fmaxf(vm, (&vs[x].x)[i]);
+      vm = fmaxf(vm, __shfl_xor(vm, 16));
+      vm = fmaxf(vm, __shfl_xor(vm, 32));
+      const float nref = pow2_at_or_above(vm);
+      const float f = a.vref / nref;  // 0 before the first valid tile: O is 0
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) a.O[nb] *= f;
+      a.vref = nref;
+    }
+    // 1 / vref, exact for a power of two in [2^-126, 2^126]
+    vinv = __uint_as_float(0x7F000000u - __float_as_uint(a.vref));
+  }
+
   // ---- O += P V over the 32 tokens, 8 blocks of 16 dims
   f16x8_t pf;
 #pragma unroll
@@ -233,7 +274,8 @@ __device__ __forceinline__ void tile_math(uint8_t* buf, const LaneOffsets& o,
       a.l += pr;
       if constexpr (kRowScales) {
         // a masked row's scale may be unwritten: its numerator stays 0
-        pf[4 * x + i] = static_cast<_Float16>(s[x][i] == -INFINITY ? 0.0f : pr * (&vs[x].x)[i]);
+        pf[4 * x + i] = static_cast<_Float16>(
+            s[x][i] == -INFINITY ? 0.0f : pr * ((&vs[x].x)[i] * vinv));
       } else {
         pf[4 * x + i] = static_cast<_Float16>(pr);
       }

@@ -30,14 +30,15 @@ def quotient(x, s) -> np.ndarray:
     """fl32(x / s) for float32-representable x (bf16 inputs) and float32 s.
 
     A NaN that the division itself creates from non-NaN operands (an infinity
-    over an infinite scale) is taken as the positive default NaN, as the GPU's
-    arithmetic units produce it; an input NaN keeps its sign."""
+    over an infinite scale) is taken as the default NaN with the sign bit
+    set, whatever the signs of the operands (the GPU's divide gives it, as
+    does x86 double division); an input NaN keeps its sign."""
     xa = np.asarray(x, dtype=np.float64)
-    with np.errstate(invalid="ignore"):
+    with np.errstate(invalid="ignore", over="ignore"):
         q = (xa / np.float64(np.float32(s))).astype(np.float32)
     made = np.isnan(q) & ~np.isnan(xa)
     if np.any(made):
-        q = np.where(made, np.float32(np.nan), q)
+        q = np.where(made, -np.float32(np.nan), q)
     return q
 
 

@@ -10,16 +10,19 @@ import torch
 import decode_attention_fp8_amd as pkv
 import workloads as W
 from oracle import e4m3, step
-from tests.gpu_state import State, assert_close
+from tests.gpu_state import State, assert_close, assert_lse_close
 
 pytestmark = pytest.mark.gpu
 dev = "cuda"
 
 
 def _check_requests(st, requests, kv_heads=None, kv_dtype=None):
+    """Output rows and lse of the sampled requests and kv heads' query heads
+    against the oracle; aborted requests must give exactly 0 and -inf."""
     w = st.w
     kv_dtype = kv_dtype or st.kv_dtype
     out = st.run().float().cpu().numpy()
+    lse = st.step.lse.cpu().numpy()
     ks, vs = step.scales(w, kv_dtype)
     flags = step.flags(w)
     assert np.array_equal(st.step.abort.cpu().numpy(), flags)
@@ -28,13 +31,34 @@ def _check_requests(st, requests, kv_heads=None, kv_dtype=None):
     hs = np.arange(w.num_kv_heads) if kv_heads is None else np.asarray(kv_heads)
     qh = np.concatenate([np.arange(h * G, (h + 1) * G) for h in hs])
     for b in requests:
-        o_ref, _ = step.request_output(w, b, kv_dtype, ks, vs, bool(flags[b]), hs, q[b])
+        o_ref, lse_ref = step.request_output(w, b, kv_dtype, ks, vs, bool(flags[b]), hs, q[b])
         got = out[b][qh]
         if flags[b]:
             assert np.all(got == 0.0), f"aborted request {b} must be zero"
+            assert np.all(np.isneginf(lse[b][qh])), f"aborted request {b} lse must be -inf"
         else:
             assert_close(got, o_ref, f"{w.name} {kv_dtype} request {b}")
+            assert_lse_close(lse[b][qh], lse_ref, f"{w.name} {kv_dtype} request {b} lse")
     return out
+
+
+def _zero_query_sentinel(st):
+    """With q = 0 every score is 0: each weight is 1 / L_b, so lse = ln L_b
+    and out = the mean of the request's values. The denominators count
+    tokens exactly, so a tile lost or read twice anywhere in the launch moves
+    lse by about 32 / L_b (2e-3 at 16k tokens), far outside 1e-5."""
+    w = st.w
+    st.q.zero_()
+    st.run()
+    lse = st.step.lse.cpu().numpy().astype(np.float64)
+    flags = step.flags(w)
+    for b in range(w.batch):
+        if flags[b]:
+            assert np.all(np.isneginf(lse[b]))
+        else:
+            err = np.abs(lse[b] - math.log(int(w.seq_lens[b])))
+            assert err.max() <= 1e-5, f"{w.name} request {b}: lse off ln L by {err.max():.2e}"
+    return flags
 
 
 @pytest.mark.parametrize("kv", ["fp8", "bf16"])
@@ -67,6 +91,39 @@ def test_sweep_b8(kv):
 def test_sweep_b64_full_size_sampled():
     st = State(W.sweep(64), "fp8")
     _check_requests(st, [0, 31, 63], kv_heads=[3])
+
+
+@pytest.mark.parametrize("B", [1, 16, 32])
+def test_sweep_other_batches_sampled(B):
+    st = State(W.sweep(B), "fp8")
+    reqs = sorted({0, B // 2, B - 1})
+    _check_requests(st, reqs, kv_heads=[0, 7] if B == 1 else [5])
+
+
+@pytest.mark.parametrize("make", [lambda: W.sweep(64), W.long_context],
+                         ids=["sweep_b64", "long_b4"])
+def test_bf16_cache_at_the_sizes_timed(make):
+    """The bf16-cache comparison runs at the sizes the measurement times."""
+    w = make()
+    st = State(w, "bf16")
+    _check_requests(st, [0, w.batch - 1], kv_heads=[2])
+
+
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+@pytest.mark.parametrize("make", [lambda: W.sweep(64), W.long_context, W.mla],
+                         ids=["sweep_b64", "long_b4", "mla_b64"])
+def test_zero_query_sentinel_full_size(make, kv):
+    """Every (request, head) of the full workload at once: lse must be ln L_b
+    to 1e-5 (and the output the mean value row, checked on one request)."""
+    w = make()
+    st = State(w, kv)
+    flags = _zero_query_sentinel(st)
+    b = int(np.argmin(np.where(flags == 0, w.seq_lens, np.iinfo(np.int32).max)))
+    ks, vs = step.scales(w, kv)
+    _, v = step.request_kv(w, b, kv, ks, vs, heads=[0])
+    mean = v[:, 0, :].mean(axis=0)
+    got = st.step.out[b, :w.group].float().cpu().numpy()
+    assert_close(got, np.broadcast_to(mean, got.shape), f"{w.name} {kv} zero query, request {b}")
 
 
 def test_short_splits_on_long_ragged_requests():
@@ -270,6 +327,48 @@ def test_mla_score_jump_far_above_the_first_tile(kv):
     out = ds.attend(q.to(dev), bt, lens, sm, None).float().cpu().numpy()[0]
     ref, _ = attention.attend(q[0].double().numpy(), k_hat[:, None, :], k_hat[:, None, :dv], sm)
     assert_close(out, ref, f"mla score jump {kv}")
+
+
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+@pytest.mark.parametrize("jumps", [((128 + 5, 7.0),), ((128 + 2, 5.0), (128 + 5, 7.0)),
+                                   ((128 + 1, 7.0), (128 + 6, 5.0)), ((160 + 12, 6.0),)],
+                         ids=["one_token_upper_half", "halves_different_upper_higher",
+                              "halves_different_lower_higher", "one_token_second_block"])
+def test_mla_score_jump_single_tokens(kv, jumps):
+    """Single tokens whose keys align with head 0's query jump far above the
+    first tile's scores. Token t of a 32-token block sits in one of two lane
+    halves by bit 2 of t, so a jump in one half only (and jumps of different
+    size in the two halves of one block) must still give every lane of the
+    head the same reference max."""
+    from oracle import attention
+    hq, dk, dv, P, L = 128, 576, 512, 64, 256
+    rng = np.random.default_rng(19)
+    q = torch.from_numpy(rng.standard_normal((1, hq, dk)).astype(np.float32)).to(torch.bfloat16)
+    sign = np.sign(q[0, 0].float().numpy())
+    sign[sign == 0] = 1
+    vals = rng.standard_normal((L, dk)).astype(np.float32) * 0.01
+    for t, a in jumps:
+        vals[t] = a * sign
+    scale = np.float32(7.0 / 448.0)
+    cache = pkv.allocate_cache(4, 1, P, dk, dv, kv, latent=True, device=dev)
+    if kv == "fp8":
+        codes = e4m3.encode((vals / scale).astype(np.float32))
+        k_hat = e4m3.DECODE[codes] * np.float64(scale)
+        cache.k_pool[:, 0] = torch.from_numpy(codes.reshape(4, P, dk)).to(dev)
+        cache.k_scale.fill_(float(scale))
+        cache.v_scale = cache.k_scale
+    else:
+        kb = torch.from_numpy(vals).to(torch.bfloat16)
+        k_hat = kb.double().numpy()
+        cache.k_pool[:, 0] = kb.view(4, P, dk).to(dev)
+    bt = torch.arange(4, dtype=torch.int32, device=dev).view(1, 4)
+    lens = torch.tensor([L], dtype=torch.int32, device=dev)
+    sm = 1 / math.sqrt(dk)
+    ds = pkv.DecodeStep(cache, hq, 1, L, 256, verify=False)
+    out = ds.attend(q.to(dev), bt, lens, sm, None).float().cpu().numpy()[0]
+    ref, lse_ref = attention.attend(q[0].double().numpy(), k_hat[:, None, :], k_hat[:, None, :dv], sm)
+    assert_close(out, ref, f"mla single-token jump {kv} {jumps}")
+    assert np.allclose(ds.lse.cpu().numpy()[0], lse_ref, rtol=0, atol=1e-3)
 
 
 def _gqa_direct_case(kv, vals_k, vals_v, bt_pages, L, hq, P, split, num_pages, seed=11):

@@ -134,9 +134,10 @@ def test_row_scale_leaves_nan_out_of_the_row_amax():
     c2, s2 = quant.quantize_rows(np.full((1, 4), np.nan))
     assert s2[0] == 1.0 and np.all(c2 == 0x7F)
     # an infinity is a magnitude: scale inf, finite values encode as zero codes and
-    # inf / inf is the positive default NaN
-    c3, s3 = quant.quantize_rows(np.array([[np.inf, 3.0, -3.0]]))
-    assert np.isinf(s3[0]) and c3[0, 0] == 0x7F and c3[0, 1] == 0x00 and c3[0, 2] == 0x80
+    # inf / inf is the default NaN with the sign bit set, for either sign of inf
+    c3, s3 = quant.quantize_rows(np.array([[np.inf, 3.0, -3.0, -np.inf]]))
+    assert np.isinf(s3[0]) and c3[0, 0] == 0xFF and c3[0, 1] == 0x00 and c3[0, 2] == 0x80
+    assert c3[0, 3] == 0xFF
 
 
 def test_scale_from_amax_subnormal_results():
