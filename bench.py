@@ -3,18 +3,25 @@
 A step is one pass of the whole hot path over a batch of decode requests:
     pkv_verify -> pkv_append (one new token per request) -> pkv_decode_attn
     -> pkv_combine
-captured once as a HIP graph and replayed K times between two device
-synchronizations (wall clock); a separate eager pass times the decode kernel
-with events on the stream it is launched on.
+captured once as a HIP graph. Before every timed step a 1 GiB buffer is
+written and read back (pkv_fill_u32, pkv_read_u32, outside the graph),
+which evicts the 256 MB last-level cache as the model's other layers would
+between two decode steps of one layer (the read makes the write-back of the
+dirty lines happen there, not in the step); each step is then bracketed by
+HIP events on its stream.
+``ms_per_step`` is the median of those flushed steps (with a distribution-free
+95% confidence interval); warm figures (replays back to back, no flush) are
+reported beside them. A separate flushed eager pass times the decode kernel
+alone with events on the stream it is launched on (the roofline figure).
 Default workload: the concurrency-sweep point at batch 64 (contexts uniform
 on [2048, 32768], 64 query / 8 KV heads, head dim 128, page 16, per-head
 e4m3 scales, tag check on). Inputs are built on the GPU before timing.
 
 Printed: one JSON line. ``value`` is KV GB/s of the step (e4m3 cache bytes
-read by the step / step time); also sequence-steps/s, the BF16-cache step for
-comparison, the decode kernel's roofline (its algorithmic bytes over its
-average duration, timed with events on the launching stream) and the oracle
-on the host as a CPU baseline.
+read by the step / median flushed step time); also sequence-steps/s, the
+BF16-cache step for comparison, the decode kernel's roofline (its algorithmic
+bytes over its average flushed duration) and the oracle on the host's cores
+as a CPU baseline (run first, before the GPU is touched).
 
     python bench.py [--steps K] [--warmup W] [--batch B] [--no-bf16]
                     [--no-cpu-baseline] [--sweep] [--integrity]
@@ -29,6 +36,7 @@ import time
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK = 2500.0  # TFLOP/s, dense
+FLUSH_BYTES = 1 << 30    # written, then read, before every timed step: 4x the 256 MB MALL
 
 # HBM traffic of the decode kernel from rocprofv3 --pmc runs of this same
 # command (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, mean over the
@@ -179,31 +187,98 @@ class Runner:
         torch.cuda.synchronize()
         return g
 
-    def time(self, steps: int, warmup: int):
-        """(ms per step, decode kernel ms). Eager steps with events around the
-        decode launch give the kernel's own duration; the step time is K
-        replays of the captured step between two synchronizations."""
+    def time(self, steps: int, warmup: int, flush=None) -> dict:
+        """Flushed and warm timings of the step (milliseconds).
+
+        decode: a flushed eager pass, each step's decode launch bracketed by
+          events on its stream (the kernel's own duration).
+        flushed: the captured step replayed once per flush, bracketed by
+          events; warm: replays back to back. Each list holds one time per
+          step; the headline is the flushed median."""
         torch = self.torch
+        flush = flush or Flusher()
+        ev = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
         for _ in range(warmup):
+            flush()
             self.one()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
+        evs = [ev() for _ in range(steps)]
         torch.cuda.synchronize()
         for e in evs:
+            flush()
             self.one(e)
         torch.cuda.synchronize()
-        dec_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+        dec = [a.elapsed_time(b) for a, b in evs]
         g = self.capture()
         for _ in range(warmup):
+            flush()
             g.replay()
+        fl = [ev() for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(steps):
+        for a, b in fl:
+            flush()
+            a.record()
             g.replay()
+            b.record()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        wm = [ev() for _ in range(steps)]
+        for a, b in wm:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
         del g
-        return (t1 - t0) * 1e3 / steps, dec_ms
+        return {"flushed": [a.elapsed_time(b) for a, b in fl],
+                "warm": [a.elapsed_time(b) for a, b in wm],
+                "decode": dec,
+                "wall_ms_per_flushed_step": (t1 - t0) * 1e3 / steps}
+
+
+class Flusher:
+    """Evicts the last-level cache on the current stream: writes FLUSH_BYTES
+    with the library's fill kernel (a new value each call), then reads them
+    back with its read kernel, so that the dirty lines the writes leave are
+    written back here and not inside the next timed step."""
+
+    def __init__(self):
+        import torch
+
+        import decode_attention_fp8_amd as pkv
+        self.pkv = pkv
+        self.buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+        self.sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.pkv.pkv_fill_u32(self.buf, self.n)
+        self.pkv.pkv_read_u32(self.buf, self.sink)
+
+
+def median_ci(xs):
+    """(median, lo, hi): the sample median and a distribution-free 95%
+    confidence interval for the median, between the order statistics j and
+    n + 1 - j with j the 2.5% quantile of Binomial(n, 1/2)."""
+    from scipy.stats import binom
+    v = sorted(xs)
+    n = len(v)
+    med = (v[(n - 1) // 2] + v[n // 2]) / 2
+    j = int(binom.ppf(0.025, n, 0.5))
+    if j < 1:
+        return med, v[0], v[-1]
+    return med, v[j - 1], v[n - j]
+
+
+def summary(t: dict) -> dict:
+    """Median, 95% CI and mean of the flushed, warm and decode timings."""
+    out = {}
+    for key in ("flushed", "warm", "decode"):
+        med, lo, hi = median_ci(t[key])
+        out[key] = {"median_ms": round(med, 5), "ci95_ms": [round(lo, 5), round(hi, 5)],
+                    "mean_ms": round(sum(t[key]) / len(t[key]), 5)}
+    out["wall_ms_per_flushed_step"] = round(t["wall_ms_per_flushed_step"], 5)
+    return out
 
 
 def time_handoff(steps: int, n_pages: int = 8192):
@@ -366,44 +441,139 @@ def time_int4(steps: int, warmup: int, layers: int = 16, n: int = 8192, k: int =
             "rows": rows}
 
 
-def cpu_baseline(w, budget_s: float = 12.0):
-    """The oracle (quantise + tag check + attention) on a bounded sample of the
-    same workload: whole requests in order, until the time budget is spent."""
+def _oracle_unit(task):
+    """One (request, kv head) unit of the oracle in a worker process: the
+    unit's bf16 inputs are drawn first (not timed), then quantise K and V
+    under the head's scales and run float64 attention for the head's query
+    heads (timed). Returns (tokens, seconds)."""
+    name, b, h, ks, vs, aborted = task
+    from oracle import attention, quant, step
+    if name not in _BUILT:
+        _register_workloads()
+        _BUILT[name] = _WORKLOADS[name]()
+    w = _BUILT[name]
+    x = step.bf16_bits_to_f64(w.k_bits(b, heads=[h]))[:, 0, :]
+    y = step.bf16_bits_to_f64(w.v_bits(b, heads=[h]))[:, 0, :]
+    q = step.bf16_bits_to_f64(w.q_bits()[b, h * w.group:(h + 1) * w.group])
+    t = time.perf_counter()
+    kk = quant.dequantize(quant.quantize(x, ks), ks)[:, None, :]
+    vv = quant.dequantize(quant.quantize(y, vs), vs)[:, None, :]
+    if not aborted:
+        attention.attend(q, kk, vv, w.sm_scale)
+    return int(w.seq_lens[b]), time.perf_counter() - t
+
+
+def _worker_init():
     from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+    try:
+        import torch
+        torch.set_num_threads(1)
+    except ImportError:
+        pass
+
+
+_WORKLOADS = {}  # name -> constructor of the workloads the baseline can sample
+_BUILT = {}      # name -> workload, per process
+
+
+def _register_workloads():
+    import workloads as W
+    _WORKLOADS.update({f"sweep_b{B}": (lambda B=B: W.sweep(B)) for B in W.SWEEP_BATCHES})
+    _WORKLOADS.update({"gqa_b8": W.gqa, "long_b4": W.long_context})
+
+
+def cpu_cores() -> int:
+    """Host cores to use: this process's CPU affinity, at most 16 (a GPU machine's
+    share for one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, budget_s: float = 6.0):
+    """The oracle (tag check, quantise, float64 attention) on the host's
+    cores, one process per core over (request, kv head) units, BLAS at one
+    thread. Runs before the GPU is touched. A bounded sample: whole requests
+    in order, as many as the first round of units (one per process, timed
+    under full load) says fit in about budget_s of wall time; throughput =
+    sample bytes / (summed unit time / processes). A unit's inputs are drawn
+    before its clock starts."""
+    import multiprocessing as mp
 
     import oracle
-    from oracle import attention, quant, step
-
+    from oracle import step
+    _register_workloads()
+    if w.name not in _WORKLOADS:
+        return None
+    n = cpu_cores()
     ks, vs = step.scales(w, "fp8")
-    qall = w.q_values().double().numpy()
-    G = w.group
-    t_total, tokens, reqs = 0.0, 0, 0
-    with threadpool_limits(1):
-        t = time.perf_counter()
-        flags = oracle.verify.verify(w.page_tags, w.block_table, w.expected_tags, w.seq_lens,
-                                     w.page_size)
-        t_total += time.perf_counter() - t
-        for b in range(w.batch):
-            for h in range(w.num_kv_heads):
-                x = w.k_values(b, heads=[h]).double().numpy()[:, 0, :]
-                y = w.v_values(b, heads=[h]).double().numpy()[:, 0, :]
-                t = time.perf_counter()
-                kk = quant.dequantize(quant.quantize(x, ks[h]), ks[h])[:, None, :]
-                vv = quant.dequantize(quant.quantize(y, vs[h]), vs[h])[:, None, :]
-                if not flags[b]:
-                    attention.attend(qall[b, h * G:(h + 1) * G], kk, vv, w.sm_scale)
-                t_total += time.perf_counter() - t
-            tokens += int(w.seq_lens[b])
-            reqs += 1
-            if t_total > budget_s:
+    t = time.perf_counter()
+    flags = oracle.verify.verify(w.page_tags, w.block_table, w.expected_tags, w.seq_lens,
+                                 w.page_size)
+    t_verify = time.perf_counter() - t
+    H = w.num_kv_heads
+    units = lambda reqs: [(w.name, b, h, ks[h], vs[h], bool(flags[b])) for b in reqs
+                          for h in range(H)]
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(n, initializer=_worker_init) as pool:
+        # first, enough whole requests to give every process a unit; their
+        # time under full load sets how many more requests fit the budget
+        reqs = list(range(min(w.batch, -(-n // H))))
+        res = pool.map(_oracle_unit, units(reqs), chunksize=1)
+        per = sum(r[1] for r in res) / max(1, sum(r[0] for r in res))  # s per token and head
+        est = sum(r[1] for r in res) / n
+        more = []
+        for b in range(len(reqs), w.batch):
+            if est >= budget_s:
                 break
+            more.append(b)
+            est += per * int(w.seq_lens[b]) * H / n
+        if more:
+            res += pool.map(_oracle_unit, units(more), chunksize=1)
+        reqs += more
+    tasks = units(reqs)
+    busy = sum(r[1] for r in res) + t_verify
+    tokens = sum(int(w.seq_lens[b]) for b in reqs)
     sample_bytes = tokens * w.num_kv_heads * (w.head_dim_k + w.head_dim_v)
-    return {"value": round(sample_bytes / t_total / 1e9, 6), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"first {reqs} of {w.batch} requests ({tokens} context tokens, all "
-                      f"{w.num_kv_heads} kv heads): quantise K/V, tag check of the batch, "
-                      f"float64 attention; {t_total:.2f} s on one thread",
-            "seq_steps_per_s": round(reqs / t_total, 4)}
+    wall = busy / n
+    return {"value": round(sample_bytes / wall / 1e9, 6), "unit": "GB/s", "cores": n,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"first {len(reqs)} of {w.batch} requests ({tokens} context tokens, all "
+                      f"{w.num_kv_heads} kv heads, {len(tasks)} units on {n} processes): "
+                      f"tag check of the batch, quantise K/V, float64 attention; "
+                      f"{busy:.1f} s of unit time",
+            "seq_steps_per_s": round(len(reqs) / wall, 4)}
+
+
+def step_record(t: dict, nbytes: int, batch: int) -> dict:
+    """Per-step figures from Runner.time: flushed median (headline) with its
+    95% CI, warm median, decode kernel mean."""
+    sm = summary(t)
+    med = sm["flushed"]["median_ms"]
+    return {"ms_per_step": med, "ci95_ms": sm["flushed"]["ci95_ms"],
+            "kv_gbs": round(nbytes / (med * 1e-3) / 1e9, 2),
+            "hbm_frac": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "seq_steps_per_s": round(batch / (med * 1e-3), 1),
+            "warm_ms_per_step": sm["warm"]["median_ms"],
+            "warm_kv_gbs": round(nbytes / (sm["warm"]["median_ms"] * 1e-3) / 1e9, 2),
+            "decode_ms": sm["decode"]["mean_ms"]}
+
+
+DTYPE = ("e4m3 KV cache; QK^T bf16 x bf16 and P.V f16 x f16 on MFMA (codes convert exactly, "
+         "numerators rounded to f16), f32 accumulation and softmax")
 
 
 def main():
@@ -415,6 +585,13 @@ def main():
     import torch
 
     import workloads as W
+
+    w = {"sweep": lambda: W.sweep(args.batch), "gqa": W.gqa, "long": W.long_context,
+         "mla": W.mla}[args.workload]()
+    # the oracle on the host's cores first, while no process has touched the GPU
+    cpu = None
+    if not args.no_cpu_baseline and not w.latent and not args.copy_calibration:
+        cpu = cpu_baseline(w)
 
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
@@ -429,10 +606,12 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
         return
 
-    w = {"sweep": lambda: W.sweep(args.batch), "gqa": W.gqa, "long": W.long_context,
-         "mla": W.mla}[args.workload]()
+    flush = Flusher()
     run = Runner(w, "fp8", args.split or None)
-    ms, dec_ms = run.time(args.steps, args.warmup)
+    t = run.time(args.steps, args.warmup, flush)
+    sm = summary(t)
+    ms = sm["flushed"]["median_ms"]
+    dec_ms = sm["decode"]["mean_ms"]
     split = run.step.split_tokens
     # requests the step actually reads: those the tag check did not abort
     read = (run.step.abort.cpu().numpy() == 0) if run.step.verify else None
@@ -445,14 +624,22 @@ def main():
         "metric": "FP8 paged decode-attn KV GB/s (% HBM peak) and seq-steps/s at B=1..64",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "e4m3-kv/f32",
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE,
         "data": "synthetic (seeded counter-based bf16 N(0,1); lengths U[2048,32768])",
         "config": {"workload": f"{w.name}: {w.description}", "batch": w.batch,
                    "total_context_tokens": w.total_tokens, "split_tokens": split,
                    "aborted_requests": n_aborted, "context_tokens_read": tokens_read,
                    "kv_dtype": "e4m3", "kv_bytes": fp8_bytes},
+        "flushed": True,
+        "timing": {"method": f"median of {args.steps} steps, each after a {FLUSH_BYTES >> 20} MiB "
+                             "write and read-back that evict the last-level cache; HIP events around each "
+                             "graph replay on its stream",
+                   **sm},
+        "ci95_ms": sm["flushed"]["ci95_ms"],
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "seq_steps_per_s": round(w.batch / (ms * 1e-3), 1),
+        "warm": {"ms_per_step": sm["warm"]["median_ms"],
+                 "kv_gbs": round(fp8_bytes / (sm["warm"]["median_ms"] * 1e-3) / 1e9, 2)},
     }
     if w.latent:
         # the dense contraction bounds this kernel: QK^T over 576 dims and PV
@@ -479,14 +666,12 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_bf16:
         rb = Runner(w, "bf16", args.split or None)  # its own suggested split
-        ms_b, dec_b = rb.time(args.steps, args.warmup)
+        tb = rb.time(args.steps, args.warmup, flush)
+        split_b = rb.step.split_tokens
         del rb
         torch.cuda.empty_cache()
-        rec["bf16"] = {"ms_per_step": round(ms_b, 5),
-                       "kv_gbs": round(kv_bytes(w, 2, read) / (ms_b * 1e-3) / 1e9, 2),
-                       "decode_ms": round(dec_b, 5),
-                       "seq_steps_per_s": round(w.batch / (ms_b * 1e-3), 1)}
-        rec["fp8_speedup_over_bf16"] = round(ms_b / ms, 4)
+        rec["bf16"] = {**step_record(tb, kv_bytes(w, 2, read), w.batch), "split_tokens": split_b}
+        rec["fp8_speedup_over_bf16"] = round(rec["bf16"]["ms_per_step"] / ms, 4)
     if args.sweep:
         rows = []
         for B in W.SWEEP_BATCHES:
@@ -494,13 +679,11 @@ def main():
             row = {"batch": B}
             for kv, e in (("fp8", 1), ("bf16", 2)):
                 r = Runner(ws, kv, None)
-                m, d = r.time(max(10, args.steps // 2), 5)
+                tr = r.time(max(20, args.steps), 5, flush)
                 nb = kv_bytes(ws, e, r.step.abort.cpu().numpy() == 0)
+                row[kv] = {**step_record(tr, nb, B), "split_tokens": r.step.split_tokens}
                 del r
                 torch.cuda.empty_cache()
-                row[kv] = {"ms_per_step": round(m, 5), "kv_gbs": round(nb / (m * 1e-3) / 1e9, 2),
-                           "hbm_frac": round(nb / (m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                           "seq_steps_per_s": round(B / (m * 1e-3), 1), "decode_ms": round(d, 5)}
             row["fp8_speedup_over_bf16"] = round(row["bf16"]["ms_per_step"] / row["fp8"]["ms_per_step"], 4)
             rows.append(row)
         rec["sweep"] = rows
@@ -509,34 +692,40 @@ def main():
         for B in (1, 2, 4, 8):
             wi = W.integrity_cost(B)
             on = Runner(wi, "fp8", None, verify=True)
-            m_on, _ = on.time(max(20, args.steps), 10)
+            t_on = summary(on.time(max(50, args.steps), 10, flush))
             del on
             off = Runner(wi, "fp8", None, verify=False)
-            m_off, _ = off.time(max(20, args.steps), 10)
+            t_off = summary(off.time(max(50, args.steps), 10, flush))
             del off
             torch.cuda.empty_cache()
-            rows.append({"batch": B, "ms_verify_on": round(m_on, 5), "ms_noop": round(m_off, 5),
-                         "overhead": round((m_on - m_off) / m_off, 4)})
+            m_on, m_off = t_on["flushed"]["median_ms"], t_off["flushed"]["median_ms"]
+            w_on, w_off = t_on["warm"]["median_ms"], t_off["warm"]["median_ms"]
+            rows.append({"batch": B, "ms_verify_on": m_on, "ci95_on": t_on["flushed"]["ci95_ms"],
+                         "ms_noop": m_off, "ci95_noop": t_off["flushed"]["ci95_ms"],
+                         "overhead": round((m_on - m_off) / m_off, 4),
+                         "warm_overhead": round((w_on - w_off) / w_off, 4)})
         rec["integrity_cost"] = rows
     if args.handoff:
         rec["handoff"] = time_handoff(args.steps)
     if args.row_scales and not w.latent:
         rr = Runner(w, "fp8", args.split or None, row_scales=True)
-        ms_r, dec_r = rr.time(args.steps, args.warmup)
+        tr = summary(rr.time(args.steps, args.warmup, flush))
         del rr
         torch.cuda.empty_cache()
+        ms_r, dec_r = tr["flushed"]["median_ms"], tr["decode"]["mean_ms"]
         scale_bytes = int(w.seq_lens[read].sum() if read is not None else w.total_tokens) * \
             w.num_kv_heads * 2 * 4
         rec["row_scales"] = {
-            "ms_per_step": round(ms_r, 5), "decode_ms": round(dec_r, 5),
+            "ms_per_step": round(ms_r, 5), "ci95_ms": tr["flushed"]["ci95_ms"],
+            "decode_ms": round(dec_r, 5),
             "kv_gbs": round(fp8_bytes / (ms_r * 1e-3) / 1e9, 2),
             "decode_gbs_codes_and_scales": round((fp8_bytes + scale_bytes) / (dec_r * 1e-3) / 1e9, 2),
             "step_vs_static_scales": round(ms_r / ms, 4),
             "kernel": "decode_gqa_mfma_kernel<2, true>"}
     if args.int4:
         rec["int4_linear"] = time_int4(max(10, args.steps // 2), 3)
-    if not args.no_cpu_baseline and not w.latent:
-        rec["cpu_baseline"] = cpu_baseline(w)
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)
 
 

@@ -15,7 +15,7 @@ from ._binding import (EXPORTS, LIB_PATH, PKV_EHIP, PKV_EINVAL, PKV_EUNSUPPORTED
                        PKV_KV_E4M3, PKV_OK, Cache, PkvCacheStruct, PkvError, pkv_append,
                        pkv_combine, pkv_decode_attn, pkv_decode_attn_drafts, pkv_int4_linear,
                        pkv_int4_linear_workspace, int4_workspace,
-                       pkv_requantize_pages, pkv_scales_from_amax,
+                       pkv_fill_u32, pkv_read_u32, pkv_requantize_pages, pkv_scales_from_amax,
                        pkv_strerror,
                        pkv_suggest_split, pkv_verify, pkv_version)
 from .step import DecodeStep, allocate_cache
@@ -24,6 +24,6 @@ __all__ = ["EXPORTS", "LIB_PATH", "PKV_EHIP", "PKV_EINVAL", "PKV_EUNSUPPORTED", 
            "PKV_KV_E4M3", "PKV_OK", "Cache", "PkvCacheStruct", "PkvError", "pkv_append",
            "pkv_combine", "pkv_decode_attn", "pkv_decode_attn_drafts", "pkv_int4_linear",
            "pkv_int4_linear_workspace", "int4_workspace",
-           "pkv_requantize_pages", "pkv_scales_from_amax",
+           "pkv_fill_u32", "pkv_read_u32", "pkv_requantize_pages", "pkv_scales_from_amax",
            "pkv_strerror",
            "pkv_suggest_split", "pkv_verify", "pkv_version", "DecodeStep", "allocate_cache"]

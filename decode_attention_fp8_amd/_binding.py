@@ -21,7 +21,8 @@ PKV_KV_E4M3, PKV_KV_BF16 = 1, 2
 
 EXPORTS = ("pkv_scales_from_amax", "pkv_append", "pkv_verify", "pkv_decode_attn",
            "pkv_combine", "pkv_decode_attn_drafts", "pkv_requantize_pages", "pkv_int4_linear",
-           "pkv_int4_linear_workspace",
+           "pkv_int4_linear_workspace", "pkv_fill_u32", "pkv_read_u32",
+
            "pkv_suggest_split", "pkv_strerror", "pkv_version")
 
 
@@ -59,6 +60,8 @@ def _load() -> ctypes.CDLL:
         "pkv_requantize_pages": (I32, [CP, CP, P, P, P, P, I32, P]),
         "pkv_int4_linear": (I32, [P, P, P, I32, I32, I32, P, P, P]),
         "pkv_int4_linear_workspace": (I64, [I32, I32, I32]),
+        "pkv_fill_u32": (I32, [P, I64, ctypes.c_uint32, P]),
+        "pkv_read_u32": (I32, [P, I64, P, P]),
         "pkv_suggest_split": (I32, [CP, I32, I32, I64, I32]),
         "pkv_strerror": (ctypes.c_char_p, [I32]),
         "pkv_version": (I32, []),
@@ -332,3 +335,24 @@ def pkv_combine(o_part: torch.Tensor, lse_part: torch.Tensor, seq_lens: torch.Te
     _check("pkv_combine", _lib.pkv_combine(
         _ptr(o_part), _ptr(lse_part), _ptr(seq_lens), B, Hq, Dv, int(split_tokens), max_splits,
         int(max_seq_len), _ptr(abort_flags), _ptr(out), _ptr(lse_out), _stream(stream)))
+
+
+def pkv_fill_u32(dst: torch.Tensor, value: int, stream=None) -> None:
+    """Write `value` to every 32-bit word of a contiguous device tensor (a
+    measurement helper: evicts the last-level cache between timed steps)."""
+    if not dst.is_contiguous() or dst.numel() * dst.element_size() % 4:
+        raise ValueError("dst must be contiguous whole 32-bit words")
+    _check("pkv_fill_u32", _lib.pkv_fill_u32(
+        _ptr(dst), dst.numel() * dst.element_size() // 4, int(value) & 0xFFFFFFFF,
+        _stream(stream)))
+
+
+
+def pkv_read_u32(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read every whole 16-byte word of a contiguous device tensor, XORing
+    into sink (one int32 on the device): with pkv_fill_u32, the last-level
+    cache flush of the measurement."""
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    _check("pkv_read_u32", _lib.pkv_read_u32(
+        _ptr(src), src.numel() * src.element_size() // 4, _ptr(sink), _stream(stream)))

@@ -343,6 +343,26 @@ int64_t pkv_int4_linear_workspace(int32_t batch, int32_t n, int32_t k);
 int32_t pkv_suggest_split(const pkv_cache* cache, int32_t num_q_heads, int32_t batch,
                           int64_t total_tokens, int32_t max_seq_len);
 
+/*
+ * Measurement helper, not part of the method: writes `value` to n_words
+ * consecutive uint32 words of dst (device pointer, 16-byte aligned,
+ * caller-owned) with a plain write kernel. Writing a buffer several times
+ * the 256 MB last-level cache between timed decode steps evicts the
+ * previous step's lines, as the model's other layers do in serving.
+ * EINVAL: NULL or misaligned dst, n_words < 0.
+ */
+int pkv_fill_u32(void* dst, int64_t n_words, uint32_t value, hipStream_t stream);
+
+/*
+ * Measurement helper, not part of the method: reads the whole 16-byte words
+ * of n_words uint32 words of src (device pointer, 16-byte aligned) and XORs
+ * what it read into *sink (one device word, caller-owned). Read after
+ * pkv_fill_u32 over the same buffer, it evicts the dirty lines the fill
+ * left, so their write-back is not charged to the next timed step.
+ * EINVAL: NULL or misaligned pointers, n_words < 0.
+ */
+int pkv_read_u32(const void* src, int64_t n_words, uint32_t* sink, hipStream_t stream);
+
 /* Host helper: a static string naming a status code. */
 const char* pkv_strerror(int32_t status);
 
