@@ -13,7 +13,8 @@ abort the request).
 """
 from ._binding import (EXPORTS, LIB_PATH, PKV_EHIP, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_KV_BF16,
                        PKV_KV_E4M3, PKV_OK, Cache, PkvCacheStruct, PkvError, pkv_append,
-                       pkv_combine, pkv_decode_attn, pkv_decode_attn_drafts, pkv_int4_linear,
+                       pkv_combine, pkv_decode_attn, pkv_decode_attn_drafts,
+                       pkv_decode_attn_static, STATIC_SCRATCH_BYTES, pkv_int4_linear,
                        pkv_int4_linear_workspace, int4_workspace,
                        pkv_fill_u32, pkv_read_u32, pkv_requantize_pages, pkv_scales_from_amax,
                        pkv_strerror,
@@ -22,7 +23,8 @@ from .step import DecodeStep, allocate_cache
 
 __all__ = ["EXPORTS", "LIB_PATH", "PKV_EHIP", "PKV_EINVAL", "PKV_EUNSUPPORTED", "PKV_KV_BF16",
            "PKV_KV_E4M3", "PKV_OK", "Cache", "PkvCacheStruct", "PkvError", "pkv_append",
-           "pkv_combine", "pkv_decode_attn", "pkv_decode_attn_drafts", "pkv_int4_linear",
+           "pkv_combine", "pkv_decode_attn", "pkv_decode_attn_drafts",
+           "pkv_decode_attn_static", "STATIC_SCRATCH_BYTES", "pkv_int4_linear",
            "pkv_int4_linear_workspace", "int4_workspace",
            "pkv_fill_u32", "pkv_read_u32", "pkv_requantize_pages", "pkv_scales_from_amax",
            "pkv_strerror",

@@ -22,7 +22,7 @@ PKV_KV_E4M3, PKV_KV_BF16 = 1, 2
 EXPORTS = ("pkv_scales_from_amax", "pkv_append", "pkv_verify", "pkv_decode_attn",
            "pkv_combine", "pkv_decode_attn_drafts", "pkv_requantize_pages", "pkv_int4_linear",
            "pkv_int4_linear_workspace", "pkv_fill_u32", "pkv_read_u32",
-
+           "pkv_decode_attn_static",
            "pkv_suggest_split", "pkv_strerror", "pkv_version")
 
 
@@ -62,6 +62,7 @@ def _load() -> ctypes.CDLL:
         "pkv_int4_linear_workspace": (I64, [I32, I32, I32]),
         "pkv_fill_u32": (I32, [P, I64, ctypes.c_uint32, P]),
         "pkv_read_u32": (I32, [P, I64, P, P]),
+        "pkv_decode_attn_static": (I32, [CP, P, I32, P, P, I32, I32, I32, P, F, I32, P, P, P]),
         "pkv_suggest_split": (I32, [CP, I32, I32, I64, I32]),
         "pkv_strerror": (ctypes.c_char_p, [I32]),
         "pkv_version": (I32, []),
@@ -356,3 +357,23 @@ def pkv_read_u32(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
         raise ValueError("src must be contiguous")
     _check("pkv_read_u32", _lib.pkv_read_u32(
         _ptr(src), src.numel() * src.element_size() // 4, _ptr(sink), _stream(stream)))
+
+STATIC_SCRATCH_BYTES = 64 << 20  # PKV_STATIC_SCRATCH_BYTES of include/pkv.h
+
+
+def pkv_decode_attn_static(cache: Cache, q: torch.Tensor, block_table: torch.Tensor,
+                           seq_lens: torch.Tensor, max_seq_len: int,
+                           abort_flags: torch.Tensor | None, sm_scale: float, split_tokens: int,
+                           out: torch.Tensor, lse_out: torch.Tensor | None = None,
+                           stream=None) -> None:
+    """Decode and combine with the partials in the library's own device array
+    (no caller buffers, nothing allocated): q bf16 [B, Hq, Dk] -> out bf16
+    [B, Hq, Dv], lse_out f32 [B, Hq] or None."""
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.bfloat16, "out")
+    B, Hq, _ = q.shape
+    cs = cache.struct()
+    _check("pkv_decode_attn_static", _lib.pkv_decode_attn_static(
+        ctypes.byref(cs), _ptr(q), Hq, _ptr(block_table), _ptr(seq_lens), B,
+        int(block_table.shape[1]), int(max_seq_len), _ptr(abort_flags), float(sm_scale),
+        int(split_tokens), _ptr(out), _ptr(lse_out), _stream(stream)))

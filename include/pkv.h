@@ -344,6 +344,35 @@ int32_t pkv_suggest_split(const pkv_cache* cache, int32_t num_q_heads, int32_t b
                           int64_t total_tokens, int32_t max_seq_len);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that forbid hipMalloc): pkv_decode_attn followed by
+ * pkv_combine on `stream`, with the split partials (o_part, lse_part) held in
+ * a fixed array of PKV_STATIC_SCRATCH_BYTES inside the library instead of
+ * caller buffers. Calls no allocating routine.
+ *
+ * Arguments and results as for pkv_decode_attn then pkv_combine with
+ * max_splits = max(1, ceil(max_seq_len / split_tokens)); the caller passes
+ * only the inputs and the outputs:
+ *   out:     bf16 [batch][num_q_heads][head_dim_v]
+ *   lse_out: float32 [batch][num_q_heads], or NULL.
+ * The partials need batch * num_q_heads * max_splits * (head_dim_v + 1) * 4
+ * bytes (the first part rounded up to 256); above PKV_STATIC_SCRATCH_BYTES
+ * the call returns PKV_EINVAL and enqueues nothing (the allocating pair then
+ * serves). Each GPU holds one copy of the array from the first call on it
+ * until the process ends; every call on that GPU shares it, so calls that
+ * overlap in time on one GPU (two streams, two threads) race and must be
+ * ordered by the caller. Nothing in it needs clearing between calls.
+ * Errors: as for pkv_decode_attn and pkv_combine; PKV_EHIP if the array's
+ * address cannot be obtained.
+ */
+#define PKV_STATIC_SCRATCH_BYTES (64ll << 20)
+int pkv_decode_attn_static(const pkv_cache* cache, const void* q, int32_t num_q_heads,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           int32_t batch, int32_t max_pages, int32_t max_seq_len,
+                           const uint8_t* abort_flags, float sm_scale, int32_t split_tokens,
+                           void* out, float* lse_out, hipStream_t stream);
+
+/*
  * Measurement helper, not part of the method: writes `value` to n_words
  * consecutive uint32 words of dst (device pointer, 16-byte aligned,
  * caller-owned) with a plain write kernel. Writing a buffer several times
