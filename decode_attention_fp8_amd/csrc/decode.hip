@@ -7,8 +7,8 @@
 // separate tag check is never read.
 //
 // This file holds the entry point and the generic kernel used for shapes
-// without a specialised one (decode_gqa.hip covers head dim 128 with 8 query
-// heads per kv head).
+// without a specialised one (decode_gqa_mfma.hip covers head dim 128 with up
+// to 16 query heads per kv head, decode_mla.hip the latent layout).
 //
 // Work unit = (request b, kv head g, group of NH query heads, split c).
 // A workgroup of four waves takes one work unit; wave w handles tokens
@@ -247,16 +247,14 @@ extern "C" int pkv_decode_attn(const pkv_cache* cache, const void* q, int32_t nu
   if (cache->k_row_scale) {
     // scales set at append: the grouped-query MFMA kernel reads them
     if (gqa_mfma_path_supported(dk, dv, G, latent, split_tokens, cache->page_size))
-      return launch_decode_gqa_mfma(p, static_cast<int>(n_split_blocks), batch, stream);
+      return launch_decode_gqa_mfma(p, true, static_cast<int>(n_split_blocks), batch, stream);
     return PKV_EUNSUPPORTED;
   }
   if (latent && mla_fast_path_supported(dk, dv, cache->num_kv_heads, num_q_heads,
                                         cache->page_size, split_tokens))
     return launch_decode_mla(p, e4m3, static_cast<int>(n_split_blocks), batch, stream);
-  if (e4m3 && gqa_mfma_path_supported(dk, dv, G, latent, split_tokens, cache->page_size))
-    return launch_decode_gqa_mfma(p, static_cast<int>(n_split_blocks), batch, stream);
-  if (gqa_fast_path_supported(dk, dv, G, latent, split_tokens, cache->page_size))
-    return launch_decode_gqa(p, e4m3, static_cast<int>(n_split_blocks), batch, stream);
+  if (gqa_mfma_path_supported(dk, dv, G, latent, split_tokens, cache->page_size))
+    return launch_decode_gqa_mfma(p, e4m3, static_cast<int>(n_split_blocks), batch, stream);
   return e4m3 ? dispatch<true>(p, latent, dk, G, static_cast<int>(n_split_blocks), batch, stream)
               : dispatch<false>(p, latent, dk, G, static_cast<int>(n_split_blocks), batch, stream);
 }

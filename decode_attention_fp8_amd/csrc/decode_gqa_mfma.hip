@@ -1,16 +1,21 @@
-// Grouped-query decode over an e4m3 cache with head dim 128 on MFMA, one
+// Grouped-query decode with head dim 128 on MFMA, e4m3 or bf16 cache, one
 // work unit per wave in the hardware dispatcher's order.
 //
 // "Smaller, faster, safer: running Kimi and GLM at scale" (Cloudflare blog),
 // section "Quantizing the KV cache": K and V are held as e4m3 and the
-// attention kernel converts codes as it reads them. The tile math (QK^T and
-// PV on MFMA 16x16x32, the softmax) is that of gqa_mfma_tile.h.
+// attention kernel converts codes as it reads them; the bf16 cache it is
+// compared with is read as stored. The tile math (QK^T and PV on MFMA
+// 16x16x32, the softmax) is that of gqa_mfma_tile.h, in the same layouts for
+// both: only the bytes per value, the conversion and the LDS swizzles differ.
 //
 // One wave per work unit (request, kv head, split), in the one-dimensional
 // longest-first order of find_unit. A split runs in tiles of 32 tokens whose
-// K and V bytes (4 KB each) travel HBM -> LDS by direct-to-LDS loads into a
-// ring of kSlots tiles. With scales set at append (one per row), a tile's 32
-// K and 32 V row scales travel with it (two more loads, 512 bytes of slot).
+// K and V bytes (4 KB each for e4m3, 8 KB for bf16) travel HBM -> LDS by
+// direct-to-LDS loads into a ring of kSlots tiles. With scales set at append
+// (one per row), a tile's 32 K and 32 V row scales travel with it (two more
+// loads, 512 bytes of slot).
+#include <type_traits>
+
 #include "common.h"
 #include "decode_params.h"
 #include "gqa_mfma_tile.h"
@@ -37,11 +42,13 @@ __device__ __forceinline__ void wait_tiles(int ahead) {
   }
 }
 
-template <int kSlots, bool kRowScales>
+template <int kSlots, bool kRowScales, bool kBf16 = false>
 __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
   static_assert(kSlots >= 2 && kSlots <= 4, "ring of 2 to 4 tiles");
-  constexpr int kSlotBytes = kTileBytes + (kRowScales ? 512 : 0);
-  constexpr int kLoads = kRowScales ? 10 : 8;  // loads per tile
+  static_assert(!(kBf16 && kRowScales), "row scales are for e4m3 caches");
+  constexpr int kElem = kBf16 ? 2 : 1;
+  constexpr int kSlotBytes = (kBf16 ? bf16c::kTileBytes : kTileBytes) + (kRowScales ? 512 : 0);
+  constexpr int kLoads = kBf16 ? 16 : (kRowScales ? 10 : 8);  // loads per tile
   __shared__ __attribute__((aligned(16))) uint8_t ring[kSlots * kSlotBytes];
   __shared__ float rowbuf[kRows];
   const int lane = threadIdx.x;
@@ -74,8 +81,8 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
     }
   }
   // row scales: each row's own, applied per token in the tile math
-  const float qk_scale = kRowScales ? p.sm_scale_log2 : p.k_scale[g] * p.sm_scale_log2;
-  const float o_scale = kRowScales ? 1.0f : p.v_scale[g];
+  const float qk_scale = (kRowScales || kBf16) ? p.sm_scale_log2 : p.k_scale[g] * p.sm_scale_log2;
+  const float o_scale = (kRowScales || kBf16) ? 1.0f : p.v_scale[g];
 
   // the unit's pages: lane j holds the byte offsets of (page 64 h + j, kv
   // head g) in vector h < kPageVecs (named variables, so that selecting one
@@ -90,7 +97,8 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
   // the launch's footprint (codes, plus the row scales when set at append),
   // summed while the loads above are in flight
   const int64_t tokens = p.batch <= 64 ? pkv::wave_sum(len) : pkv::launch_tokens(p);
-  const bool stream = pkv::stream_cache(tokens * p.num_kv_heads * (2 * kD + (kRowScales ? 8 : 0)));
+  const bool stream =
+      pkv::stream_cache(tokens * p.num_kv_heads * (2 * kD * kElem + (kRowScales ? 8 : 0)));
 #pragma unroll
   for (int s = 0; s < 4; ++s) asm volatile("" : : "v"(qf[s]));
   asm volatile("" : : "v"(pg0), "v"(pg1), "v"(pg2), "v"(pg3));
@@ -102,7 +110,7 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
   };
   auto page_off = [&](int pg) __attribute__((always_inline)) {
     return (static_cast<int64_t>(page_ok_lane(pg) ? pg : 0) * p.num_kv_heads + g) *
-           (static_cast<int64_t>(P) * kD);
+           (static_cast<int64_t>(P) * kD * kElem);
   };
   const uint64_t valid0 = __ballot(page_ok_lane(pg0)), valid1 = __ballot(page_ok_lane(pg1)),
                  valid2 = __ballot(page_ok_lane(pg2)), valid3 = __ballot(page_ok_lane(pg3));
@@ -118,7 +126,13 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
   const uint8_t* kpool = static_cast<const uint8_t*>(p.k_pool);
   const uint8_t* vpool = static_cast<const uint8_t*>(p.v_pool);
   const uint32_t ring0 = lds_addr(ring);
-  const LaneOffsets lo = lane_offsets(lane);
+  using Offsets = std::conditional_t<kBf16, bf16c::LaneOffsets, LaneOffsets>;
+  Offsets lo;
+  if constexpr (kBf16) {
+    lo = bf16c::lane_offsets(lane);
+  } else {
+    lo = lane_offsets(lane);
+  }
 
   auto group_base = [&](int gg) __attribute__((always_inline)) {
     const int j = (gg << 4) >> log2P;
@@ -129,7 +143,7 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
              __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint64_t>(o) >> 32), jl)))
          << 32) |
         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(o), jl));
-    return off + static_cast<uint32_t>(((gg << 4) & (P - 1)) * kD);
+    return off + static_cast<uint32_t>(((gg << 4) & (P - 1)) * kD * kElem);
   };
   // kLoads loads per tile, always: a 16-token group past the unit's end
   // loads the tile's first group again (its scores are masked and its V rows
@@ -141,7 +155,11 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
     for (int x = 0; x < 2; ++x) {
       const int gg = (t_begin + kTile * t + 16 * x < t_end) ? 2 * t + x : 2 * t;
       offs[x] = group_base(gg);
-      dma_group(slot, x, lo, kpool + offs[x], vpool + offs[x], stream);
+      if constexpr (kBf16) {
+        bf16c::dma_group(slot, x, lo, kpool + offs[x], vpool + offs[x], stream);
+      } else {
+        dma_group(slot, x, lo, kpool + offs[x], vpool + offs[x], stream);
+      }
     }
     if constexpr (kRowScales) {
       // a row's scale sits at 4 bytes per 128 of its codes; lanes 0..31 load
@@ -172,8 +190,12 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
     const bool g0_ok = page_ok(((2 * t) << 4) >> log2P);
     const bool g1_ok = tile0 + 16 < t_end && page_ok(((2 * t + 1) << 4) >> log2P);
     uint8_t* buf = ring + (t % kSlots) * kSlotBytes;
-    tile_math<kRowScales>(buf, lo, qf, qk_scale, g0_ok, g1_ok, min(kTile, t_end - tile0),
-                          rowbuf, a, reinterpret_cast<const float*>(buf + kTileBytes));
+    if constexpr (kBf16) {
+      bf16c::tile_math(buf, lo, qf, qk_scale, g0_ok, g1_ok, min(kTile, t_end - tile0), rowbuf, a);
+    } else {
+      tile_math<kRowScales>(buf, lo, qf, qk_scale, g0_ok, g1_ok, min(kTile, t_end - tile0),
+                            rowbuf, a, reinterpret_cast<const float*>(buf + kTileBytes));
+    }
   }
   // scales set at append: O is relative to the unit's V reference scale
   finish(p, b, g, c, G, kRowScales ? a.vref : o_scale, rowbuf, a);
@@ -187,10 +209,14 @@ bool gqa_mfma_path_supported(int dk, int dv, int group, bool latent, int split_t
          split_tokens <= kMaxUnitPages * page_size;
 }
 
-int launch_decode_gqa_mfma(const DecodeParams& p, int n_split_blocks, int batch,
+int launch_decode_gqa_mfma(const DecodeParams& p, bool e4m3, int n_split_blocks, int batch,
                            hipStream_t stream) {
   const int64_t units = static_cast<int64_t>(n_split_blocks) * p.num_kv_heads * batch;
   if (units > 0x7FFFFFFF) return PKV_EUNSUPPORTED;
+  if (!e4m3) {
+    decode_gqa_mfma_kernel<2, false, true><<<dim3(static_cast<uint32_t>(units)), 64, 0, stream>>>(p);
+    return pkv::launch_status();
+  }
   if (p.k_row_scale) {
     // row-scale offsets are 32-bit
     if (static_cast<int64_t>(p.num_pages) * p.num_kv_heads * p.page_size * 4 > 0xFFFFFFFFLL)

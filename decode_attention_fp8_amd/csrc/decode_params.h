@@ -25,17 +25,11 @@ struct DecodeParams {
   float sm_scale_log2;  // sm_scale * log2(e)
 };
 
-// grouped-query kernel for head dim 128, 8 query heads per kv head
-bool gqa_fast_path_supported(int dk, int dv, int group, bool latent, int split_tokens,
-                             int page_size);
-int launch_decode_gqa(const DecodeParams& p, bool e4m3, int n_split_blocks, int batch,
-                      hipStream_t stream);
-
-// grouped-query kernel on MFMA for an e4m3 cache, head dim 128, up to 16
-// query heads per kv head
+// grouped-query kernel on MFMA for an e4m3 or bf16 cache, head dim 128, up
+// to 16 query heads per kv head
 bool gqa_mfma_path_supported(int dk, int dv, int group, bool latent, int split_tokens,
                              int page_size);
-int launch_decode_gqa_mfma(const DecodeParams& p, int n_split_blocks, int batch,
+int launch_decode_gqa_mfma(const DecodeParams& p, bool e4m3, int n_split_blocks, int batch,
                            hipStream_t stream);
 
 // several query positions per request (a token and its drafts), e4m3, head dim 128

@@ -290,6 +290,172 @@ __device__ __forceinline__ void tile_math(uint8_t* buf, const LaneOffsets& o,
   __builtin_amdgcn_wave_barrier();
 }
 
+// ---------------------------------------------------------------------------
+// bf16 cache: the same tile and operand layouts with two bytes per value, no
+// conversion. A tile's K and V are 8 KB each (16 KB per slot); a 16-token
+// group is 4 KB of K and 4 KB of V, four direct-to-LDS loads each.
+//
+// LDS rows are 256 bytes, 16 chunks of 16 bytes; 64 banks of 4 bytes cover
+// one row, chunk position p taking banks 4p .. 4p+3. K chunk c of tile row t
+// sits at c ^ (t & 15): the 8 rows of one pass of a 16-byte read (lanes
+// 8k .. 8k+7, rows 8(k%2) .. +7 at one chunk) fall on distinct banks. V
+// chunk c of row t sits at c ^ 2(t & 3): one pass of a transposing read
+// (16 lanes: 4 rows x the two chunks of 16 dims) covers 8 distinct
+// positions.
+namespace bf16c {
+
+constexpr int kHalf = kTile * kD * 2;  // K (or V) bytes of a tile
+constexpr int kTileBytes = 2 * kHalf;  // K then V: 16 KB
+
+__device__ __forceinline__ uint32_t kswz(uint32_t t) { return t & 15u; }
+__device__ __forceinline__ uint32_t vswz(uint32_t t) { return (t & 3u) << 1; }
+
+struct LaneOffsets {
+  // DMA sources inside a 16-token group block: load i fills group rows
+  // 4i + (lane >> 4), chunk position lane & 15 (the swizzles depend only on
+  // the row within its group, so both halves of a tile share them)
+  uint32_t kdma[4], vdma[4];
+  // K operand of half x, k-step s: chunk 4 qg + s (dims 32 qg + 8 s ..) of
+  // tile row 16 x + col
+  uint32_t kread[2][4];
+  // V operand of dim block nb: transposing reads of rows 4 qg + e and
+  // 16 + 4 qg + e (e = (lane & 15) >> 2), 8 bytes at chunk 2 nb + (i >> 1),
+  // byte 8 (i & 1) (i = lane & 3): the 16 dims 16 nb .. 16 nb + 15
+  uint32_t vread[8][2];
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
+  LaneOffsets o;
+  const int col = lane & 15, qg = lane >> 4;
+  const uint32_t pos = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t r = 4 * i + (lane >> 4);
+    o.kdma[i] = r * 2 * kD + ((pos ^ kswz(r)) << 4);
+    o.vdma[i] = r * 2 * kD + ((pos ^ vswz(r)) << 4);
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const uint32_t row = 16 * x + col;
+      o.kread[x][st] = row * 2 * kD + ((static_cast<uint32_t>(4 * qg + st) ^ kswz(row)) << 4);
+    }
+  const uint32_t e = (lane & 15) >> 2, i = lane & 3;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t row = 16 * h + 4 * qg + e;
+      const uint32_t c = 2 * nb + (i >> 1);
+      o.vread[nb][h] = kHalf + row * 2 * kD + ((c ^ vswz(row)) << 4) + 8 * (i & 1);
+    }
+  return o;
+}
+
+// DMA of one 16-token group (K and V, 4 KB each) into half x of a slot
+__device__ __forceinline__ void dma_group(uint32_t slot, int x, const LaneOffsets& o,
+                                          const uint8_t* kgroup, const uint8_t* vgroup,
+                                          bool stream) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (stream) {
+      dma16_stream(slot + 4096 * x + 1024 * i, o.kdma[i], kgroup);
+      dma16_stream(slot + kHalf + 4096 * x + 1024 * i, o.vdma[i], vgroup);
+    } else {
+      dma16(slot + 4096 * x + 1024 * i, o.kdma[i], kgroup);
+      dma16(slot + kHalf + 4096 * x + 1024 * i, o.vdma[i], vgroup);
+    }
+  }
+}
+
+// QK^T, softmax and PV of the tile in buf (as tile_math, bf16 values): the
+// numerators are rounded to bf16 for PV, and the rounded values are what the
+// denominator sums, so the weights are normalised exactly as used.
+__device__ __forceinline__ void tile_math(uint8_t* buf, const LaneOffsets& o,
+                                          const bf16x8_t (&qf)[4], float qk_scale, bool g0_ok,
+                                          bool g1_ok, int nv, float* rowbuf, Acc& a) {
+  const int lane = threadIdx.x;
+  const int col = lane & 15, qg = lane >> 4;
+  const bool full = g0_ok && g1_ok && nv == kTile;
+  if (!full) {
+    // V rows past the unit or of a page outside the pool: zero (their
+    // scores are masked, and 0 * NaN must not reach the accumulators)
+    for (int q = lane; q < kTile * 16; q += 64) {
+      const int row = q >> 4;
+      const bool keep = row < nv && (row < 16 ? g0_ok : g1_ok);
+      if (!keep) *reinterpret_cast<uint4*>(buf + kHalf + 16 * q) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  floatx4_t s[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[x][i] = 0.0f;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const uint4 kq = *reinterpret_cast<const uint4*>(buf + o.kread[x][st]);
+      s[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kq), qf[st], s[x], 0, 0, 0);
+    }
+  }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = s[x][i] * qk_scale;
+      if (!full) {
+        const int tt = 16 * x + 4 * qg + i;
+        v = (tt < nv && (x == 0 ? g0_ok : g1_ok)) ? v : -INFINITY;
+      }
+      s[x][i] = v;
+      tmax = fmaxf(tmax, v);
+    }
+  if (a.m == kMUnset) {
+    float hm = fmaxf(tmax, __shfl_xor(tmax, 16));
+    hm = fmaxf(hm, __shfl_xor(hm, 32));
+    if (hm > -INFINITY) a.m = hm;
+  }
+  if (__any(tmax > a.m + kTau)) {
+    float hm = fmaxf(tmax, __shfl_xor(tmax, 16));
+    hm = fmaxf(hm, __shfl_xor(hm, 32));
+    const float mn = hm > a.m + kTau ? hm : a.m;
+    const float al = __builtin_amdgcn_exp2f(a.m - mn);
+    a.m = mn;
+    a.l *= al;
+    if (qg == 0) rowbuf[col] = al;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float f = rowbuf[4 * qg + i];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) a.O[nb][i] *= f;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  bf16x8_t pf;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const __bf16 pb = static_cast<__bf16>(__builtin_amdgcn_exp2f(s[x][i] - a.m));
+      pf[4 * x + i] = pb;
+      a.l += static_cast<float>(pb);
+    }
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const v4s_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(buf + o.vread[nb][0]));
+    const v4s_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(buf + o.vread[nb][1]));
+    a.O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, join_bf16x4(r0, r1), a.O[nb], 0, 0, 0);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+}  // namespace bf16c
+
 // The unit's partials: per query head g G + h (h < G) of request b, split c,
 // o = v_scale O / l and lse = (m + log2 l) ln 2 (o = 0, lse = -inf where no
 // token was valid).

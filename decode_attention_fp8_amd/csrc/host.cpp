@@ -43,18 +43,12 @@ extern "C" int32_t pkv_suggest_split(const pkv_cache* cache, int32_t num_q_heads
     // longest split that still gives about one unit per compute unit (7/8)
     s = 4096;
     while (s > P && units(s, num_q_heads / 128) < 224) s /= 2;
-  } else if (!latent && cache->dtype == PKV_KV_E4M3 && cache->head_dim_k == 128 &&
-             cache->head_dim_v == 128 && G <= 16) {
-    // MFMA grouped-query kernel: single-wave units, nine per compute unit;
-    // splits of 128 .. 2048 tokens (256 pages at most), the longest giving
-    // 4096 units or more: long units pay their start (three dependent
-    // memory round trips) less often
+  } else if (!latent && cache->head_dim_k == 128 && cache->head_dim_v == 128 && G <= 16) {
+    // MFMA grouped-query kernel (e4m3 or bf16): single-wave units, nine
+    // (five with bf16) per compute unit; splits of 128 .. 2048 tokens (256
+    // pages at most), the longest giving 4096 units or more: long units pay
+    // their start (three dependent memory round trips) less often
     s = std::min<int64_t>(2048, 256 * P);
-    while (s > 128 && units(s, cache->num_kv_heads) < 4096) s /= 2;
-  } else if (!latent && cache->head_dim_k == 128 && cache->head_dim_v == 128 && G == 8) {
-    // grouped-query kernel: single-wave units, two per SIMD; splits of
-    // 128 .. 512 tokens, the longest giving 4096 units or more
-    s = 512;
     while (s > 128 && units(s, cache->num_kv_heads) < 4096) s /= 2;
   } else {
     constexpr int64_t kTargetUnits = 16384;

@@ -191,10 +191,11 @@ def test_ragged_lengths_and_splits(lens, P, split, kv):
     _check_requests(st, range(w.batch))
 
 
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
 @pytest.mark.parametrize("G,dk", [(1, 64), (1, 128), (2, 128), (16, 128), (4, 64)])
-def test_group_sizes_and_head_dims(G, dk):
+def test_group_sizes_and_head_dims(G, dk, kv):
     w = W.custom(f"g{G}", 78, [77, 513], hq=2 * G, hkv=2, dk=dk, dv=dk, page=16)
-    st = State(w, "fp8")
+    st = State(w, kv)
     _check_requests(st, range(w.batch))
 
 
