@@ -1,8 +1,8 @@
 """Throughput of the FP8 paged decode step on one MI355X.
 
 A step is one pass of the whole hot path over a batch of decode requests:
-    pkv_verify -> pkv_append (one new token per request) -> pkv_decode_attn
-    -> pkv_combine
+    pkv_verify_append (the tag check, then one new token per request) ->
+    pkv_decode_attn -> pkv_combine
 captured once as a HIP graph. Before every timed step a 1 GiB buffer is
 written and read back (pkv_fill_u32, pkv_read_u32, outside the graph),
 which evicts the 256 MB last-level cache as the model's other layers would
@@ -160,9 +160,12 @@ class Runner:
         pkv, s = self.pkv, self.step
         abort = None
         if s.verify:
-            pkv.pkv_verify(self.cache, self.bt, self.exp, self.lens, s.abort)
+            # the check and the append of each request's new token, one launch
+            pkv.pkv_verify_append(self.cache, self.bt, self.exp, self.lens, s.abort, self.new_k,
+                                  self.new_v, self.new_slot)
             abort = s.abort
-        pkv.pkv_append(self.cache, self.new_k, self.new_v, self.new_slot, self.new_req, abort)
+        else:
+            pkv.pkv_append(self.cache, self.new_k, self.new_v, self.new_slot)
         if ev is not None:
             ev[0].record()
         pkv.pkv_decode_attn(self.cache, self.q, self.bt, self.lens, s.max_seq_len, abort,

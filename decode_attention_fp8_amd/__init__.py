@@ -18,7 +18,7 @@ from ._binding import (EXPORTS, LIB_PATH, PKV_EHIP, PKV_EINVAL, PKV_EUNSUPPORTED
                        pkv_int4_linear_workspace, int4_workspace,
                        pkv_fill_u32, pkv_read_u32, pkv_requantize_pages, pkv_scales_from_amax,
                        pkv_strerror,
-                       pkv_suggest_split, pkv_verify, pkv_version)
+                       pkv_suggest_split, pkv_verify, pkv_verify_append, pkv_version)
 from .step import DecodeStep, allocate_cache
 
 __all__ = ["EXPORTS", "LIB_PATH", "PKV_EHIP", "PKV_EINVAL", "PKV_EUNSUPPORTED", "PKV_KV_BF16",
@@ -28,4 +28,5 @@ __all__ = ["EXPORTS", "LIB_PATH", "PKV_EHIP", "PKV_EINVAL", "PKV_EUNSUPPORTED", 
            "pkv_int4_linear_workspace", "int4_workspace",
            "pkv_fill_u32", "pkv_read_u32", "pkv_requantize_pages", "pkv_scales_from_amax",
            "pkv_strerror",
-           "pkv_suggest_split", "pkv_verify", "pkv_version", "DecodeStep", "allocate_cache"]
+           "pkv_suggest_split", "pkv_verify", "pkv_verify_append", "pkv_version", "DecodeStep",
+           "allocate_cache"]

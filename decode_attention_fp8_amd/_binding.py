@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(HERE, "libpkv.so")
 PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP = 0, -1, -2, -3
 PKV_KV_E4M3, PKV_KV_BF16 = 1, 2
 
-EXPORTS = ("pkv_scales_from_amax", "pkv_append", "pkv_verify", "pkv_decode_attn",
+EXPORTS = ("pkv_scales_from_amax", "pkv_append", "pkv_verify", "pkv_verify_append",
+           "pkv_decode_attn",
            "pkv_combine", "pkv_decode_attn_drafts", "pkv_requantize_pages", "pkv_int4_linear",
            "pkv_int4_linear_workspace", "pkv_fill_u32", "pkv_read_u32",
            "pkv_decode_attn_static",
@@ -53,6 +54,7 @@ def _load() -> ctypes.CDLL:
         "pkv_scales_from_amax": (I32, [P, I64, I32, I32, I32, P, P]),
         "pkv_append": (I32, [CP, P, P, P, P, P, I64, P]),
         "pkv_verify": (I32, [CP, P, P, P, I32, I32, P, P]),
+        "pkv_verify_append": (I32, [CP, P, P, P, I32, I32, P, P, P, P, P]),
         "pkv_decode_attn": (I32, [CP, P, I32, P, P, I32, I32, I32, P, F, I32, I32, P, P, P]),
         "pkv_combine": (I32, [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P]),
         "pkv_decode_attn_drafts": (I32, [CP, P, I32, I32, P, P, I32, I32, I32, P, F, I32, I32, P,
@@ -308,6 +310,30 @@ def pkv_verify(cache: Cache, block_table: torch.Tensor, expected_tags: torch.Ten
     _check("pkv_verify", _lib.pkv_verify(
         ctypes.byref(cs), _ptr(block_table), _ptr(expected_tags), _ptr(seq_lens), B, max_pages,
         _ptr(abort_out), _stream(stream)))
+
+
+def pkv_verify_append(cache: Cache, block_table: torch.Tensor, expected_tags: torch.Tensor,
+                      seq_lens: torch.Tensor, abort_out: torch.Tensor, k_new: torch.Tensor,
+                      v_new: torch.Tensor | None, slot: torch.Tensor, stream=None) -> None:
+    """The tag check and the append of one new token per request (k_new[b]
+    of request b, at slot[b]) in one launch; an aborted request writes
+    nothing."""
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    _need(abort_out, torch.uint8, "abort_out")
+    _need(slot, torch.int32, "slot")
+    _need(k_new, torch.bfloat16, "k_new")
+    if v_new is not None:
+        _need(v_new, torch.bfloat16, "v_new")
+    if expected_tags.element_size() != 4:
+        raise ValueError("expected_tags are 32-bit")
+    B, max_pages = block_table.shape
+    if k_new.shape[0] != B or slot.numel() != B:
+        raise ValueError("one new token per request")
+    cs = cache.struct()
+    _check("pkv_verify_append", _lib.pkv_verify_append(
+        ctypes.byref(cs), _ptr(block_table), _ptr(expected_tags), _ptr(seq_lens), B, max_pages,
+        _ptr(abort_out), _ptr(k_new), _ptr(v_new), _ptr(slot), _stream(stream)))
 
 
 def pkv_decode_attn(cache: Cache, q: torch.Tensor, block_table: torch.Tensor,

@@ -26,17 +26,6 @@ struct AppendArgs {
   int pool_dim;         // row length in the pool (>= dim; latent rows)
 };
 
-__device__ __forceinline__ float abs_max16(const uint4& w0, const uint4& w1) {
-  const uint32_t u[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-  float m = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    m = fmaxf(m, fabsf(__uint_as_float(u[j] << 16)));
-    m = fmaxf(m, fabsf(__uint_as_float(u[j] & 0xFFFF0000u)));
-  }
-  return m;
-}
-
 template <bool kE4M3, bool kRows>
 __global__ void __launch_bounds__(256) append_kernel(AppendArgs a, const int32_t* __restrict__ slot,
                                                      const int32_t* __restrict__ token_req,
@@ -66,7 +55,7 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a, const int32_t
       if constexpr (kRows) {
         // the row's lanes are aligned groups of `chunks` lanes, all active
         // or all skipped together
-        float m = abs_max16(w0, w1);
+        float m = pkv::abs_max16(w0, w1);
         for (int off = 1; off < chunks; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
         scale = m == 0.0f ? 1.0f : __fdiv_rn(m, 448.0f);
         if (c == 0) a.row_scale[(page * heads + h) * page_size + row] = scale;
@@ -94,12 +83,6 @@ int launch(const AppendArgs& a, const int32_t* slot, const int32_t* token_req,
   return pkv::launch_status();
 }
 
-// rows of dim / 16 threads must tile the 64 lanes of a wave
-bool row_lanes_ok(int dim) {
-  const int chunks = dim / 16;
-  return chunks >= 1 && chunks <= 64 && (chunks & (chunks - 1)) == 0;
-}
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
@@ -118,7 +101,7 @@ extern "C" int pkv_append(const pkv_cache* cache, const void* k_new, const void*
   const bool e4m3 = cache->dtype == PKV_KV_E4M3;
   const int64_t n_slots = static_cast<int64_t>(cache->num_pages) * cache->page_size;
   if (cache->k_row_scale) {
-    if (!row_lanes_ok(cache->head_dim_k) || !row_lanes_ok(cache->head_dim_v))
+    if (!pkv::row_lanes_ok(cache->head_dim_k) || !pkv::row_lanes_ok(cache->head_dim_v))
       return PKV_EUNSUPPORTED;
     AppendArgs k{static_cast<const uint16_t*>(k_new), static_cast<uint8_t*>(cache->k_pool),
                  nullptr, cache->k_row_scale, cache->head_dim_k, cache->head_dim_k};

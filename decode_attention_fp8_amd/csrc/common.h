@@ -37,9 +37,29 @@ inline int launch_status() {
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Scales set at append: the dim / 16 threads of a row must tile the 64 lanes
+// of a wave (a power of two at most 64).
+inline bool row_lanes_ok(int dim) {
+  const int chunks = dim / 16;
+  return chunks >= 1 && chunks <= 64 && (chunks & (chunks - 1)) == 0;
+}
+
 // -------------------------------------------------------------- device side
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Largest magnitude of 16 bf16 values (two 16-byte words); fmaxf leaves
+// NaNs out.
+__device__ __forceinline__ float abs_max16(const uint4& w0, const uint4& w1) {
+  const uint32_t u[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    m = fmaxf(m, fabsf(__uint_as_float(u[j] << 16)));
+    m = fmaxf(m, fabsf(__uint_as_float(u[j] & 0xFFFF0000u)));
+  }
+  return m;
 }
 
 // float32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.

@@ -77,8 +77,8 @@ __global__ void __launch_bounds__(64 * W) decode_drafts_kernel(DecodeParams p, i
   const int col = lane & 31, hl = lane >> 5;
   const int parts = (row_groups + W - 1) / W;
   const int rg = (static_cast<int>(blockIdx.x) % parts) * W + wv;
-  int b, g, c, L, len;
-  if (!pkv::find_unit(p, static_cast<int>(blockIdx.x) / parts, b, g, c, L, len)) return;
+  int b, g, c, L;
+  if (!pkv::find_unit(p, static_cast<int>(blockIdx.x) / parts, b, g, c, L)) return;
   const int G = p.num_q_heads / p.num_kv_heads;
   const int T = p.q_len;
   const int rows = T * G;
@@ -121,12 +121,9 @@ __global__ void __launch_bounds__(64 * W) decode_drafts_kernel(DecodeParams p, i
   const int n_pages = (t_end - t_begin + P - 1) >> log2P;
   int pg = -1;
   if (lane < n_pages) pg = bt[first_page + lane];
-  // the launch's footprint, summed while the loads above are in flight
-  const int64_t tokens = p.batch <= 64 ? pkv::wave_sum(len) : pkv::launch_tokens(p);
-  const bool stream = pkv::stream_cache(tokens * p.num_kv_heads * 2 * kD);
 #pragma unroll
   for (int s = 0; s < 8; ++s) asm volatile("" : : "v"(qf[s]));
-  asm volatile("" : : "v"(qk_scale), "v"(o_scale), "v"(pg), "s"(static_cast<int>(stream)));
+  asm volatile("" : : "v"(qk_scale), "v"(o_scale), "v"(pg));
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" : : : "memory");
   const bool pg_ok = pg >= 0 && pg < p.num_pages;
   const uint64_t valid = __ballot(pg_ok);
@@ -171,14 +168,8 @@ __global__ void __launch_bounds__(64 * W) decode_drafts_kernel(DecodeParams p, i
       src[i] = kind == 0 ? koff0 : (kind == 1 ? koff1 : (kind == 2 ? voff0 : voff1));
       from[i] = (kind < 2 ? kpool : vpool) + group_base(gg);
     }
-    // one branch per tile selects the load form
-    if (stream) {
 #pragma unroll
-      for (int i = 0; i < kMine; ++i) dma16_stream(dst[i], src[i], from[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kMine; ++i) dma16(dst[i], src[i], from[i]);
-    }
+    for (int i = 0; i < kMine; ++i) dma16_stream(dst[i], src[i], from[i]);
   };
 
   // per-lane LDS offsets. K operand, chunk 2kp + h of token row col.

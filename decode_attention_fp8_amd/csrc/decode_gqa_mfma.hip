@@ -53,8 +53,8 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
   __shared__ float rowbuf[kRows];
   const int lane = threadIdx.x;
   const int col = lane & 15, qg = lane >> 4;
-  int b, g, c, L, len;
-  if (!pkv::find_unit(p, static_cast<int>(blockIdx.x), b, g, c, L, len)) return;
+  int b, g, c, L;
+  if (!pkv::find_unit(p, static_cast<int>(blockIdx.x), b, g, c, L)) return;
   const int G = p.num_q_heads / p.num_kv_heads;
   const int t_begin = c * p.split_tokens;
   const int t_end = min(L, t_begin + p.split_tokens);
@@ -94,15 +94,10 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
     return 64 * h + lane < n_pages ? bt[first_page + 64 * h + lane] : -1;
   };
   const int pg0 = load_page(0), pg1 = load_page(1), pg2 = load_page(2), pg3 = load_page(3);
-  // the launch's footprint (codes, plus the row scales when set at append),
-  // summed while the loads above are in flight
-  const int64_t tokens = p.batch <= 64 ? pkv::wave_sum(len) : pkv::launch_tokens(p);
-  const bool stream =
-      pkv::stream_cache(tokens * p.num_kv_heads * (2 * kD * kElem + (kRowScales ? 8 : 0)));
 #pragma unroll
   for (int s = 0; s < 4; ++s) asm volatile("" : : "v"(qf[s]));
   asm volatile("" : : "v"(pg0), "v"(pg1), "v"(pg2), "v"(pg3));
-  asm volatile("" : : "v"(qk_scale), "v"(o_scale), "s"(static_cast<int>(stream)));
+  asm volatile("" : : "v"(qk_scale), "v"(o_scale));
   // from here on the only vector memory loads in flight are the ring's
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" : : : "memory");
   auto page_ok_lane = [&](int pg) __attribute__((always_inline)) {
@@ -156,9 +151,9 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
       const int gg = (t_begin + kTile * t + 16 * x < t_end) ? 2 * t + x : 2 * t;
       offs[x] = group_base(gg);
       if constexpr (kBf16) {
-        bf16c::dma_group(slot, x, lo, kpool + offs[x], vpool + offs[x], stream);
+        bf16c::dma_group(slot, x, lo, kpool + offs[x], vpool + offs[x]);
       } else {
-        dma_group(slot, x, lo, kpool + offs[x], vpool + offs[x], stream);
+        dma_group(slot, x, lo, kpool + offs[x], vpool + offs[x]);
       }
     }
     if constexpr (kRowScales) {
@@ -168,13 +163,8 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
                           4u * (lane & 15);
       const uint8_t* ks = reinterpret_cast<const uint8_t*>(p.k_row_scale);
       const uint8_t* vs = reinterpret_cast<const uint8_t*>(p.v_row_scale);
-      if (stream) {
-        dma4_stream(slot + kTileBytes, so, ks);
-        dma4_stream(slot + kTileBytes + 256, so, vs);
-      } else {
-        dma4(slot + kTileBytes, so, ks);
-        dma4(slot + kTileBytes + 256, so, vs);
-      }
+      dma4_stream(slot + kTileBytes, so, ks);
+      dma4_stream(slot + kTileBytes + 256, so, vs);
     }
   };
 

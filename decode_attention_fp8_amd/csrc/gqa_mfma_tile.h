@@ -100,22 +100,16 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
   return o;
 }
 
-// DMA of one 16-token group (K and V, 2 KB each) into half x of a slot;
-// `stream` (wave-uniform) selects the non-temporal form.
+// DMA of one 16-token group (K and V, 2 KB each) into half x of a slot, in
+// the non-temporal form: a step reads each cache byte once, and the next
+// step of the same layer comes after the model's other layers, so keeping
+// the lines would only evict others.
 __device__ __forceinline__ void dma_group(uint32_t slot, int x, const LaneOffsets& o,
-                                          const uint8_t* kgroup, const uint8_t* vgroup,
-                                          bool stream) {
-  if (stream) {
-    dma16_stream(slot + 2048 * x, o.kdma0, kgroup);
-    dma16_stream(slot + 2048 * x + 1024, o.kdma1, kgroup);
-    dma16_stream(slot + kHalf + 2048 * x, o.vdma[x][0], vgroup);
-    dma16_stream(slot + kHalf + 2048 * x + 1024, o.vdma[x][1], vgroup);
-  } else {
-    dma16(slot + 2048 * x, o.kdma0, kgroup);
-    dma16(slot + 2048 * x + 1024, o.kdma1, kgroup);
-    dma16(slot + kHalf + 2048 * x, o.vdma[x][0], vgroup);
-    dma16(slot + kHalf + 2048 * x + 1024, o.vdma[x][1], vgroup);
-  }
+                                          const uint8_t* kgroup, const uint8_t* vgroup) {
+  dma16_stream(slot + 2048 * x, o.kdma0, kgroup);
+  dma16_stream(slot + 2048 * x + 1024, o.kdma1, kgroup);
+  dma16_stream(slot + kHalf + 2048 * x, o.vdma[x][0], vgroup);
+  dma16_stream(slot + kHalf + 2048 * x + 1024, o.vdma[x][1], vgroup);
 }
 
 struct Acc {
@@ -354,18 +348,13 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
 }
 
 // DMA of one 16-token group (K and V, 4 KB each) into half x of a slot
+// (non-temporal, as above)
 __device__ __forceinline__ void dma_group(uint32_t slot, int x, const LaneOffsets& o,
-                                          const uint8_t* kgroup, const uint8_t* vgroup,
-                                          bool stream) {
+                                          const uint8_t* kgroup, const uint8_t* vgroup) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (stream) {
-      dma16_stream(slot + 4096 * x + 1024 * i, o.kdma[i], kgroup);
-      dma16_stream(slot + kHalf + 4096 * x + 1024 * i, o.vdma[i], vgroup);
-    } else {
-      dma16(slot + 4096 * x + 1024 * i, o.kdma[i], kgroup);
-      dma16(slot + kHalf + 4096 * x + 1024 * i, o.vdma[i], vgroup);
-    }
+    dma16_stream(slot + 4096 * x + 1024 * i, o.kdma[i], kgroup);
+    dma16_stream(slot + kHalf + 4096 * x + 1024 * i, o.vdma[i], vgroup);
   }
 }
 

@@ -21,14 +21,14 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
 
-__global__ void __launch_bounds__(kThreads) verify_kernel(const uint32_t* __restrict__ page_tags,
-                                                          int32_t num_pages, int32_t page_size,
-                                                          const int32_t* __restrict__ block_table,
-                                                          const uint32_t* __restrict__ expected,
-                                                          const int32_t* __restrict__ seq_lens,
-                                                          int32_t max_pages,
-                                                          uint8_t* __restrict__ abort_out) {
-  const int b = blockIdx.x;
+// The check of request b by one workgroup: nonzero (the same in every
+// thread) if the request must be aborted.
+__device__ __forceinline__ int check_request(const uint32_t* __restrict__ page_tags,
+                                             int32_t num_pages, int32_t page_size,
+                                             const int32_t* __restrict__ block_table,
+                                             const uint32_t* __restrict__ expected,
+                                             const int32_t* __restrict__ seq_lens,
+                                             int32_t max_pages, int b) {
   const int tid = threadIdx.x;
   const int32_t L = seq_lens[b];
   const int64_t need = L > 0 ? (static_cast<int64_t>(L) + page_size - 1) / page_size : 0;
@@ -60,8 +60,88 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(const uint32_t* __rest
       }
     }
   }
-  bad = __syncthreads_or(bad);
-  if (tid == 0) abort_out[b] = bad ? 1 : 0;
+  return __syncthreads_or(bad);
+}
+
+__global__ void __launch_bounds__(kThreads) verify_kernel(const uint32_t* __restrict__ page_tags,
+                                                          int32_t num_pages, int32_t page_size,
+                                                          const int32_t* __restrict__ block_table,
+                                                          const uint32_t* __restrict__ expected,
+                                                          const int32_t* __restrict__ seq_lens,
+                                                          int32_t max_pages,
+                                                          uint8_t* __restrict__ abort_out) {
+  const int b = blockIdx.x;
+  const int bad = check_request(page_tags, num_pages, page_size, block_table, expected, seq_lens,
+                                max_pages, b);
+  if (threadIdx.x == 0) abort_out[b] = bad ? 1 : 0;
+}
+
+// The rows of one new token for one pool (K or V): heads x dim / 16 chunks of
+// 16 values, chunk i taken by thread i (i < 256 per round). With scales set
+// at append, a row's dim / 16 threads are consecutive lanes of one wave (a
+// power of two, aligned) and share the row's largest magnitude by shuffles.
+template <bool kE4M3, bool kRows>
+__device__ __forceinline__ void append_token(const uint16_t* __restrict__ src, uint8_t* pool,
+                                             const float* scale, float* row_scale, int heads,
+                                             int dim, int pool_dim, int page_size, int64_t page,
+                                             int row) {
+  const int chunks = dim / 16;
+  const int total = heads * chunks;
+  for (int i = threadIdx.x; i < total; i += kThreads) {
+    const int h = i / chunks;
+    const int c = i - h * chunks;
+    const uint4 w0 = *reinterpret_cast<const uint4*>(src + h * dim + c * 16);
+    const uint4 w1 = *reinterpret_cast<const uint4*>(src + h * dim + c * 16 + 8);
+    const int64_t dst = ((page * heads + h) * page_size + row) * pool_dim + c * 16;
+    if constexpr (kE4M3) {
+      float s;
+      if constexpr (kRows) {
+        float m = pkv::abs_max16(w0, w1);
+        for (int off = 1; off < chunks; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+        s = m == 0.0f ? 1.0f : __fdiv_rn(m, 448.0f);
+        if (c == 0) row_scale[(page * heads + h) * page_size + row] = s;
+      } else {
+        s = scale[h];
+      }
+      *reinterpret_cast<uint4*>(pool + dst) = pkv::encode16(w0, w1, s);
+    } else {
+      uint4* d = reinterpret_cast<uint4*>(pool + dst * 2);
+      d[0] = w0;
+      d[1] = w1;
+    }
+  }
+}
+
+struct Pool {
+  uint8_t* pool;
+  const float* scale;
+  float* row_scale;
+  int dim, pool_dim;
+};
+
+// pkv_verify_append: workgroup b checks request b, writes its flag and, if
+// the request stands, appends its new token (K then V rows) at slot[b].
+template <bool kE4M3, bool kRows>
+__global__ void __launch_bounds__(kThreads) verify_append_kernel(
+    const uint32_t* __restrict__ page_tags, int32_t num_pages, int32_t page_size,
+    const int32_t* __restrict__ block_table, const uint32_t* __restrict__ expected,
+    const int32_t* __restrict__ seq_lens, int32_t max_pages, uint8_t* __restrict__ abort_out,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ slot, Pool kp, Pool vp, int heads, int64_t n_slots) {
+  const int b = blockIdx.x;
+  const int bad = check_request(page_tags, num_pages, page_size, block_table, expected, seq_lens,
+                                max_pages, b);
+  if (threadIdx.x == 0) abort_out[b] = bad ? 1 : 0;
+  const int32_t s = slot[b];
+  if (bad || s < 0 || s >= n_slots) return;
+  const int64_t page = s / page_size;
+  const int row = s - static_cast<int>(page) * page_size;
+  append_token<kE4M3, kRows>(k_new + static_cast<int64_t>(b) * heads * kp.dim, kp.pool, kp.scale,
+                             kp.row_scale, heads, kp.dim, kp.pool_dim, page_size, page, row);
+  if (v_new)
+    append_token<kE4M3, kRows>(v_new + static_cast<int64_t>(b) * heads * vp.dim, vp.pool,
+                               vp.scale, vp.row_scale, heads, vp.dim, vp.pool_dim, page_size,
+                               page, row);
 }
 
 }  // namespace
@@ -78,5 +158,49 @@ extern "C" int pkv_verify(const pkv_cache* cache, const int32_t* block_table,
   verify_kernel<<<batch, kThreads, 0, stream>>>(cache->page_tags, cache->num_pages,
                                                 cache->page_size, block_table, expected_tags,
                                                 seq_lens, max_pages, abort_out);
+  return pkv::launch_status();
+}
+
+extern "C" int pkv_verify_append(const pkv_cache* cache, const int32_t* block_table,
+                                 const uint32_t* expected_tags, const int32_t* seq_lens,
+                                 int32_t batch, int32_t max_pages, uint8_t* abort_out,
+                                 const void* k_new, const void* v_new, const int32_t* slot,
+                                 hipStream_t stream) {
+  int st = pkv::check_cache(cache);
+  if (st) return st;
+  if (!cache->page_tags) return PKV_EINVAL;
+  if (!block_table || !expected_tags || !seq_lens || !abort_out || batch < 0 || max_pages < 1)
+    return PKV_EINVAL;
+  const bool latent = cache->v_pool == nullptr;
+  if (!k_new || !slot || (latent && v_new) || (!latent && !v_new)) return PKV_EINVAL;
+  auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
+  if (misaligned(k_new) || (v_new && misaligned(v_new)) || misaligned(cache->k_pool) ||
+      (cache->v_pool && misaligned(cache->v_pool)))
+    return PKV_EINVAL;
+  const bool rows = cache->k_row_scale != nullptr;
+  if (rows && (!pkv::row_lanes_ok(cache->head_dim_k) || !pkv::row_lanes_ok(cache->head_dim_v)))
+    return PKV_EUNSUPPORTED;
+  if (batch == 0) return PKV_OK;
+  const int64_t n_slots = static_cast<int64_t>(cache->num_pages) * cache->page_size;
+  const Pool kp{static_cast<uint8_t*>(cache->k_pool), cache->k_scale, cache->k_row_scale,
+                cache->head_dim_k, cache->head_dim_k};
+  const Pool vp{static_cast<uint8_t*>(cache->v_pool), cache->v_scale, cache->v_row_scale,
+                cache->head_dim_v, cache->head_dim_v};
+  const auto* kn = static_cast<const uint16_t*>(k_new);
+  const auto* vn = static_cast<const uint16_t*>(v_new);
+  const auto* tags = cache->page_tags;
+  if (cache->dtype == PKV_KV_BF16) {
+    verify_append_kernel<false, false><<<batch, kThreads, 0, stream>>>(
+        tags, cache->num_pages, cache->page_size, block_table, expected_tags, seq_lens, max_pages,
+        abort_out, kn, vn, slot, kp, vp, cache->num_kv_heads, n_slots);
+  } else if (rows) {
+    verify_append_kernel<true, true><<<batch, kThreads, 0, stream>>>(
+        tags, cache->num_pages, cache->page_size, block_table, expected_tags, seq_lens, max_pages,
+        abort_out, kn, vn, slot, kp, vp, cache->num_kv_heads, n_slots);
+  } else {
+    verify_append_kernel<true, false><<<batch, kThreads, 0, stream>>>(
+        tags, cache->num_pages, cache->page_size, block_table, expected_tags, seq_lens, max_pages,
+        abort_out, kn, vn, slot, kp, vp, cache->num_kv_heads, n_slots);
+  }
   return pkv::launch_status();
 }

@@ -5,13 +5,15 @@ allocates); every computation is a libpkv launch on the current stream, in
 the order the integrity rule needs ("Smaller, faster, safer", section
 "Protecting a shared KV cache": the mapping is checked before decode reads):
     pkv_verify -> pkv_append -> pkv_decode_attn -> pkv_combine
+with the first two as one launch (pkv_verify_append) when each request
+appends one token.
 """
 from __future__ import annotations
 
 import torch
 
 from ._binding import (Cache, pkv_append, pkv_combine, pkv_decode_attn, pkv_suggest_split,
-                       pkv_verify)
+                       pkv_verify, pkv_verify_append)
 
 E4M3_NAN = 0x7F
 BF16_NAN = 0x7FC0
@@ -74,10 +76,18 @@ class DecodeStep:
 
     def run(self, q, block_table, expected_tags, seq_lens, sm_scale, k_new=None, v_new=None,
             slot=None, token_req=None):
+        """One step. New tokens k_new[i] (v_new[i]) go to slot[i] for request
+        token_req[i]; token_req None means one token per request, token b of
+        request b, and then the check and the append are one launch."""
         c = self.cache
         abort = None
         if self.verify:
-            pkv_verify(c, block_table, expected_tags, seq_lens, self.abort)
+            if k_new is not None and token_req is None:
+                pkv_verify_append(c, block_table, expected_tags, seq_lens, self.abort, k_new,
+                                  v_new, slot)
+                k_new = None
+            else:
+                pkv_verify(c, block_table, expected_tags, seq_lens, self.abort)
             abort = self.abort
         if k_new is not None:
             pkv_append(c, k_new, v_new, slot, token_req, abort)

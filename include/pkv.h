@@ -167,6 +167,29 @@ int pkv_verify(const pkv_cache* cache, const int32_t* block_table,
                hipStream_t stream);
 
 /*
+ * pkv_verify and then pkv_append of one new token per request, in one launch
+ * (sections "Protecting a shared KV cache" and "Quantizing the KV cache":
+ * the mapping is checked before anything reads or writes the request's
+ * pages; an aborted request writes nothing).
+ *
+ * For each request b < batch: abort_out[b] as pkv_verify computes it; then,
+ * unless abort_out[b] is set or slot[b] < 0 (or past the pool), the rows
+ * k_new[b] (and v_new[b]) are written at slot[b] exactly as pkv_append
+ * writes them (static scales, scales set at append, or a bf16 copy).
+ *   k_new: bf16 [batch][num_kv_heads][head_dim_k]; v_new: bf16
+ *          [batch][num_kv_heads][head_dim_v], NULL for the latent layout
+ *   slot:  int32 [batch]
+ *   other arguments as for pkv_verify.
+ * One workgroup per request: a request's flag and its append are in the
+ * same workgroup, so no other ordering is needed. Two requests with the same
+ * slot race. Errors as for pkv_verify and pkv_append.
+ */
+int pkv_verify_append(const pkv_cache* cache, const int32_t* block_table,
+                      const uint32_t* expected_tags, const int32_t* seq_lens, int32_t batch,
+                      int32_t max_pages, uint8_t* abort_out, const void* k_new,
+                      const void* v_new, const int32_t* slot, hipStream_t stream);
+
+/*
  * Split-KV paged decode attention (section "Quantizing the KV cache": the
  * FP8 kernel converts values as it reads them; section "Protecting a shared
  * KV cache": paged attention over a shared physical cache).

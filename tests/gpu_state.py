@@ -50,9 +50,12 @@ class State:
         self.new_slot = self.slot[last].contiguous()
         self.new_req = torch.arange(w.batch, dtype=torch.int32, device=device)
 
-    def run(self):
+    def run(self, fused: bool = True):
+        """The step; fused: the check and the append in one launch
+        (pkv_verify_append), else the two separate calls."""
         out = self.step.run(self.q, self.block_table, self.expected, self.seq_lens,
-                            self.w.sm_scale, self.new_k, self.new_v, self.new_slot, self.new_req)
+                            self.w.sm_scale, self.new_k, self.new_v, self.new_slot,
+                            None if fused else self.new_req)
         torch.cuda.synchronize()
         return out
 

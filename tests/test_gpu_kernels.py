@@ -214,3 +214,49 @@ def test_verify_long_rows_across_rounds():
     ref = verify.verify(tags, bt, exp, lens, P)
     assert ref.tolist() == [1] * 6 + [0, 1, 1]
     assert np.array_equal(_gpu_flags(w, bt, exp, tags), ref)
+
+
+# ------------------------------------------------- check and append in one launch
+def _pools(c):
+    out = [c.k_pool.view(torch.uint8).clone()]
+    if c.v_pool is not None:
+        out.append(c.v_pool.view(torch.uint8).clone())
+    if c.k_row_scale is not None:
+        out += [c.k_row_scale.clone(), c.v_row_scale.clone()]
+    return out
+
+
+@pytest.mark.parametrize("kv,rows,latent", [("fp8", False, False), ("bf16", False, False),
+                                             ("fp8", True, False), ("fp8", False, True),
+                                             ("bf16", False, True)])
+def test_verify_append_equals_verify_then_append(kv, rows, latent):
+    """pkv_verify_append gives the flags of pkv_verify and the pools of
+    pkv_append with each request's token and the flags, byte for byte:
+    aborted requests (reallocated pages) write nothing, a negative slot
+    writes nothing."""
+    dk, dv = (576, 512) if latent else (128, 128)
+    w = W.custom(f"va_{kv}_{rows}_{latent}", 95, [300, 17, 1000, 64, 2048, 5], hq=128 if latent else 16,
+                 hkv=1 if latent else 2, dk=dk, dv=dv, page=64 if latent else 16, latent=latent,
+                 n_realloc=2, sm_scale=1 / 24 if latent else None)
+    flags = step.flags(w)
+    assert flags.any() and not flags.all()
+    a = State(w, kv, row_scales=rows)
+    b = State(w, kv, row_scales=rows)
+    slot = a.new_slot.clone()
+    slot[3] = -1
+    # new rows that differ from what the bulk fill wrote there
+    k_new = torch.flip(a.new_k, dims=[0]).contiguous()
+    v_new = None if latent else torch.flip(a.new_v, dims=[0]).contiguous()
+    ab_a = torch.full((w.batch,), 7, dtype=torch.uint8, device=dev)
+    ab_b = torch.full((w.batch,), 7, dtype=torch.uint8, device=dev)
+    pkv.pkv_verify_append(a.cache, a.block_table, a.expected, a.seq_lens, ab_a, k_new, v_new, slot)
+    pkv.pkv_verify(b.cache, b.block_table, b.expected, b.seq_lens, ab_b)
+    pkv.pkv_append(b.cache, k_new, v_new, slot, b.new_req, ab_b)
+    torch.cuda.synchronize()
+    assert np.array_equal(ab_a.cpu().numpy(), flags) and torch.equal(ab_a, ab_b)
+    for x, y in zip(_pools(a.cache), _pools(b.cache)):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+    # and the step through the fused call decodes as the separate calls do
+    oa = a.run(fused=True).clone()
+    ob = b.run(fused=False).clone()
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
