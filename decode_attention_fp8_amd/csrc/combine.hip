@@ -13,11 +13,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // One workgroup of 256 threads per (request, query head). The maximum lse is
-// reduced over the workgroup; then the threads split into P = 256 / (Dv / 4)
-// groups, group sg merging splits sg, sg + P, ... with each thread owning
-// one 16-byte chunk of the head, so a workgroup reads P whole split rows per
-// step and consecutive steps' loads are independent. The P partial sums meet
-// in LDS.
+// reduced over the workgroup. Then, 256 split rows at a time, the rows that
+// hold tokens (lse > -inf; the latent kernel leaves the other rows of a run
+// of splits it merged empty) are listed in LDS in split order, with their
+// weights, and the threads split into P = 256 / (Dv / 4) groups: group sg
+// merges listed rows sg, sg + P, ... with each thread owning one 16-byte
+// chunk of the head, so a workgroup reads P whole split rows per step and
+// consecutive steps' loads are independent. The P partial sums meet in LDS.
+// The order of every sum is fixed, so the result is the same bits on every
+// run.
 template <int DV>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
@@ -43,25 +47,16 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   const float4* op = reinterpret_cast<const float4*>(o_part + bh * max_splits * DV);
 
   __shared__ float red[4];
+  __shared__ int cnt_s[4];
+  __shared__ int idx_s[256];
+  __shared__ float w_s[256];
   __shared__ float den_s[kP];
   __shared__ float4 acc_s[kP][kC];
 
-  // this thread's first two split rows load now, independent of the max
-  // they are weighted by, so their latency overlaps the max's
-  const int c0 = sg, c1 = sg + kP;
-  float4 v0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), v1 = v0;
-  float l0 = -INFINITY, l1 = -INFINITY;
-  if (c0 < n) {
-    v0 = op[static_cast<int64_t>(c0) * kC + ch];
-    l0 = lse[c0];
-  }
-  if (c1 < n) {
-    v1 = op[static_cast<int64_t>(c1) * kC + ch];
-    l1 = lse[c1];
-  }
-
-  float mx = -INFINITY;
-  for (int c = t; c < n; c += 256) mx = fmaxf(mx, lse[c]);
+  // the first 256 rows' lse, kept for the listing below
+  const float lse0 = t < n ? lse[t] : -INFINITY;
+  float mx = lse0;
+  for (int c = t + 256; c < n; c += 256) mx = fmaxf(mx, lse[c]);
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if (lane == 0) red[wave] = mx;
   __syncthreads();
@@ -71,31 +66,36 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float den = 0.0f;
   if (!empty) {
-    if (c0 < n) {
-      const float w = exp2f((l0 - M) * kLog2e);
-      den += w;
-      acc.x += w * v0.x;
-      acc.y += w * v0.y;
-      acc.z += w * v0.z;
-      acc.w += w * v0.w;
-    }
-    if (c1 < n) {
-      const float w = exp2f((l1 - M) * kLog2e);
-      den += w;
-      acc.x += w * v1.x;
-      acc.y += w * v1.y;
-      acc.z += w * v1.z;
-      acc.w += w * v1.w;
-    }
+    for (int base = 0; base < n; base += 256) {
+      const int c = base + t;
+      const float lc = base == 0 ? lse0 : (c < n ? lse[c] : -INFINITY);
+      const bool used = lc != -INFINITY;
+      const uint64_t bal = __ballot(used);
+      const int before = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) cnt_s[wave] = __popcll(bal);
+      __syncthreads();
+      int pos = before, listed = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        pos += w < wave ? cnt_s[w] : 0;
+        listed += cnt_s[w];
+      }
+      if (used) {
+        idx_s[pos] = c;
+        w_s[pos] = exp2f((lc - M) * kLog2e);
+      }
+      __syncthreads();
 #pragma unroll 4
-    for (int c = sg + 2 * kP; c < n; c += kP) {
-      const float w = exp2f((lse[c] - M) * kLog2e);
-      const float4 v = op[static_cast<int64_t>(c) * kC + ch];
-      den += w;
-      acc.x += w * v.x;
-      acc.y += w * v.y;
-      acc.z += w * v.z;
-      acc.w += w * v.w;
+      for (int k = sg; k < listed; k += kP) {
+        const float w = w_s[k];
+        const float4 v = op[static_cast<int64_t>(idx_s[k]) * kC + ch];
+        den += w;
+        acc.x += w * v.x;
+        acc.y += w * v.y;
+        acc.z += w * v.z;
+        acc.w += w * v.w;
+      }
+      __syncthreads();  // the list is read before the next round writes it
     }
   }
   acc_s[sg][ch] = acc;

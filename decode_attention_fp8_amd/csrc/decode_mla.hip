@@ -397,300 +397,592 @@ __global__ void __launch_bounds__(256) decode_mla_kernel(DecodeParams p, int n_s
 }
 
 // ---------------------------------------------------------------------------
-// Wide variant for an e4m3 cache and query heads in multiples of 128: one
-// workgroup of 4 waves takes all 128 heads of a (request, split), each wave
-// 32 heads, so every cached byte is converted and read from LDS by 4 waves
-// instead of 8. MFMA 32x32x16 (bf16 in, fp32 out):
+// Wide variant for query heads in multiples of 128, e4m3 or bf16 cache: one
+// workgroup of 4 waves takes all 128 heads of a range of splits. MFMA
+// 32x32x16 (bf16 in, fp32 out):
 //   A lane l: row l%32, k 8(l/32)..+7;  B lane l: column l%32, k 8(l/32)..+7;
 //   D lane l, element i: row 8(i/4) + 4(l/32) + i%4, column l%32.
-// S^T = K Q^T per 32-token block (M = tokens, N = the wave's 32 heads, 36
-// k-steps of 16 dims), so a lane holds the scores of one head (l%32) for
-// tokens {8u + 4(l/32) + r}; those are exactly the A operand of P V (M =
-// heads, k = tokens) when the V operand is read in the same token order with
-// ds_read_tr8_b64. The 32 x 512 accumulators of a wave live in the
-// accumulation registers.
+// The cache is taken 32 tokens (half a tile) at a time. QK^T: wave w holds
+// q of heads 32 w .. 32 w + 31 in registers and forms S^T = K Q^T for them
+// (M = tokens, N = heads, 36 k-steps of 16 dims); its softmax numerators go
+// to LDS as bf16 (row = head, 32 tokens). P V: after a barrier, wave w
+// multiplies all 128 heads' numerators (A, read back from LDS) by dims 128 w
+// .. 128 w + 127 of V (B, read with ds_read_b64_tr_b16), so every V byte in
+// LDS is read once per workgroup instead of once per wave; its 128 x 128
+// accumulators live in the accumulation registers. One accumulator per
+// 32-token block of S^T suffices: dependent MFMAs issue back to back.
 //
-// Tile layout in LDS: 16-byte chunk c of row r at position c ^ ((r >> 2) & 3)
-// of the row, which puts any 16 consecutive rows of one chunk (K operand
-// reads) and the 8 rows x 2 half-chunks of a transposing V read on distinct
-// bank groups. The ring holds 4 tiles; tile t + 3 is loaded into the buffer
-// of tile t - 1 right after the barrier that opens tile t, so one barrier per
-// tile suffices.
+// Every MFMA reads bf16 operands from a bf16 copy of 32 rows in LDS. An e4m3
+// tile arrives by direct-to-LDS loads into one of two code slots (the next
+// tile loads while one is used) and each half is converted once, by all
+// four waves together, into one of two bf16 buffers: the conversion of half
+// u + 1 is interleaved with the MFMAs of half u's P V (a step after every
+// third MFMA), so it costs issue slots the MFMAs leave free. A bf16 cache
+// arrives straight in a four-slot ring of bf16 halves (three halves load
+// while one is used), already in the layout the operands are read in. The
+// cache loads of a later half or tile are spread over the MFMAs of a QK^T.
 //
-// Work unit order: blockIdx.y counts splits from the end of each request
-// downwards (the first units dispatched are the ones far from the end,
-// which are full), so the short last splits run last and fill the tail;
-// the request index is rotated by blockIdx.y so that one request's units
-// spread over all XCDs.
+// bf16 half layout (32 rows of 72 chunks of 16 bytes): nine 4 KB groups,
+// group g holding chunks 8 g .. 8 g + 7 of every row, row r at 128 r of the
+// group and chunk c at position (c % 8) ^ swz(r) of those 128 bytes, swz(r)
+// = bit 1 | bit 2 << 1 | (bit 1 ^ bit 3) << 2 of r. The bank group (of 16
+// four-bank groups) of position p in row r is then 8 (r & 1) + p; with this
+// swizzle the 16 rows of one pass of a K operand read (16 consecutive rows,
+// one chunk), the 4 rows x 4 chunks of one pass of a transposing V read and
+// the 2 rows x 8 chunks of one pass of the e4m3 conversion's writes all fall
+// on distinct bank groups (checked exhaustively). Every lane's offsets are a
+// fixed base plus immediates: a cache load fills 1 KB of a group (8 rows x
+// 128 bytes of the page), an operand read steps 4 KB per 8 chunks.
+//
+// Work split: one workgroup per compute unit (per 128-head group), each
+// taking an equal share of the launch's tiles. The tiles of the requests
+// with work (not aborted, not empty) are laid end to end; range i is
+// [i T / R, (i + 1) T / R) of the T tiles, each end moved to the nearest
+// split boundary of the request it falls in, so a range is a run of whole
+// splits of one or more requests (a segment per request). A segment is
+// decoded as one unit (its softmax state carried across its splits) and
+// writes its partial in the row of its first split; the rows of its other
+// splits get lse = -inf and no o_part (pkv_combine skips them). Shares of
+// equal size keep every compute unit busy to the end whatever the length
+// mix; the split only sets the granularity of the cuts.
 constexpr int kWideHeads = 32;
-constexpr float kWideTau = 60.0f;  // log2 headroom of the reference max
-constexpr int kWideBufs = 2;
-constexpr int kWideTileBytes = kTile * kDk;          // 36 KB
-constexpr int kWideDma = kWideTileBytes / 1024;      // 36 loads of 1 KB
-constexpr int kWideMine = kWideDma / 4;              // 9 per wave
+constexpr float kWideTau = 60.0f;            // log2 headroom of the reference max
+constexpr int kRow16 = kDk * 2;              // bf16 row: 1152 bytes, 72 chunks
+constexpr int kHalf16 = 32 * kRow16;         // 36 KB: 32 bf16 rows
+constexpr int kGroup16 = 32 * 128;           // 4 KB: 8 chunks of each of 32 rows
+constexpr int kVmcnt0 = 0x0F70;              // s_waitcnt vmcnt(0), other counters free
+constexpr int kTile16 = kTile * kRow16;      // 72 KB: a bf16 page
+constexpr int kTile8 = kTile * kDk;          // 36 KB of codes
+constexpr int kDma = 9;                      // loads per wave per code tile or bf16 half
+constexpr int kSlots8 = 2;                   // code tiles in the ring
+constexpr int kSlots16 = 4;                  // bf16 halves in the ring
 
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ int wide_pos(int r, int c) { return c ^ ((r >> 2) & 3); }
+__device__ __forceinline__ int wswz(int r) {
+  return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
+}
 
-__global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p, int n_splits,
-                                                                 int head_groups) {
-  static_assert((kWideBufs - 2) * kWideMine <= 63, "vmcnt counts to 63");
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[kWideBufs * kWideTileBytes];
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ int wave_scan_i(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Tiles request j contributes to the launch (0 if it has no work).
+__device__ __forceinline__ int req_tiles(const DecodeParams& p, int j) {
+  if (j >= p.batch) return 0;
+  const int L = p.seq_lens[j];
+  const bool ab = p.abort_flags && p.abort_flags[j];
+  return (ab || L <= 0 || L > p.max_seq_len) ? 0 : (L + kTile - 1) / kTile;
+}
+
+// Total tiles of the launch (uniform).
+__device__ __forceinline__ int64_t launch_tiles(const DecodeParams& p) {
+  const int lane = threadIdx.x & 63;
+  int64_t t = 0;
+  for (int b0 = 0; b0 < p.batch; b0 += 64)
+    t += __builtin_amdgcn_readlane(wave_scan_i(req_tiles(p, b0 + lane)), 63);
+  return t;
+}
+
+// The request holding flattened tile x (x < total): its index, its first
+// flattened tile and its tile count (uniform).
+__device__ __forceinline__ void locate(const DecodeParams& p, int64_t x, int& b_out,
+                                       int64_t& start_out, int& n_out) {
+  const int lane = threadIdx.x & 63;
+  int64_t base = 0;
+  for (int b0 = 0; b0 < p.batch; b0 += 64) {
+    const int n = req_tiles(p, b0 + lane);
+    const int incl = wave_scan_i(n);
+    const int tot = __builtin_amdgcn_readlane(incl, 63);
+    if (x < base + tot) {
+      const int bl = __popcll(__ballot(base + incl <= x));
+      b_out = b0 + bl;
+      start_out = base + __builtin_amdgcn_readlane(incl - n, bl);
+      n_out = __builtin_amdgcn_readlane(n, bl);
+      return;
+    }
+    base += tot;
+  }
+  b_out = p.batch;
+  start_out = base;
+  n_out = 0;
+}
+
+// Flattened tile x moved to the nearest split boundary of its request (or
+// the request's end); the same x gives the same boundary in every workgroup.
+__device__ __forceinline__ int64_t snap(const DecodeParams& p, int64_t x, int64_t total,
+                                        int tps) {
+  if (x >= total) return total;
+  int b, n;
+  int64_t start;
+  locate(p, x, b, start, n);
+  const int j = static_cast<int>(x - start);
+  const int jj = min(n, (j + tps / 2) / tps * tps);
+  return start + jj;
+}
+
+template <bool kE4M3>
+__global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p, int head_groups,
+                                                                 int n_ranges) {
+  // e4m3: [code tiles: 2 x 36 KB][bf16 halves: 2 x 36 KB]; bf16: [ring of 4 bf16 halves:
+  // 4 x 36 KB]; both then the half's numerators P: 128 heads x 32 tokens of bf16, rows
+  // padded to 80 bytes
+  constexpr int kTiles = kE4M3 ? kSlots8 * kTile8 + 2 * kHalf16 : kSlots16 * kHalf16;
+  constexpr int kPRow = 80;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kTiles + 128 * kPRow];
   __shared__ int32_t pages[kMaxUnitTiles];
-  __shared__ float l_s[4][kWideHeads];
-  __shared__ int vote[2][4];
+  __shared__ float l_all[128];
+  __shared__ int vote[4];
 
-  // Consecutive workgroup ids go to the 8 XCDs in turn, so the (request,
-  // head group) index is rotated by the split row: the units of one request
-  // land on different XCDs instead of all on XCD (index mod 8).
-  const int bx = static_cast<int>((blockIdx.x + blockIdx.y) % gridDim.x);
-  const int b = bx / head_groups;
-  const int hg = bx - b * head_groups;
+  const int hg = static_cast<int>(blockIdx.x) % head_groups;
+  const int ri = static_cast<int>(blockIdx.x) / head_groups;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5;     // which half of the k range this lane supplies
   const int col = lane & 31;    // head (QK, D of S^T) or dim (PV, D of O)
+  const int tps = p.split_tokens / kTile;  // tiles per split
 
-  if (p.abort_flags && p.abort_flags[b]) return;
-  const int L = p.seq_lens[b];
-  if (L > p.max_seq_len || L <= 0) return;
-  const int n_b = (L + p.split_tokens - 1) / p.split_tokens;
-  const int c = n_b - n_splits + static_cast<int>(blockIdx.y);
-  if (c < 0) return;
-  const int t_begin = c * p.split_tokens;
-  const int t_end = min(L, t_begin + p.split_tokens);
-  const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
+  // this workgroup's range [s0, s1) of the launch's flattened tiles
+  const int64_t total = launch_tiles(p);
+  const int64_t s0 = snap(p, ri * total / n_ranges, total, tps);
+  const int64_t s1 = snap(p, (ri + 1) * total / n_ranges, total, tps);
+  if (s0 >= s1) return;
+
+  const float qk_scale = (kE4M3 ? p.k_scale[0] : 1.0f) * p.sm_scale_log2;
+  const float o_scale = kE4M3 ? p.v_scale[0] : 1.0f;
+  const uint8_t* kpool = static_cast<const uint8_t*>(p.k_pool);
+  const uint32_t lds0 = lds_addr(lds);
+  uint8_t* pbuf = lds + kTiles;
+  // QK: this wave's 32 heads; PV: this wave's 128 dims, all 128 heads
   const int h_base = hg * 128 + wave * kWideHeads;
 
-  // q as B operands: k-step ks covers dims 32(ks/2) + 16hh + 8(ks%2) .. +7 for
-  // this lane's head, so one 16-byte K read serves two k-steps
-  bf16x8_t qf[36];
+  // Per-lane LDS byte offsets in a bf16 half (the swizzle only touches the
+  // low three bits of a chunk index, so the rest is an immediate or a
+  // wave-uniform add):
+  // K operand of k-step ks: row col, chunk 2 ks + hh in group ks / 4 at
+  // position (2 (ks % 4) + hh) ^ swz(col);
+  // V operand of dim block nb, token step u: the 16 lanes of group gq =
+  // lane / 16 read rows 8 hh + e and 8 hh + 4 + e of the step (e = (lane %
+  // 16) / 4), the 8 bytes (lane % 2) of chunk 16 wave + 4 nb + 2 a +
+  // (lane % 4) / 2 (a = gq % 2): dims 128 wave + 32 nb + 16 a .. + 15;
+  // P operand of head block hb, token step u: head 32 hb + col, tokens
+  // 16 u + 8 hh .. + 7.
+  uint32_t koff[4], voff[2][2];
   {
-    const int qi = b * p.num_q_heads + h_base + col;  // < 2^31 (checked on the host)
-    const uint16_t* qrow = p.q + static_cast<int64_t>(qi) * kDk;
+    const int fr = wswz(col);
 #pragma unroll
-    for (int ks = 0; ks < 36; ++ks)
-      qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * (ks >> 1) + 16 * hh + 8 * (ks & 1));
-  }
-  const float qk_scale = p.k_scale[0] * p.sm_scale_log2;
-  const float o_scale = p.v_scale[0];
-
-  const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_pages;
-  const int first_page = t_begin / kTile;
-  for (int j = tid; j < n_tiles; j += 256) pages[j] = bt[first_page + j];
-#pragma unroll
-  for (int ks = 0; ks < 36; ++ks) asm volatile("" : : "v"(qf[ks]));
-  asm volatile("" : : "s"(qk_scale), "s"(o_scale));
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : : : "memory");
-
-  // per-lane source of this wave's load i of a tile: load k = wave + 4i fills
-  // LDS chunks 64k .. 64k+63, chunk q = row q/36, position q%36
-  auto doff = [&](int i) __attribute__((always_inline)) {
-    const int q = 64 * (wave + 4 * i) + lane;
-    const int r = q / 36;
-    const int pp = q - 36 * r;
-    return static_cast<uint32_t>(r * kDk + wide_pos(r, pp) * 16);
-  };
-  const uint8_t* kpool = static_cast<const uint8_t*>(p.k_pool);
-  const uint32_t tiles0 = lds_addr(tiles);
-  auto page_of = [&](int t) __attribute__((always_inline)) {
-    return __builtin_amdgcn_readfirstlane(pages[t]);
-  };
-  auto issue = [&](int t) __attribute__((always_inline)) {
-    int page = page_of(t);
-    if (page < 0 || page >= p.num_pages) page = 0;  // loaded but never used
-    const uint8_t* base = kpool + static_cast<int64_t>(page) * kWideTileBytes;
-    const uint32_t buf = tiles0 + (t % kWideBufs) * kWideTileBytes;
-#pragma unroll
-    for (int i = 0; i < kWideMine; ++i) dma16(buf + 1024 * (wave + 4 * i), doff(i), base);
-  };
-
-  floatx16_t O[16];
-#pragma unroll
-  for (int nb = 0; nb < 16; ++nb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) O[nb][i] = 0.f;
-  // Scores are taken relative to a reference max m (log2 domain) that is set
-  // by the first tile and never moves by less than kWideTau: p = 2^(s - m)
-  // stays below 2^kWideTau, far inside bf16 and fp32 range, so O never has to
-  // be rescaled inside the loop. A score above m + kWideTau (not reachable by
-  // attention scores in practice) restarts the unit with the larger m.
-  float m = kMInit;
-  float l = 0.f;
-  const int a16 = (lane >> 4) & 1;
-  const int jj = lane & 15;
-  const int kk = jj >> 1;
-
-  // Per-lane LDS offsets. The swizzle term (r >> 2) & 3 of every row a lane
-  // reads is the same in both halves and both k-steps of a half (row offsets
-  // 32mb + 16u are multiples of 16), so four bases cover all reads:
-  // K operand, chunk 2j + hh of row 32mb + col, sits at position
-  // 4(j/2) + ((2(j%2) + hh) ^ sw): base koff[j%2] + 64(j/2) + 32mb rows;
-  // V operand of k-step (mb, u): the 16 lanes of a group address rows
-  // T[jj/2] of the step, half-chunk jj%2 of chunk 2nb + a16, at position
-  // 4(nb/2) + ((2(nb%2) + a16) ^ sw): base voff[nb%2] + 64(nb/2) + (32mb + 16u) rows.
-  // Lane i of a group then holds dim 32nb + 16a16 + i of the step's 8 tokens
-  // in P's order.
-  uint32_t koff[2], voff[2];
-  {
-    const int rk = col;
-    const int rv = 8 * (kk >> 2) + 4 * hh + (kk & 3);
+    for (int j = 0; j < 4; ++j) koff[j] = static_cast<uint32_t>(col * 128 + (((2 * j + hh) ^ fr) << 4));
+    const int e = (lane & 15) >> 2, a = (lane >> 4) & 1, i4 = lane & 3;
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      koff[x] = static_cast<uint32_t>(rk * kDk + wide_pos(rk, 2 * x + hh) * 16);
-      voff[x] = static_cast<uint32_t>(rv * kDk + wide_pos(rv, 2 * x + a16) * 16 + 8 * (jj & 1));
+      const int rv = 8 * hh + 4 * x + e;
+#pragma unroll
+      for (int par = 0; par < 2; ++par)  // parity of nb
+        voff[x][par] = static_cast<uint32_t>(
+            rv * 128 + ((((4 * par + 2 * a + (i4 >> 1)) ^ wswz(rv))) << 4) + 8 * (i4 & 1));
     }
   }
-  bool jump = false;  // a score went above the reference max by more than kWideTau
+  const uint32_t vwave = static_cast<uint32_t>(wave) * 2 * kGroup16;  // chunk 16 wave
+  const uint32_t poff = static_cast<uint32_t>(col * kPRow + 16 * hh);
+  // bf16 cache loads: lane l of wave w takes row 8 w + l / 8 of a half, the
+  // chunk that lands at position l % 8 of that row's group
+  const uint32_t code_off = static_cast<uint32_t>(16 * lane);
+  const int dma_row = 8 * wave + (lane >> 3);
+  const uint32_t dma_off = static_cast<uint32_t>(dma_row * kRow16 + (((lane & 7) ^ wswz(dma_row)) << 4));
 
-  // One 32-token half (mb) of a tile: S^T, numerators, O += P V.
-  auto half_tile = [&](const uint8_t* buf, int mb, int nv) __attribute__((always_inline)) {
-    floatx16_t st;
+  int64_t x = s0;
+  while (x < s1) {
+    // ---- the segment of request b in this range: its tiles [j0, j1)
+    int b, nt;
+    int64_t start;
+    locate(p, x, b, start, nt);
+    const int j0 = static_cast<int>(x - start);
+    const int j1 = static_cast<int>(min<int64_t>(nt, s1 - start));
+    x = start + j1;
+    const int L = p.seq_lens[b];
+    const int t_begin = j0 * kTile;
+    const int t_end = min(L, j1 * kTile);
+    const int n_tiles = j1 - j0;
+    const int c0 = j0 / tps;  // the split whose row takes the partial
+
+    // q as B operands: k-step ks covers dims 16 ks + 8 hh .. +7 of head h_base + col
+    bf16x8_t qf[36];
+    {
+      const int qi = b * p.num_q_heads + h_base + col;  // < 2^31 (checked on the host)
+      const uint16_t* qrow = p.q + static_cast<int64_t>(qi) * kDk + 8 * hh;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) st[i] = 0.f;
-    const uint8_t* kb0 = buf + 32 * mb * kDk + koff[0];
-    const uint8_t* kb1 = buf + 32 * mb * kDk + koff[1];
-    auto k_read = [&](int j) __attribute__((always_inline)) {
-      return *reinterpret_cast<const uint4*>(((j & 1) ? kb1 : kb0) + 64 * (j >> 1));
-    };
-    constexpr int kKAhead = 3;  // 16-byte K reads in flight ahead of their MFMAs
-    uint4 kq[kKAhead];
-#pragma unroll
-    for (int a = 0; a < kKAhead; ++a) kq[a] = k_read(a);
-#pragma unroll
-    for (int j = 0; j < 18; ++j) {
-      const uint4 cur = kq[j % kKAhead];
-      if (j + kKAhead < 18) kq[j % kKAhead] = k_read(j + kKAhead);
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(cur.x, cur.y), qf[2 * j], st, 0, 0, 0);
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16(cur.z, cur.w), qf[2 * j + 1], st, 0, 0, 0);
+      for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * ks);
+      // wait for q here, with a wait the compiler accounts for: it does not
+      // see the cache loads (inline asm), and a wait it placed for q inside
+      // the tile loop would also wait for every tile load in flight
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
     }
-    // scores: st[i] is token 32mb + 8(i/4) + 4hh + i%4 of head h_base + col
-    float lm = -INFINITY;
+    const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_pages;
+
+    // O[hb][nb]: heads 32 hb + .., dims 128 wave + 32 nb + .. (D layout)
+    floatx16_t O[4][4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float v = st[i] * qk_scale;
-      st[i] = (32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3) < nv) ? v : -INFINITY;
-      lm = fmaxf(lm, st[i]);
-    }
-    // the lanes col and col + 32 hold the two token halves of one head and
-    // feed the same A row of PV: both take the head's maximum, so their m
-    // (and the numerators summed into one l) always agree
-    lm = fmaxf(lm, __shfl_xor(lm, 32));
-    if (m == kMInit) {  // first scores of the unit set the reference max
-      m = lm > -INFINITY ? lm : kMInit;
-    } else if (lm > m + kWideTau) {
-      jump = true;
-      m = lm;  // raised; the unit is redone with it (see the pipeline)
-    }
-    // numerators as A operands of the two PV k-steps of this half:
-    // k-step u takes st[8u .. 8u+7] (tokens 32mb + 16u + {0..3, 8..11} + 4hh)
+    for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      float pr[8];
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        pr[k] = __builtin_amdgcn_exp2f(st[8 * u + k] - m);
-        l += pr[k];
-      }
-      bf16x8_t pf;
+        for (int i = 0; i < 16; ++i) O[hb][nb][i] = 0.f;
+    // Scores are taken relative to a reference max m (log2 domain) that is
+    // set by the first tile and never moves by less than kWideTau: p = 2^(s
+    // - m) stays below 2^kWideTau, far inside bf16 and fp32 range, so O never
+    // has to be rescaled inside the loop (which is what lets the waves that
+    // own a head's scores and the waves that own its output rows differ). A
+    // score above m + kWideTau (not reachable by attention scores in
+    // practice) restarts the segment with the larger m.
+    float m = kMInit;
+    float l = 0.f;
+    bool jump = false;
+
+    // QK^T of a 32-token half (rows of buf; row r is token 32 mb + r of the
+    // tile, of which nv are valid) for this wave's 32 heads; the numerators
+    // go to pbuf as bf16 (row = head, natural token order).
+    // `after(ks)` runs after the MFMA of k-step ks (the cache loads are
+    // spread over the chain there, so their issue overlaps the MFMAs).
+    auto qk_half = [&](const uint8_t* buf, int mb, int nv, auto&& after) __attribute__((always_inline)) {
+      floatx16_t st;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) pf[k] = static_cast<__bf16>(pr[k]);
-      const uint8_t* vb0 = buf + (32 * mb + 16 * u) * kDk + voff[0];
-      const uint8_t* vb1 = buf + (32 * mb + 16 * u) * kDk + voff[1];
-      auto v_read = [&](int nb) __attribute__((always_inline)) {
-        const uint8_t* ad = ((nb & 1) ? vb1 : vb0) + 64 * (nb >> 1);
-        const v2i_t r8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)ad);
-        return make_uint2(static_cast<uint32_t>(r8[0]), static_cast<uint32_t>(r8[1]));
+      for (int i = 0; i < 16; ++i) st[i] = 0.f;
+      auto k_read = [&](int ks) __attribute__((always_inline)) {
+        return *reinterpret_cast<const uint4*>(buf + koff[ks & 3] + kGroup16 * (ks >> 2));
       };
-      constexpr int kVAhead = 6;  // tr8 reads in flight ahead of their MFMA
-      uint2 vq[kVAhead];
+      constexpr int kKAhead = 4;  // K reads in flight ahead of their MFMAs
+      uint4 kq[kKAhead];
 #pragma unroll
-      for (int a = 0; a < kVAhead; ++a) vq[a] = v_read(a);
+      for (int a = 0; a < kKAhead; ++a) kq[a] = k_read(a);
 #pragma unroll
-      for (int nb = 0; nb < 16; ++nb) {
-        const uint2 cur = vq[nb % kVAhead];
-        if (nb + kVAhead < 16) vq[nb % kVAhead] = v_read(nb + kVAhead);
-        O[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf, fp8x8_to_bf16(cur.x, cur.y), O[nb], 0, 0, 0);
+      for (int ks = 0; ks < 36; ++ks) {
+        const uint4 cur = kq[ks % kKAhead];
+        if (ks + kKAhead < 36) kq[ks % kKAhead] = k_read(ks + kKAhead);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur.x, cur.y, cur.z, cur.w),
+                                                     qf[ks], st, 0, 0, 0);
+        after(ks);
       }
-    }
-  };
-
-  // ---- tile pipeline: kWideBufs - 1 tiles loaded ahead. A unit in which
-  // some score jumped (see above) is redone from tile 0 with the raised
-  // reference maxima once every wave has voted.
-  bool done = false;
-  while (!done) {
+      // scores: st[i] is token 32mb + 8(i/4) + 4hh + i%4 of head h_base + col;
+      // the exponent of token i is st[i] * qk_scale - m (one fused step
+      // where every token of the half is in the context)
+      const bool full = 32 * mb + 32 <= nv;
+      float lm = -INFINITY;
+      if (full) {
+        // the largest scaled score, from the largest (or, for a negative
+        // scale, smallest) raw one: rounding is monotonic
+        if (qk_scale >= 0.0f) {
 #pragma unroll
-    for (int t = 0; t < kWideBufs - 1; ++t)
-      if (t < n_tiles) issue(t);
-    for (int t = 0; t < n_tiles; ++t) {
-      const int after = min(kWideBufs - 2, n_tiles - 1 - t);
-      if (after >= 2) wait_vm<2 * kWideMine>();
-      else if (after == 1) wait_vm<kWideMine>();
-      else wait_vm<0>();
-      wg_barrier();  // tile t is in LDS for every wave; every wave is done with tile t - 1
-      if (t + kWideBufs - 1 < n_tiles) issue(t + kWideBufs - 1);
-      const int page = page_of(t);
-      const int nv = min(kTile, t_end - (t_begin + kTile * t));
-      if (page >= 0 && page < p.num_pages) {
-        uint8_t* buf = tiles + (t % kWideBufs) * kWideTileBytes;
-        if (nv < kTile) {
-          // rows past the context hold stale bytes; their V part must be finite
-          const int n16 = (kTile - nv) * (kDk / 16);
-          for (int i = tid; i < n16; i += 256)
-            *reinterpret_cast<uint4*>(buf + nv * kDk + 16 * i) = make_uint4(0u, 0u, 0u, 0u);
-          wg_barrier();
+          for (int i = 0; i < 16; ++i) lm = fmaxf(lm, st[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) lm = fmaxf(lm, -st[i]);
         }
-#pragma unroll 1
-        for (int mb = 0; mb < 2; ++mb) half_tile(buf, mb, nv);
+        lm *= fabsf(qk_scale);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float v = st[i] * qk_scale;
+          st[i] = (32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3) < nv) ? v : -INFINITY;
+          lm = fmaxf(lm, st[i]);
+        }
       }
-    }
-    if (lane == 0) vote[0][wave] = jump ? 1 : 0;
-    wg_barrier();
-    done = (vote[0][0] | vote[0][1] | vote[0][2] | vote[0][3]) == 0;
-    if (!done) {
-      // drain the loads in flight (none: the last tile waited for all) and
-      // start over; each head keeps its raised reference max
-      wait_vm<0>();
-      jump = false;
-      l = 0.f;
+      // the lanes col and col + 32 hold the two token halves of one head:
+      // both take the head's maximum, so their m (and the numerators summed
+      // into one l) always agree
+      lm = fmaxf(lm, __shfl_xor(lm, 32));
+      if (m == kMInit) {  // first scores of the segment set the reference max
+        m = lm > -INFINITY ? lm : kMInit;
+      } else if (lm > m + kWideTau) {
+        jump = true;
+        m = lm;  // raised; the segment is redone with it (see the pipeline)
+      }
 #pragma unroll
-      for (int nb = 0; nb < 16; ++nb)
+      for (int q = 0; q < 4; ++q) {
+        float pr[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) O[nb][i] = 0.f;
-    }
-    wg_barrier();  // the vote has been read before it is written again
-  }
+        for (int k = 0; k < 4; ++k) {
+          const float e = full ? __builtin_fmaf(st[4 * q + k], qk_scale, -m) : st[4 * q + k] - m;
+          pr[k] = __builtin_amdgcn_exp2f(e);
+          l += pr[k];
+        }
+        const bf16x2_t lo = {static_cast<__bf16>(pr[0]), static_cast<__bf16>(pr[1])};
+        const bf16x2_t hi = {static_cast<__bf16>(pr[2]), static_cast<__bf16>(pr[3])};
+        *reinterpret_cast<uint2*>(pbuf + (wave * kWideHeads + col) * kPRow + 16 * q + 8 * hh) =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+      }
+    };
 
-  // ---- finish: denominators per head, then the normalised partial rows.
-  // Lane indices and output addresses are formed afresh here (mbcnt gives
-  // the lane) so that nothing from the prologue stays alive through the loop.
-  const int lane_e = static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
-  const int col_e = lane_e & 31, hh_e = lane_e >> 5;
-  l += __shfl_xor(l, 32);
-  if (hh_e == 0) l_s[wave][col_e] = l;
-  __builtin_amdgcn_wave_barrier();
-  int b_out = b, h_out = h_base, c_out = c;
-  asm volatile("" : "+s"(b_out), "+s"(h_out), "+s"(c_out));
-  const int bh0 = b_out * p.num_q_heads + h_out;
-  if (hh_e == 0)
-    p.lse_part[static_cast<int64_t>(bh0 + col_e) * p.max_splits + c_out] =
-        l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
-  float f[16];
+    // O += P V of a half for this wave's 128 dims and all 128 heads;
+    // `after(j)` runs after MFMA j of 32 (work that interleaves with them)
+    auto pv_half = [&](const uint8_t* buf, auto&& after) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float lh = l_s[wave][8 * (i >> 2) + 4 * hh_e + (i & 3)];
-    f[i] = lh > 0.0f ? o_scale / lh : 0.0f;
+      for (int u = 0; u < 2; ++u) {
+        bf16x8_t pa[4], vb[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          pa[hb] = *reinterpret_cast<const bf16x8_t*>(pbuf + poff + hb * 32 * kPRow + 32 * u);
+        const uint8_t* vrow = buf + 16 * u * 128 + vwave;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const uint32_t o = kGroup16 * (nb >> 1);
+          const v4s_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(vrow + voff[0][nb & 1] + o));
+          const v4s_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(vrow + voff[1][nb & 1] + o));
+          vb[nb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) {
+            O[hb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[hb], vb[nb], O[hb][nb], 0, 0, 0);
+            after(16 * u + 4 * nb + hb);
+          }
+      }
+    };
+
+    // ---- the segment's tiles, in chunks of at most kMaxUnitTiles (their
+    // page ids in LDS). A segment in which some score jumped (see above) is
+    // redone from its first tile with the raised reference maxima once every
+    // wave has voted.
+    bool done = false;
+    while (!done) {
+      for (int k0 = 0; k0 < n_tiles; k0 += kMaxUnitTiles) {
+        const int kn = min(kMaxUnitTiles, n_tiles - k0);
+        for (int j = tid; j < kn; j += 256) pages[j] = bt[j0 + k0 + j];
+        // every load so far (q, page ids) completes before the first tile
+        // load, so the vmcnt waits below count tile loads only
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : : : "memory");
+        auto page_of = [&](int t) __attribute__((always_inline)) {
+          return __builtin_amdgcn_readfirstlane(pages[t]);
+        };
+        auto page_base = [&](int t) __attribute__((always_inline)) {
+          int page = page_of(t);
+          if (page < 0 || page >= p.num_pages) page = 0;  // loaded but never used
+          return kpool + static_cast<int64_t>(page) * (kE4M3 ? kTile8 : kTile16);
+        };
+        auto nv_of = [&](int t) __attribute__((always_inline)) {
+          return min(kTile, t_end - (t_begin + kTile * (k0 + t)));
+        };
+        // one half: QK^T, its numerators in LDS for every wave, then PV
+        auto half = [&](const uint8_t* buf, int mb, int nv, auto&& after) __attribute__((always_inline)) {
+          qk_half(buf, mb, nv, after);
+          wg_barrier();  // every head's numerators are in pbuf
+          pv_half(buf, [](int) {});
+        };
+        if constexpr (kE4M3) {
+          // ---- codes: whole tiles, a plain copy of the page, in two slots;
+          // each half is converted into one of two bf16 buffers while the
+          // half before it is multiplied by V. Load i of tile t (of this
+          // wave's nine):
+          auto issue_one = [&](int t, const uint8_t* base, int i) __attribute__((always_inline)) {
+            const int k = wave + 4 * i;
+            dma16(lds0 + (t % kSlots8) * kTile8 + 1024 * k, code_off, base + 1024 * k);
+          };
+          auto issue = [&](int t) __attribute__((always_inline)) {
+            const uint8_t* base = page_base(t);
+#pragma unroll
+            for (int i = 0; i < kDma; ++i) issue_one(t, base, i);
+          };
+          uint8_t* const bf = lds + kSlots8 * kTile8;  // bf16 half u in bf + (u % 2) * kHalf16
+          // rows 32 xh .. 32 xh + 31 of code tile t into bf16 buffer `dst0`:
+          // thread t takes row t / 8 and its chunks t % 8 + 8 k (8 codes
+          // each), so both offsets are a fixed base plus 64 k (codes) and 4
+          // KB k (bf16: group k of the row). A read pass (32 lanes: 4 rows x
+          // 64 bytes, rows 576 bytes apart) and a write pass (16 lanes: 2
+          // rows x 8 chunks) each touch every bank once. Rows past the
+          // context become zeros (V must be finite there); the codes are
+          // selected, not branched on, so the conversion can interleave
+          // with the MFMAs around it.
+          struct Conv {
+            const uint8_t* src;
+            uint8_t* dst;
+            bool in;
+          };
+          auto conv_of = [&](int t, int xh, int nv, uint8_t* dst0) __attribute__((always_inline)) {
+            const int r = tid >> 3, c8 = tid & 7;
+            return Conv{lds + (t % kSlots8) * kTile8 + (32 * xh + r) * kDk + 8 * c8,
+                        dst0 + r * 128 + ((c8 ^ wswz(r)) << 4), 32 * xh + r < nv};
+          };
+          auto conv_step = [&](const Conv& c, int k) __attribute__((always_inline)) {
+            uint2 w = *reinterpret_cast<const uint2*>(c.src + 64 * k);
+            w.x = c.in ? w.x : 0u;
+            w.y = c.in ? w.y : 0u;
+            *reinterpret_cast<uint4*>(c.dst + kGroup16 * k) = __builtin_bit_cast(uint4, fp8x8_to_bf16(w.x, w.y));
+          };
+          auto convert = [&](int t, int xh, int nv, uint8_t* dst0) __attribute__((always_inline)) {
+            const Conv c = conv_of(t, xh, nv, dst0);
+#pragma unroll
+            for (int k = 0; k < 9; ++k) conv_step(c, k);
+          };
+          // half u = 2 t + xh is decoded when its page is in the pool and
+          // it holds tokens of the context
+          auto live = [&](int u) __attribute__((always_inline)) {
+            const int page = page_of(u >> 1);
+            return page >= 0 && page < p.num_pages && 32 * (u & 1) < nv_of(u >> 1);
+          };
+          const int nu = 2 * kn;
+          issue(0);
+          if (kn > 1) issue(1);
+          if (kn > 1) wait_vm<kDma>();
+          else wait_vm<0>();
+          wg_barrier();  // tile 0's codes are in LDS
+          convert(0, 0, nv_of(0), bf);
+          for (int u = 0; u < nu; ++u) {
+            wg_barrier();  // half u is converted; pbuf and the other buffer are free
+            const int t = u >> 1;
+            // the slot of tile t takes tile t + 2 once its second half is
+            // converted (before the barrier above), during this half's QK^T
+            const bool more = (u & 1) && t + 2 < kn;
+            const uint8_t* nbase = more ? page_base(t + 2) : nullptr;
+            const bool next = u + 1 < nu;
+            // the next half opens tile t + 1: its codes must have landed
+            // (tile t + 2 may still be loading behind it)
+            const bool wait_next = next && (u & 1);
+            uint8_t* const cur = bf + (u & 1) * kHalf16;
+            uint8_t* const nxt = bf + ((u + 1) & 1) * kHalf16;
+            if (live(u)) {
+              const int nv = nv_of(t);
+              qk_half(cur, u & 1, nv, [&](int ks) __attribute__((always_inline)) {
+                if (more && (ks & 3) == 3) issue_one(t + 2, nbase, ks >> 2);
+              });
+              if (wait_next) {
+                if (t + 2 < kn) wait_vm<kDma>();
+                else wait_vm<0>();
+              }
+              wg_barrier();  // every head's numerators are in pbuf; tile t + 1 is in LDS
+              // the next half's conversion, one step after every third MFMA
+              // (after the last half it fills the spare buffer with bytes
+              // nothing reads)
+              const int un = u + 1;
+              const Conv c = conv_of(un >> 1, un & 1, nv_of(un >> 1), nxt);
+              pv_half(cur, [&](int j) __attribute__((always_inline)) {
+                if (j % 3 == 2 && j / 3 < 9) conv_step(c, j / 3);
+              });
+            } else {
+              if (more) issue(t + 2);
+              if (wait_next) {
+                if (t + 2 < kn) wait_vm<kDma>();
+                else wait_vm<0>();
+              }
+              wg_barrier();  // tile t + 1 is in LDS for every wave
+              if (next) {
+                const int un = u + 1;
+                convert(un >> 1, un & 1, nv_of(un >> 1), nxt);
+              }
+            }
+          }
+        } else {
+          // ---- bf16: halves of a page, three ahead, straight into the
+          // layout the operands are read in: load i of wave w fills group i,
+          // rows 8 w .. 8 w + 7 (1 KB of LDS), each lane one chunk, reading
+          // 128 bytes of each of 8 rows of the page
+          const int nh = 2 * kn;
+          auto half_base = [&](int h) __attribute__((always_inline)) {
+            return page_base(h >> 1) + (h & 1) * kHalf16;
+          };
+          auto issue_one = [&](int h, const uint8_t* base, int i) __attribute__((always_inline)) {
+            dma16(lds0 + (h % kSlots16) * kHalf16 + 1024 * wave + kGroup16 * i, dma_off, base + 128 * i);
+          };
+          auto issue = [&](int h) __attribute__((always_inline)) {
+            const uint8_t* base = half_base(h);
+#pragma unroll
+            for (int i = 0; i < kDma; ++i) issue_one(h, base, i);
+          };
+          for (int h = 0; h < 3 && h < nh; ++h) issue(h);
+          for (int h = 0; h < nh; ++h) {
+            const int later = min(2, nh - 1 - h);  // halves loading behind half h
+            if (later == 2) wait_vm<2 * kDma>();
+            else if (later == 1) wait_vm<kDma>();
+            else wait_vm<0>();
+            wg_barrier();  // half h is in LDS; every wave is done with half h - 1 and pbuf
+            // half h + 3 goes to the slot of half h - 1, during half h's QK^T
+            const bool more = h + 3 < nh;
+            const uint8_t* nbase = more ? half_base(h + 3) : nullptr;
+            const int t = h >> 1, xh = h & 1;
+            const int page = page_of(t);
+            const int nv = nv_of(t);
+            if (!(page >= 0 && page < p.num_pages && 32 * xh < nv)) {
+              if (more) issue(h + 3);
+            } else {
+              uint8_t* buf = lds + (h % kSlots16) * kHalf16;
+              if (nv < 32 * xh + 32) {
+                // rows past the context hold stale bytes; V must be finite there
+                const int r0 = nv - 32 * xh;
+                const int per_group = (32 - r0) * 8;  // chunks of those rows in a group
+                for (int i = tid; i < 9 * per_group; i += 256) {
+                  const int g = i / per_group, rem = i - g * per_group;
+                  *reinterpret_cast<uint4*>(buf + g * kGroup16 + (r0 + (rem >> 3)) * 128 + 16 * (rem & 7)) =
+                      make_uint4(0u, 0u, 0u, 0u);
+                }
+                wg_barrier();
+              }
+              half(buf, xh, nv, [&](int ks) __attribute__((always_inline)) {
+                if (more && (ks & 3) == 3) issue_one(h + 3, nbase, ks >> 2);
+              });
+            }
+          }
+        }
+        wg_barrier();  // every wave is done with the slots and the page ids
+      }
+      if (lane == 0) vote[wave] = jump ? 1 : 0;
+      wg_barrier();
+      done = (vote[0] | vote[1] | vote[2] | vote[3]) == 0;
+      if (!done) {
+        // nothing is in flight (the last tile waited for all); start over,
+        // each head keeping its raised reference max
+        jump = false;
+        l = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) O[hb][nb][i] = 0.f;
+      }
+      wg_barrier();  // the vote has been read before it is written again
+    }
+
+    // ---- the segment's partial: denominators per head (from the waves
+    // that own the heads' scores), then the normalised rows (from the waves
+    // that own the dims) in split c0's row; the rows of its other splits get
+    // lse = -inf
+    l += __shfl_xor(l, 32);
+    const int64_t bh0 = static_cast<int64_t>(b) * p.num_q_heads + hg * 128;
+    if (hh == 0) {
+      l_all[wave * kWideHeads + col] = l;
+      const int64_t row = (bh0 + wave * kWideHeads + col) * p.max_splits;
+      p.lse_part[row + c0] = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+      const int c_last = (j1 - 1) / tps;
+      for (int cx = c0 + 1; cx <= c_last; ++cx) p.lse_part[row + cx] = -INFINITY;
+    }
+    wg_barrier();  // every head's denominator is in l_all
+    // the stride is made opaque here so that the 64 row addresses are formed
+    // per segment instead of being kept live (and spilled) across segments
+    int64_t head_stride = static_cast<int64_t>(p.max_splits) * kDv;
+    asm volatile("" : "+s"(head_stride));
+    float* dst0 = p.o_part + (bh0 * p.max_splits + c0) * kDv + 128 * wave + col;
+    int hq = 4 * hh;  // opaque for the same reason
+    asm volatile("" : "+v"(hq));
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int hl = 32 * hb + 8 * (i >> 2) + hq + (i & 3);
+        const float lh = l_all[hl];
+        const float f = lh > 0.0f ? o_scale / lh : 0.0f;
+        float* dst = dst0 + hl * head_stride;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) dst[32 * nb] = O[hb][nb][i] * f;
+      }
+    wg_barrier();  // l_all is read before the next segment writes it
   }
-  float* dst0 = p.o_part + (static_cast<int64_t>(bh0 + 4 * hh_e) * p.max_splits + c_out) * kDv + col_e;
-  const int64_t head_stride = static_cast<int64_t>(p.max_splits) * kDv;
-#pragma unroll
-  for (int nb = 0; nb < 16; ++nb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      dst0[(8 * (i >> 2) + (i & 3)) * head_stride + 32 * nb] = O[nb][i] * f[i];
 }
 
 }  // namespace
@@ -701,12 +993,33 @@ bool mla_fast_path_supported(int dk, int dv, int num_kv_heads, int num_q_heads, 
          num_q_heads % 64 == 0 && num_q_heads <= 1024 && split_tokens <= kMaxUnitTiles * kTile;
 }
 
+// Compute units of the current device (looked up once per device).
+int cu_count() {
+  static int counts[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (counts[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    counts[dev] = n;
+  }
+  return counts[dev];
+}
+
 int launch_decode_mla(const DecodeParams& p, bool e4m3, int n_split_blocks, int batch,
                       hipStream_t stream) {
-  if (e4m3 && p.num_q_heads % 128 == 0 && n_split_blocks <= 65535) {
+  if (p.num_q_heads % 128 == 0) {
+    // one workgroup per compute unit and 128-head group, each an equal share
+    // of the launch's tiles
     const int head_groups = p.num_q_heads / 128;
-    const dim3 grid(batch * head_groups, n_split_blocks);
-    decode_mla_wide_kernel<<<grid, 256, 0, stream>>>(p, n_split_blocks, head_groups);
+    const int n_ranges = std::max(1, cu_count() / head_groups);
+    const dim3 grid(n_ranges * head_groups);
+    if (e4m3) {
+      decode_mla_wide_kernel<true><<<grid, 256, 0, stream>>>(p, head_groups, n_ranges);
+    } else {
+      decode_mla_wide_kernel<false><<<grid, 256, 0, stream>>>(p, head_groups, n_ranges);
+    }
     return pkv::launch_status();
   }
   const int head_groups = p.num_q_heads / 64;

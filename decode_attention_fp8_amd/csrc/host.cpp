@@ -37,12 +37,17 @@ extern "C" int32_t pkv_suggest_split(const pkv_cache* cache, int32_t num_q_heads
   const bool latent = cache->v_pool == nullptr;
   const int G = num_q_heads / cache->num_kv_heads;
   int64_t s;
-  if (latent && cache->dtype == PKV_KV_E4M3 && cache->head_dim_k == 576 &&
-      cache->head_dim_v == 512 && cache->num_kv_heads == 1 && P == 64 && num_q_heads % 128 == 0) {
-    // wide latent kernel: one workgroup per compute unit and unit; the
-    // longest split that still gives about one unit per compute unit (7/8)
-    s = 4096;
-    while (s > P && units(s, num_q_heads / 128) < 224) s /= 2;
+  if (latent && cache->head_dim_k == 576 && cache->head_dim_v == 512 &&
+      cache->num_kv_heads == 1 && P == 64 && num_q_heads % 128 == 0) {
+    // wide latent kernel (e4m3 or bf16): every compute unit takes an equal
+    // share of the batch's pages, cut at split boundaries, so the split
+    // only sets how finely the shares can be cut: about an eighth of a
+    // share (a power of two of pages, 1 .. 64), which keeps the cuts within
+    // a few percent of equal while the partial rows stay few
+    const int64_t share = std::max<int64_t>(1, total / P / (256 / (num_q_heads / 128)));
+    int64_t pages = 1;
+    while (pages * 2 <= share / 8 && pages < 64) pages *= 2;
+    s = pages * P;
   } else if (!latent && cache->head_dim_k == 128 && cache->head_dim_v == 128 && G <= 16) {
     // MFMA grouped-query kernel (e4m3 or bf16): single-wave units, nine
     // (five with bf16) per compute unit; splits of 128 .. 2048 tokens (256

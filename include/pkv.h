@@ -213,8 +213,14 @@ int pkv_verify_append(const pkv_cache* cache, const int32_t* block_table,
  *   o_part:   float32 [batch][num_q_heads][max_splits][head_dim_v]
  *   lse_part: float32 [batch][num_q_heads][max_splits]
  * Only the splits a request has are written; aborted requests write
- * nothing. A block-table entry outside [0, num_pages) is never read: its
- * tokens are left out (pkv_verify turns such requests into aborts).
+ * nothing. For the latent layout with query heads in multiples of 128, the
+ * launch gives every compute unit an equal share of the batch's tokens, cut
+ * at split boundaries: a run of consecutive splits of one request decoded
+ * together writes its partial in its first split's row, and the other rows
+ * of the run get lse_part = -inf with o_part left unwritten (pkv_combine
+ * skips such rows; the merge is the same). A block-table entry outside
+ * [0, num_pages) is never read: its tokens are left out (pkv_verify turns
+ * such requests into aborts).
  * EINVAL: NULL pointers, num_q_heads not a multiple of num_kv_heads,
  * split_tokens invalid, max_seq_len or max_splits inconsistent.
  * EUNSUPPORTED: a shape with no kernel; supported are
@@ -236,6 +242,7 @@ int pkv_decode_attn(const pkv_cache* cache, const void* q, int32_t num_q_heads,
  * splits:
  *   M = max_c lse_c, w_c = exp(lse_c - M),
  *   out[b][h] = bf16_RNE( sum_c w_c * o_c / sum_c w_c ),
+ * where a row with lse_c = -inf adds nothing and its o_c is not read,
  *   lse_out[b][h] = M + ln sum_c w_c.
  * Aborted (abort_flags[b] != 0) or empty (L <= 0) requests get out = 0 and
  * lse_out = -inf; a request with L > max_seq_len gets NaN.
