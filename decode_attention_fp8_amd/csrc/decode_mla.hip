@@ -463,6 +463,16 @@ __device__ __forceinline__ int wswz(int r) {
   return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
 }
 
+// max(x, x of lane l ^ 32) in every lane: a copy of x and x swap their
+// halves of the wave (v_permlane32_swap), so every lane holds both values.
+// Written out (the swap, and the wait state its read of the copy needs):
+// the compiler builtin for it lets the max be folded away.
+__device__ __forceinline__ float max_across_halves(float x) {
+  float a = x, b;
+  asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "=&v"(b));
+  return fmaxf(a, b);
+}
+
 // Inclusive prefix sum over the wave.
 __device__ __forceinline__ int wave_scan_i(int x) {
   const int lane = threadIdx.x & 63;
@@ -695,28 +705,44 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
         }
       }
       // the lanes col and col + 32 hold the two token halves of one head:
-      // both take the head's maximum, so their m (and the numerators summed
-      // into one l) always agree
-      lm = fmaxf(lm, __shfl_xor(lm, 32));
-      if (m == kMInit) {  // first scores of the segment set the reference max
-        m = lm > -INFINITY ? lm : kMInit;
-      } else if (lm > m + kWideTau) {
-        jump = true;
-        m = lm;  // raised; the segment is redone with it (see the pipeline)
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float pr[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float e = full ? __builtin_fmaf(st[4 * q + k], qk_scale, -m) : st[4 * q + k] - m;
-          pr[k] = __builtin_amdgcn_exp2f(e);
-          l += pr[k];
-        }
+      // both take the head's maximum (the two halves of the wave swap
+      // values), so their m (and the numerators summed into one l) always
+      // agree
+      lm = max_across_halves(lm);
+      // the first scores of the segment set the reference max; a score
+      // above it by more than kWideTau raises it, and the segment is redone
+      const bool first = m == kMInit;
+      const bool raise = !first && lm > m + kWideTau;
+      jump = jump || raise;
+      m = first ? (lm > -INFINITY ? lm : kMInit) : (raise ? lm : m);
+      auto store = [&](int q, const float (&pr)[4]) __attribute__((always_inline)) {
         const bf16x2_t lo = {static_cast<__bf16>(pr[0]), static_cast<__bf16>(pr[1])};
         const bf16x2_t hi = {static_cast<__bf16>(pr[2]), static_cast<__bf16>(pr[3])};
         *reinterpret_cast<uint2*>(pbuf + (wave * kWideHeads + col) * kPRow + 16 * q + 8 * hh) =
             make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+      };
+      if (full) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float pr[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            pr[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[4 * q + k], qk_scale, -m));
+            l += pr[k];
+          }
+          store(q, pr);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float pr[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            pr[k] = __builtin_amdgcn_exp2f(st[4 * q + k] - m);
+            l += pr[k];
+          }
+          store(q, pr);
+        }
       }
     };
 
@@ -762,11 +788,14 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
         auto page_of = [&](int t) __attribute__((always_inline)) {
           return __builtin_amdgcn_readfirstlane(pages[t]);
         };
-        auto page_base = [&](int t) __attribute__((always_inline)) {
-          int page = page_of(t);
+        auto base_of = [&](int page) __attribute__((always_inline)) {
           if (page < 0 || page >= p.num_pages) page = 0;  // loaded but never used
           return kpool + static_cast<int64_t>(page) * (kE4M3 ? kTile8 : kTile16);
         };
+        auto page_base = [&](int t) __attribute__((always_inline)) { return base_of(page_of(t)); };
+        // a page id read ahead (kept in a vector register until it is used,
+        // so the read's latency passes during the MFMAs in between)
+        auto page_ahead = [&](int t) __attribute__((always_inline)) { return pages[min(t, kn - 1)]; };
         auto nv_of = [&](int t) __attribute__((always_inline)) {
           return min(kTile, t_end - (t_begin + kTile * (k0 + t)));
         };
@@ -823,10 +852,6 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
           };
           // half u = 2 t + xh is decoded when its page is in the pool and
           // it holds tokens of the context
-          auto live = [&](int u) __attribute__((always_inline)) {
-            const int page = page_of(u >> 1);
-            return page >= 0 && page < p.num_pages && 32 * (u & 1) < nv_of(u >> 1);
-          };
           const int nu = 2 * kn;
           issue(0);
           if (kn > 1) issue(1);
@@ -834,20 +859,26 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
           else wait_vm<0>();
           wg_barrier();  // tile 0's codes are in LDS
           convert(0, 0, nv_of(0), bf);
+          int pv_cur = page_ahead(0);  // page ids of tiles u / 2 and u / 2 + 2
+          int pv_far = page_ahead(2);
           for (int u = 0; u < nu; ++u) {
             wg_barrier();  // half u is converted; pbuf and the other buffer are free
             const int t = u >> 1;
+            const int page = __builtin_amdgcn_readfirstlane(pv_cur);
+            const int page_far = __builtin_amdgcn_readfirstlane(pv_far);
+            pv_cur = page_ahead((u + 1) >> 1);
+            pv_far = page_ahead(((u + 1) >> 1) + 2);
             // the slot of tile t takes tile t + 2 once its second half is
             // converted (before the barrier above), during this half's QK^T
             const bool more = (u & 1) && t + 2 < kn;
-            const uint8_t* nbase = more ? page_base(t + 2) : nullptr;
+            const uint8_t* nbase = more ? base_of(page_far) : nullptr;
             const bool next = u + 1 < nu;
             // the next half opens tile t + 1: its codes must have landed
             // (tile t + 2 may still be loading behind it)
             const bool wait_next = next && (u & 1);
             uint8_t* const cur = bf + (u & 1) * kHalf16;
             uint8_t* const nxt = bf + ((u + 1) & 1) * kHalf16;
-            if (live(u)) {
+            if (page >= 0 && page < p.num_pages && 32 * (u & 1) < nv_of(t)) {
               const int nv = nv_of(t);
               qk_half(cur, u & 1, nv, [&](int ks) __attribute__((always_inline)) {
                 if (more && (ks & 3) == 3) issue_one(t + 2, nbase, ks >> 2);
@@ -866,7 +897,10 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
                 if (j % 3 == 2 && j / 3 < 9) conv_step(c, j / 3);
               });
             } else {
-              if (more) issue(t + 2);
+              if (more) {
+#pragma unroll
+                for (int i = 0; i < kDma; ++i) issue_one(t + 2, nbase, i);
+              }
               if (wait_next) {
                 if (t + 2 < kn) wait_vm<kDma>();
                 else wait_vm<0>();
@@ -896,20 +930,28 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
             for (int i = 0; i < kDma; ++i) issue_one(h, base, i);
           };
           for (int h = 0; h < 3 && h < nh; ++h) issue(h);
+          int pv_cur = page_ahead(0);  // page ids of tiles h / 2 and (h + 3) / 2
+          int pv_far = page_ahead(1);
           for (int h = 0; h < nh; ++h) {
             const int later = min(2, nh - 1 - h);  // halves loading behind half h
             if (later == 2) wait_vm<2 * kDma>();
             else if (later == 1) wait_vm<kDma>();
             else wait_vm<0>();
             wg_barrier();  // half h is in LDS; every wave is done with half h - 1 and pbuf
+            const int page = __builtin_amdgcn_readfirstlane(pv_cur);
+            const int page_far = __builtin_amdgcn_readfirstlane(pv_far);
+            pv_cur = page_ahead((h + 1) >> 1);
+            pv_far = page_ahead((h + 4) >> 1);
             // half h + 3 goes to the slot of half h - 1, during half h's QK^T
             const bool more = h + 3 < nh;
-            const uint8_t* nbase = more ? half_base(h + 3) : nullptr;
+            const uint8_t* nbase = more ? base_of(page_far) + ((h + 3) & 1) * kHalf16 : nullptr;
             const int t = h >> 1, xh = h & 1;
-            const int page = page_of(t);
             const int nv = nv_of(t);
             if (!(page >= 0 && page < p.num_pages && 32 * xh < nv)) {
-              if (more) issue(h + 3);
+              if (more) {
+#pragma unroll
+                for (int i = 0; i < kDma; ++i) issue_one(h + 3, nbase, i);
+              }
             } else {
               uint8_t* buf = lds + (h % kSlots16) * kHalf16;
               if (nv < 32 * xh + 32) {
@@ -931,7 +973,9 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
         }
         wg_barrier();  // every wave is done with the slots and the page ids
       }
-      if (lane == 0) vote[wave] = jump ? 1 : 0;
+      // a jump in any lane of the wave (any of its heads) counts
+      const bool wave_jump = __builtin_amdgcn_ballot_w64(jump) != 0;
+      if (lane == 0) vote[wave] = wave_jump ? 1 : 0;
       wg_barrier();
       done = (vote[0] | vote[1] | vote[2] | vote[3]) == 0;
       if (!done) {

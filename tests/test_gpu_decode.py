@@ -335,17 +335,20 @@ def test_mla_score_jump_far_above_the_first_tile(kv):
                                    ((128 + 1, 7.0), (128 + 6, 5.0)), ((160 + 12, 6.0),)],
                          ids=["one_token_upper_half", "halves_different_upper_higher",
                               "halves_different_lower_higher", "one_token_second_block"])
-def test_mla_score_jump_single_tokens(kv, jumps):
-    """Single tokens whose keys align with head 0's query jump far above the
-    first tile's scores. Token t of a 32-token block sits in one of two lane
-    halves by bit 2 of t, so a jump in one half only (and jumps of different
-    size in the two halves of one block) must still give every lane of the
-    head the same reference max."""
+@pytest.mark.parametrize("head", [0, 45])
+def test_mla_score_jump_single_tokens(kv, jumps, head):
+    """Single tokens whose keys align with one head's query jump far above
+    the first tile's scores. Token t of a 32-token block sits in one of two
+    lane halves by bit 2 of t, so a jump in one half only (and jumps of
+    different size in the two halves of one block) must still give every lane
+    of the head the same reference max; a jump in a head other than the
+    first of its wave (head 45: wave 1, lane 13) must still make the
+    workgroup redo the segment."""
     from oracle import attention
     hq, dk, dv, P, L = 128, 576, 512, 64, 256
     rng = np.random.default_rng(19)
     q = torch.from_numpy(rng.standard_normal((1, hq, dk)).astype(np.float32)).to(torch.bfloat16)
-    sign = np.sign(q[0, 0].float().numpy())
+    sign = np.sign(q[0, head].float().numpy())
     sign[sign == 0] = 1
     vals = rng.standard_normal((L, dk)).astype(np.float32) * 0.01
     for t, a in jumps:
