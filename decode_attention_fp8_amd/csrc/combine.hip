@@ -11,6 +11,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kDirectRows = 4;  // rows per thread group on the one-pass path
 
 // One workgroup of 256 threads per (request, query head). The maximum lse is
 // reduced over the workgroup. Then, 256 split rows at a time, the rows that
@@ -22,7 +23,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 // consecutive steps' loads are independent. The P partial sums meet in LDS.
 // The order of every sum is fixed, so the result is the same bits on every
 // run.
-template <int DV>
+//
+// When every split row of a head fits in one pass (kRows rows per thread
+// group, max_splits <= kP * kRows), the rows' lse and o chunks are all
+// loaded at the start, beside the request's length: rows are bounded by
+// max_splits, not by the length, so every load is in the buffers, and rows
+// past the length are dropped afterwards. One memory round trip instead of
+// three (length, lse, o).
+template <int DV, bool kDirect>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
                                                       const int32_t* __restrict__ seq_lens,
@@ -33,6 +41,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
                                                       float* __restrict__ lse_out) {
   constexpr int kC = DV / 4;     // 16-byte chunks per split row
   constexpr int kP = 256 / kC;   // split rows merged side by side
+  constexpr int kRows = kDirectRows;
   const int b = blockIdx.y;
   const int h = blockIdx.x;
   const int t = threadIdx.x;
@@ -53,6 +62,45 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   __shared__ float den_s[kP];
   __shared__ float4 acc_s[kP][kC];
 
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float den = 0.0f;
+  float M;
+  bool empty;
+  if constexpr (kDirect) {
+    // rows sg + kP j of this thread's group, all loaded at once
+    float lr[kRows];
+    float4 vr[kRows];
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+      const int r = sg + kP * j;
+      lr[j] = r < max_splits ? lse[r] : -INFINITY;
+      vr[j] = r < max_splits ? op[static_cast<int64_t>(r) * kC + ch] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+      if (sg + kP * j >= n) lr[j] = -INFINITY;  // past the request's length
+      mx = fmaxf(mx, lr[j]);
+    }
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    empty = (M == -INFINITY);
+    if (!empty) {
+#pragma unroll
+      for (int j = 0; j < kRows; ++j) {
+        if (lr[j] != -INFINITY) {  // a row that holds a partial
+          const float w = exp2f((lr[j] - M) * kLog2e);
+          den += w;
+          acc.x += w * vr[j].x;
+          acc.y += w * vr[j].y;
+          acc.z += w * vr[j].z;
+          acc.w += w * vr[j].w;
+        }
+      }
+    }
+  } else {
   // the first 256 rows' lse, kept for the listing below
   const float lse0 = t < n ? lse[t] : -INFINITY;
   float mx = lse0;
@@ -60,11 +108,9 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if (lane == 0) red[wave] = mx;
   __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const bool empty = (M == -INFINITY);
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  empty = (M == -INFINITY);
 
-  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  float den = 0.0f;
   if (!empty) {
     for (int base = 0; base < n; base += 256) {
       const int c = base + t;
@@ -98,6 +144,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
       __syncthreads();  // the list is read before the next round writes it
     }
   }
+  }
   acc_s[sg][ch] = acc;
   if (ch == 0) den_s[sg] = den;
   __syncthreads();
@@ -126,9 +173,15 @@ template <int DV>
 int launch(const float* o_part, const float* lse_part, const int32_t* seq_lens, int batch,
            int heads, int split_tokens, int max_splits, int max_seq_len,
            const uint8_t* abort_flags, uint16_t* out, float* lse_out, hipStream_t stream) {
-  combine_kernel<DV><<<dim3(heads, batch), 256, 0, stream>>>(
-      o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags, out,
-      lse_out);
+  constexpr int kP = 256 / (DV / 4);
+  if (max_splits <= kP * kDirectRows)
+    combine_kernel<DV, true><<<dim3(heads, batch), 256, 0, stream>>>(
+        o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags, out,
+        lse_out);
+  else
+    combine_kernel<DV, false><<<dim3(heads, batch), 256, 0, stream>>>(
+        o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags, out,
+        lse_out);
   return pkv::launch_status();
 }
 

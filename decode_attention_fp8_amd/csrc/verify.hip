@@ -80,18 +80,27 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(const uint32_t* __rest
 // 16 values, chunk i taken by thread i (i < 256 per round). With scales set
 // at append, a row's dim / 16 threads are consecutive lanes of one wave (a
 // power of two, aligned) and share the row's largest magnitude by shuffles.
+// The 16 values (32 bytes) of chunk i of a new token's rows.
+struct Chunk {
+  uint4 w0, w1;
+};
+
+__device__ __forceinline__ Chunk load_chunk(const uint16_t* __restrict__ src, int dim, int chunks,
+                                            int i) {
+  const int h = i / chunks;
+  const int c = i - h * chunks;
+  return Chunk{*reinterpret_cast<const uint4*>(src + h * dim + c * 16),
+               *reinterpret_cast<const uint4*>(src + h * dim + c * 16 + 8)};
+}
+
 template <bool kE4M3, bool kRows>
-__device__ __forceinline__ void append_token(const uint16_t* __restrict__ src, uint8_t* pool,
-                                             const float* scale, float* row_scale, int heads,
-                                             int dim, int pool_dim, int page_size, int64_t page,
-                                             int row) {
-  const int chunks = dim / 16;
-  const int total = heads * chunks;
-  for (int i = threadIdx.x; i < total; i += kThreads) {
+__device__ __forceinline__ void store_chunk(const Chunk& v, int i, uint8_t* pool, const float* scale,
+                                            float* row_scale, int heads, int chunks, int pool_dim,
+                                            int page_size, int64_t page, int row) {
+  {
     const int h = i / chunks;
     const int c = i - h * chunks;
-    const uint4 w0 = *reinterpret_cast<const uint4*>(src + h * dim + c * 16);
-    const uint4 w1 = *reinterpret_cast<const uint4*>(src + h * dim + c * 16 + 8);
+    const uint4 w0 = v.w0, w1 = v.w1;
     const int64_t dst = ((page * heads + h) * page_size + row) * pool_dim + c * 16;
     if constexpr (kE4M3) {
       float s;
@@ -112,6 +121,18 @@ __device__ __forceinline__ void append_token(const uint16_t* __restrict__ src, u
   }
 }
 
+template <bool kE4M3, bool kRows>
+__device__ __forceinline__ void append_token(const uint16_t* __restrict__ src, uint8_t* pool,
+                                             const float* scale, float* row_scale, int heads,
+                                             int dim, int pool_dim, int page_size, int64_t page,
+                                             int row) {
+  const int chunks = dim / 16;
+  const int total = heads * chunks;
+  for (int i = threadIdx.x; i < total; i += kThreads)
+    store_chunk<kE4M3, kRows>(load_chunk(src, dim, chunks, i), i, pool, scale, row_scale, heads,
+                              chunks, pool_dim, page_size, page, row);
+}
+
 struct Pool {
   uint8_t* pool;
   const float* scale;
@@ -129,19 +150,39 @@ __global__ void __launch_bounds__(kThreads) verify_append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ slot, Pool kp, Pool vp, int heads, int64_t n_slots) {
   const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  // the slot and, when each pool's chunks fit one pass, the new token's
+  // values are loaded before the check, so their latency passes with it
+  // (they are stored only if the request stands)
+  const int32_t s = slot[b];
+  const uint16_t* ksrc = k_new + static_cast<int64_t>(b) * heads * kp.dim;
+  const uint16_t* vsrc = v_new ? v_new + static_cast<int64_t>(b) * heads * vp.dim : nullptr;
+  const int kch = kp.dim / 16, vch = vp.dim / 16;
+  const int ktot = heads * kch, vtot = vsrc ? heads * vch : 0;
+  const bool one_pass = ktot <= kThreads && vtot <= kThreads;
+  Chunk kv{}, vv{};
+  if (one_pass && i < ktot) kv = load_chunk(ksrc, kp.dim, kch, i);
+  if (one_pass && i < vtot) vv = load_chunk(vsrc, vp.dim, vch, i);
   const int bad = check_request(page_tags, num_pages, page_size, block_table, expected, seq_lens,
                                 max_pages, b);
   if (threadIdx.x == 0) abort_out[b] = bad ? 1 : 0;
-  const int32_t s = slot[b];
   if (bad || s < 0 || s >= n_slots) return;
   const int64_t page = s / page_size;
   const int row = s - static_cast<int>(page) * page_size;
-  append_token<kE4M3, kRows>(k_new + static_cast<int64_t>(b) * heads * kp.dim, kp.pool, kp.scale,
-                             kp.row_scale, heads, kp.dim, kp.pool_dim, page_size, page, row);
-  if (v_new)
-    append_token<kE4M3, kRows>(v_new + static_cast<int64_t>(b) * heads * vp.dim, vp.pool,
-                               vp.scale, vp.row_scale, heads, vp.dim, vp.pool_dim, page_size,
-                               page, row);
+  if (one_pass) {
+    if (i < ktot)
+      store_chunk<kE4M3, kRows>(kv, i, kp.pool, kp.scale, kp.row_scale, heads, kch, kp.pool_dim,
+                                page_size, page, row);
+    if (i < vtot)
+      store_chunk<kE4M3, kRows>(vv, i, vp.pool, vp.scale, vp.row_scale, heads, vch, vp.pool_dim,
+                                page_size, page, row);
+    return;
+  }
+  append_token<kE4M3, kRows>(ksrc, kp.pool, kp.scale, kp.row_scale, heads, kp.dim, kp.pool_dim,
+                             page_size, page, row);
+  if (vsrc)
+    append_token<kE4M3, kRows>(vsrc, vp.pool, vp.scale, vp.row_scale, heads, vp.dim, vp.pool_dim,
+                               page_size, page, row);
 }
 
 }  // namespace
