@@ -331,6 +331,47 @@ def test_mla_score_jump_far_above_the_first_tile(kv):
 
 
 @pytest.mark.parametrize("kv", ["fp8", "bf16"])
+def test_mla_huge_context_chunks_zero_query(kv):
+    """One request of 8,400,037 tokens (131,251 pages of 64, 4.8 GB as e4m3):
+    the 128-head latent kernel's equal shares then exceed 512 tiles, so a
+    segment is taken in several chunks of page ids. Every row of page p is
+    one of seven random patterns (p mod 7). With q = 0 every score is 0, so
+    the output is the mean of the rows' first 512 values, a closed form over
+    the patterns' token counts, and lse = ln L; a dropped or doubled tile
+    moves both."""
+    hq, dk, dv, P, L = 128, 576, 512, 64, 8_400_037
+    n_pages = -(-L // P)
+    rng = np.random.default_rng(23)
+    cache = pkv.allocate_cache(n_pages, 1, P, dk, dv, kv, latent=True, device=dev, poison=False)
+    which = torch.arange(n_pages, device=dev) % 7
+    if kv == "fp8":
+        pat = rng.integers(0, 256, size=(7, dk), dtype=np.uint8)
+        pat[(pat & 0x7F) == 0x7F] = 0x38                      # no NaN codes
+        scale = np.float32(0.25)
+        vals = e4m3.DECODE[pat] * np.float64(scale)
+        cache.k_pool.view(n_pages, P, dk)[:] = torch.from_numpy(pat).to(dev)[which][:, None, :]
+        cache.k_scale.fill_(float(scale))
+        cache.v_scale = cache.k_scale
+    else:
+        pat = torch.from_numpy(rng.standard_normal((7, dk)).astype(np.float32)).to(torch.bfloat16)
+        vals = pat.double().numpy()
+        cache.k_pool.view(n_pages, P, dk)[:] = pat.to(dev)[which][:, None, :]
+    # tokens per pattern: whole pages, then the last page's L - P (n_pages - 1)
+    counts = np.bincount(np.arange(n_pages) % 7, minlength=7).astype(np.float64) * P
+    counts[(n_pages - 1) % 7] -= n_pages * P - L
+    ref = (counts[:, None] * vals[:, :dv]).sum(axis=0) / L
+    bt = torch.arange(n_pages, dtype=torch.int32, device=dev).view(1, n_pages)
+    lens = torch.tensor([L], dtype=torch.int32, device=dev)
+    split = pkv.pkv_suggest_split(cache, hq, 1, L, L)
+    ds = pkv.DecodeStep(cache, hq, 1, L, split, verify=False)
+    q = torch.zeros((1, hq, dk), dtype=torch.bfloat16, device=dev)
+    out = ds.attend(q, bt, lens, 1 / math.sqrt(dk), None).float().cpu().numpy()[0]
+    assert_close(out, np.broadcast_to(ref, out.shape), f"mla huge context {kv}")
+    lse = ds.lse.cpu().numpy()[0]
+    assert np.allclose(lse, math.log(L), rtol=0, atol=1e-4), (lse.min(), lse.max(), math.log(L))
+
+
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
 @pytest.mark.parametrize("jumps", [((128 + 5, 7.0),), ((128 + 2, 5.0), (128 + 5, 7.0)),
                                    ((128 + 1, 7.0), (128 + 6, 5.0)), ((160 + 12, 6.0),)],
                          ids=["one_token_upper_half", "halves_different_upper_higher",
