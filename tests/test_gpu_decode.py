@@ -199,14 +199,33 @@ def test_group_sizes_and_head_dims(G, dk, kv):
     _check_requests(st, range(w.batch))
 
 
-def test_empty_request_gives_zero_and_neg_inf_lse():
-    w = W.custom("e", 79, [40, 40], hq=4, hkv=1, dk=64, dv=64, page=16)
-    st = State(w, "fp8")
-    st.seq_lens[1] = 0
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+@pytest.mark.parametrize("shape", [dict(hq=4, hkv=1, dk=64, dv=64, page=16),
+                                   dict(hq=8, hkv=1, dk=128, dv=128, page=16),
+                                   dict(hq=128, hkv=1, dk=576, dv=512, page=64, latent=True)],
+                         ids=["generic", "grouped_query", "latent"])
+@pytest.mark.parametrize("empty", [[1], [0, 1, 2]], ids=["one_empty", "all_empty"])
+def test_empty_request_gives_zero_and_neg_inf_lse(shape, empty, kv):
+    """Requests of length 0 give exactly 0 and lse = -inf; the others still
+    match the oracle. With every request empty the latent kernel's launch
+    has no tiles at all."""
+    w = W.custom("e", 79, [40, 130, 70], **shape)
+    st = State(w, kv)
+    for b in empty:
+        st.seq_lens[b] = 0
     out = st.step.run(st.q, st.block_table, st.expected, st.seq_lens, w.sm_scale)
     torch.cuda.synchronize()
-    assert torch.all(out[1] == 0)
-    assert torch.all(torch.isneginf(st.step.lse[1]))
+    for b in empty:
+        assert torch.all(out[b] == 0)
+        assert torch.all(torch.isneginf(st.step.lse[b]))
+    rest = [b for b in range(w.batch) if b not in empty]
+    if rest:
+        ks, vs = step.scales(w, kv)
+        q = w.q_values().double().numpy()
+        got = out.float().cpu().numpy()
+        for b in rest:
+            o_ref, _ = step.request_output(w, b, kv, ks, vs, False, np.arange(w.num_kv_heads), q[b])
+            assert_close(got[b], o_ref, f"empty-neighbour request {b}")
 
 
 def test_every_e4m3_code_decodes_exactly():
