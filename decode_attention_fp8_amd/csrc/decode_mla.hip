@@ -839,11 +839,16 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
             return Conv{lds + (t % kSlots8) * kTile8 + (32 * xh + r) * kDk + 8 * c8,
                         dst0 + r * 128 + ((c8 ^ wswz(r)) << 4), 32 * xh + r < nv};
           };
-          auto conv_step = [&](const Conv& c, int k) __attribute__((always_inline)) {
-            uint2 w = *reinterpret_cast<const uint2*>(c.src + 64 * k);
+          auto conv_read = [&](const Conv& c, int k) __attribute__((always_inline)) {
+            return *reinterpret_cast<const uint2*>(c.src + 64 * k);
+          };
+          auto conv_write = [&](const Conv& c, int k, uint2 w) __attribute__((always_inline)) {
             w.x = c.in ? w.x : 0u;
             w.y = c.in ? w.y : 0u;
             *reinterpret_cast<uint4*>(c.dst + kGroup16 * k) = __builtin_bit_cast(uint4, fp8x8_to_bf16(w.x, w.y));
+          };
+          auto conv_step = [&](const Conv& c, int k) __attribute__((always_inline)) {
+            conv_write(c, k, conv_read(c, k));
           };
           auto convert = [&](int t, int xh, int nv, uint8_t* dst0) __attribute__((always_inline)) {
             const Conv c = conv_of(t, xh, nv, dst0);
@@ -893,8 +898,19 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
               // nothing reads)
               const int un = u + 1;
               const Conv c = conv_of(un >> 1, un & 1, nv_of(un >> 1), nxt);
+              // the code reads run three steps ahead of their conversion, so
+              // a conversion never waits on a read just issued
+              constexpr int kCAhead = 3;
+              uint2 cw[kCAhead];
+#pragma unroll
+              for (int k = 0; k < kCAhead; ++k) cw[k] = conv_read(c, k);
               pv_half(cur, [&](int j) __attribute__((always_inline)) {
-                if (j % 3 == 2 && j / 3 < 9) conv_step(c, j / 3);
+                if (j % 3 == 2 && j / 3 < 9) {
+                  const int k = j / 3;
+                  const uint2 w = cw[k % kCAhead];
+                  if (k + kCAhead < 9) cw[k % kCAhead] = conv_read(c, k + kCAhead);
+                  conv_write(c, k, w);
+                }
               });
             } else {
               if (more) {
