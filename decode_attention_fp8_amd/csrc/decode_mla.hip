@@ -49,7 +49,6 @@ typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
 typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;
 constexpr float kMInit = -1e30f;
@@ -397,8 +396,9 @@ __global__ void __launch_bounds__(256) decode_mla_kernel(DecodeParams p, int n_s
 }
 
 // ---------------------------------------------------------------------------
-// Wide variant for query heads in multiples of 128, e4m3 or bf16 cache: one
-// workgroup of 4 waves takes all 128 heads of a range of splits. MFMA
+// Wide variant for query heads in multiples of 128, bf16 cache (the e4m3
+// cache has its own kernel below): one workgroup of 4 waves takes all 128
+// heads of a range of splits. MFMA
 // 32x32x16 (bf16 in, fp32 out):
 //   A lane l: row l%32, k 8(l/32)..+7;  B lane l: column l%32, k 8(l/32)..+7;
 //   D lane l, element i: row 8(i/4) + 4(l/32) + i%4, column l%32.
@@ -412,15 +412,10 @@ __global__ void __launch_bounds__(256) decode_mla_kernel(DecodeParams p, int n_s
 // accumulators live in the accumulation registers. One accumulator per
 // 32-token block of S^T suffices: dependent MFMAs issue back to back.
 //
-// Every MFMA reads bf16 operands from a bf16 copy of 32 rows in LDS. An e4m3
-// tile arrives by direct-to-LDS loads into one of two code slots (the next
-// tile loads while one is used) and each half is converted once, by all
-// four waves together, into one of two bf16 buffers: the conversion of half
-// u + 1 is interleaved with the MFMAs of half u's P V (a step after every
-// third MFMA), so it costs issue slots the MFMAs leave free. A bf16 cache
-// arrives straight in a four-slot ring of bf16 halves (three halves load
-// while one is used), already in the layout the operands are read in. The
-// cache loads of a later half or tile are spread over the MFMAs of a QK^T.
+// The cache arrives by direct-to-LDS loads in a four-slot ring of 32-row
+// halves (three halves load while one is used), already in the layout the
+// operands are read in. The loads of a later half are spread over the MFMAs
+// of a QK^T.
 //
 // bf16 half layout (32 rows of 72 chunks of 16 bytes): nine 4 KB groups,
 // group g holding chunks 8 g .. 8 g + 7 of every row, row r at 128 r of the
@@ -428,9 +423,8 @@ __global__ void __launch_bounds__(256) decode_mla_kernel(DecodeParams p, int n_s
 // = bit 1 | bit 2 << 1 | (bit 1 ^ bit 3) << 2 of r. The bank group (of 16
 // four-bank groups) of position p in row r is then 8 (r & 1) + p; with this
 // swizzle the 16 rows of one pass of a K operand read (16 consecutive rows,
-// one chunk), the 4 rows x 4 chunks of one pass of a transposing V read and
-// the 2 rows x 8 chunks of one pass of the e4m3 conversion's writes all fall
-// on distinct bank groups (checked exhaustively). Every lane's offsets are a
+// one chunk) and the 4 rows x 4 chunks of one pass of a transposing V read
+// fall on distinct bank groups (checked exhaustively). Every lane's offsets are a
 // fixed base plus immediates: a cache load fills 1 KB of a group (8 rows x
 // 128 bytes of the page), an operand read steps 4 KB per 8 chunks.
 //
@@ -454,7 +448,6 @@ constexpr int kVmcnt0 = 0x0F70;              // s_waitcnt vmcnt(0), other counte
 constexpr int kTile16 = kTile * kRow16;      // 72 KB: a bf16 page
 constexpr int kTile8 = kTile * kDk;          // 36 KB of codes
 constexpr int kDma = 9;                      // loads per wave per code tile or bf16 half
-constexpr int kSlots8 = 2;                   // code tiles in the ring
 constexpr int kSlots16 = 4;                  // bf16 halves in the ring
 
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
@@ -538,13 +531,11 @@ __device__ __forceinline__ int64_t snap(const DecodeParams& p, int64_t x, int64_
   return start + jj;
 }
 
-template <bool kE4M3>
 __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p, int head_groups,
                                                                  int n_ranges) {
-  // e4m3: [code tiles: 2 x 36 KB][bf16 halves: 2 x 36 KB]; bf16: [ring of 4 bf16 halves:
-  // 4 x 36 KB]; both then the half's numerators P: 128 heads x 32 tokens of bf16, rows
-  // padded to 80 bytes
-  constexpr int kTiles = kE4M3 ? kSlots8 * kTile8 + 2 * kHalf16 : kSlots16 * kHalf16;
+  // [ring of 4 bf16 halves: 4 x 36 KB], then the half's numerators P: 128
+  // heads x 32 tokens of bf16, rows padded to 80 bytes
+  constexpr int kTiles = kSlots16 * kHalf16;
   constexpr int kPRow = 80;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kTiles + 128 * kPRow];
   __shared__ int32_t pages[kMaxUnitTiles];
@@ -566,8 +557,7 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
   const int64_t s1 = snap(p, (ri + 1) * total / n_ranges, total, tps);
   if (s0 >= s1) return;
 
-  const float qk_scale = (kE4M3 ? p.k_scale[0] : 1.0f) * p.sm_scale_log2;
-  const float o_scale = kE4M3 ? p.v_scale[0] : 1.0f;
+  const float qk_scale = p.sm_scale_log2;
   const uint8_t* kpool = static_cast<const uint8_t*>(p.k_pool);
   const uint32_t lds0 = lds_addr(lds);
   uint8_t* pbuf = lds + kTiles;
@@ -604,7 +594,6 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
   const uint32_t poff = static_cast<uint32_t>(col * kPRow + 16 * hh);
   // bf16 cache loads: lane l of wave w takes row 8 w + l / 8 of a half, the
   // chunk that lands at position l % 8 of that row's group
-  const uint32_t code_off = static_cast<uint32_t>(16 * lane);
   const int dma_row = 8 * wave + (lane >> 3);
   const uint32_t dma_off = static_cast<uint32_t>(dma_row * kRow16 + (((lane & 7) ^ wswz(dma_row)) << 4));
 
@@ -790,7 +779,7 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
         };
         auto base_of = [&](int page) __attribute__((always_inline)) {
           if (page < 0 || page >= p.num_pages) page = 0;  // loaded but never used
-          return kpool + static_cast<int64_t>(page) * (kE4M3 ? kTile8 : kTile16);
+          return kpool + static_cast<int64_t>(page) * kTile16;
         };
         auto page_base = [&](int t) __attribute__((always_inline)) { return base_of(page_of(t)); };
         // a page id read ahead (kept in a vector register until it is used,
@@ -805,186 +794,61 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
           wg_barrier();  // every head's numerators are in pbuf
           pv_half(buf, [](int) {});
         };
-        if constexpr (kE4M3) {
-          // ---- codes: whole tiles, a plain copy of the page, in two slots;
-          // each half is converted into one of two bf16 buffers while the
-          // half before it is multiplied by V. Load i of tile t (of this
-          // wave's nine):
-          auto issue_one = [&](int t, const uint8_t* base, int i) __attribute__((always_inline)) {
-            const int k = wave + 4 * i;
-            dma16(lds0 + (t % kSlots8) * kTile8 + 1024 * k, code_off, base + 1024 * k);
-          };
-          auto issue = [&](int t) __attribute__((always_inline)) {
-            const uint8_t* base = page_base(t);
+        // ---- bf16: halves of a page, three ahead, straight into the
+        // layout the operands are read in: load i of wave w fills group i,
+        // rows 8 w .. 8 w + 7 (1 KB of LDS), each lane one chunk, reading
+        // 128 bytes of each of 8 rows of the page
+        const int nh = 2 * kn;
+        auto half_base = [&](int h) __attribute__((always_inline)) {
+          return page_base(h >> 1) + (h & 1) * kHalf16;
+        };
+        auto issue_one = [&](int h, const uint8_t* base, int i) __attribute__((always_inline)) {
+          dma16(lds0 + (h % kSlots16) * kHalf16 + 1024 * wave + kGroup16 * i, dma_off, base + 128 * i);
+        };
+        auto issue = [&](int h) __attribute__((always_inline)) {
+          const uint8_t* base = half_base(h);
 #pragma unroll
-            for (int i = 0; i < kDma; ++i) issue_one(t, base, i);
-          };
-          uint8_t* const bf = lds + kSlots8 * kTile8;  // bf16 half u in bf + (u % 2) * kHalf16
-          // rows 32 xh .. 32 xh + 31 of code tile t into bf16 buffer `dst0`:
-          // thread t takes row t / 8 and its chunks t % 8 + 8 k (8 codes
-          // each), so both offsets are a fixed base plus 64 k (codes) and 4
-          // KB k (bf16: group k of the row). A read pass (32 lanes: 4 rows x
-          // 64 bytes, rows 576 bytes apart) and a write pass (16 lanes: 2
-          // rows x 8 chunks) each touch every bank once. Rows past the
-          // context become zeros (V must be finite there); the codes are
-          // selected, not branched on, so the conversion can interleave
-          // with the MFMAs around it.
-          struct Conv {
-            const uint8_t* src;
-            uint8_t* dst;
-            bool in;
-          };
-          auto conv_of = [&](int t, int xh, int nv, uint8_t* dst0) __attribute__((always_inline)) {
-            const int r = tid >> 3, c8 = tid & 7;
-            return Conv{lds + (t % kSlots8) * kTile8 + (32 * xh + r) * kDk + 8 * c8,
-                        dst0 + r * 128 + ((c8 ^ wswz(r)) << 4), 32 * xh + r < nv};
-          };
-          auto conv_read = [&](const Conv& c, int k) __attribute__((always_inline)) {
-            return *reinterpret_cast<const uint2*>(c.src + 64 * k);
-          };
-          auto conv_write = [&](const Conv& c, int k, uint2 w) __attribute__((always_inline)) {
-            w.x = c.in ? w.x : 0u;
-            w.y = c.in ? w.y : 0u;
-            *reinterpret_cast<uint4*>(c.dst + kGroup16 * k) = __builtin_bit_cast(uint4, fp8x8_to_bf16(w.x, w.y));
-          };
-          auto conv_step = [&](const Conv& c, int k) __attribute__((always_inline)) {
-            conv_write(c, k, conv_read(c, k));
-          };
-          auto convert = [&](int t, int xh, int nv, uint8_t* dst0) __attribute__((always_inline)) {
-            const Conv c = conv_of(t, xh, nv, dst0);
-#pragma unroll
-            for (int k = 0; k < 9; ++k) conv_step(c, k);
-          };
-          // half u = 2 t + xh is decoded when its page is in the pool and
-          // it holds tokens of the context
-          const int nu = 2 * kn;
-          issue(0);
-          if (kn > 1) issue(1);
-          if (kn > 1) wait_vm<kDma>();
+          for (int i = 0; i < kDma; ++i) issue_one(h, base, i);
+        };
+        for (int h = 0; h < 3 && h < nh; ++h) issue(h);
+        int pv_cur = page_ahead(0);  // page ids of tiles h / 2 and (h + 3) / 2
+        int pv_far = page_ahead(1);
+        for (int h = 0; h < nh; ++h) {
+          const int later = min(2, nh - 1 - h);  // halves loading behind half h
+          if (later == 2) wait_vm<2 * kDma>();
+          else if (later == 1) wait_vm<kDma>();
           else wait_vm<0>();
-          wg_barrier();  // tile 0's codes are in LDS
-          convert(0, 0, nv_of(0), bf);
-          int pv_cur = page_ahead(0);  // page ids of tiles u / 2 and u / 2 + 2
-          int pv_far = page_ahead(2);
-          for (int u = 0; u < nu; ++u) {
-            wg_barrier();  // half u is converted; pbuf and the other buffer are free
-            const int t = u >> 1;
-            const int page = __builtin_amdgcn_readfirstlane(pv_cur);
-            const int page_far = __builtin_amdgcn_readfirstlane(pv_far);
-            pv_cur = page_ahead((u + 1) >> 1);
-            pv_far = page_ahead(((u + 1) >> 1) + 2);
-            // the slot of tile t takes tile t + 2 once its second half is
-            // converted (before the barrier above), during this half's QK^T
-            const bool more = (u & 1) && t + 2 < kn;
-            const uint8_t* nbase = more ? base_of(page_far) : nullptr;
-            const bool next = u + 1 < nu;
-            // the next half opens tile t + 1: its codes must have landed
-            // (tile t + 2 may still be loading behind it)
-            const bool wait_next = next && (u & 1);
-            uint8_t* const cur = bf + (u & 1) * kHalf16;
-            uint8_t* const nxt = bf + ((u + 1) & 1) * kHalf16;
-            if (page >= 0 && page < p.num_pages && 32 * (u & 1) < nv_of(t)) {
-              const int nv = nv_of(t);
-              qk_half(cur, u & 1, nv, [&](int ks) __attribute__((always_inline)) {
-                if (more && (ks & 3) == 3) issue_one(t + 2, nbase, ks >> 2);
-              });
-              if (wait_next) {
-                if (t + 2 < kn) wait_vm<kDma>();
-                else wait_vm<0>();
-              }
-              wg_barrier();  // every head's numerators are in pbuf; tile t + 1 is in LDS
-              // the next half's conversion, one step after every third MFMA
-              // (after the last half it fills the spare buffer with bytes
-              // nothing reads)
-              const int un = u + 1;
-              const Conv c = conv_of(un >> 1, un & 1, nv_of(un >> 1), nxt);
-              // the code reads run three steps ahead of their conversion, so
-              // a conversion never waits on a read just issued
-              constexpr int kCAhead = 3;
-              uint2 cw[kCAhead];
+          wg_barrier();  // half h is in LDS; every wave is done with half h - 1 and pbuf
+          const int page = __builtin_amdgcn_readfirstlane(pv_cur);
+          const int page_far = __builtin_amdgcn_readfirstlane(pv_far);
+          pv_cur = page_ahead((h + 1) >> 1);
+          pv_far = page_ahead((h + 4) >> 1);
+          // half h + 3 goes to the slot of half h - 1, during half h's QK^T
+          const bool more = h + 3 < nh;
+          const uint8_t* nbase = more ? base_of(page_far) + ((h + 3) & 1) * kHalf16 : nullptr;
+          const int t = h >> 1, xh = h & 1;
+          const int nv = nv_of(t);
+          if (!(page >= 0 && page < p.num_pages && 32 * xh < nv)) {
+            if (more) {
 #pragma unroll
-              for (int k = 0; k < kCAhead; ++k) cw[k] = conv_read(c, k);
-              pv_half(cur, [&](int j) __attribute__((always_inline)) {
-                if (j % 3 == 2 && j / 3 < 9) {
-                  const int k = j / 3;
-                  const uint2 w = cw[k % kCAhead];
-                  if (k + kCAhead < 9) cw[k % kCAhead] = conv_read(c, k + kCAhead);
-                  conv_write(c, k, w);
-                }
-              });
-            } else {
-              if (more) {
-#pragma unroll
-                for (int i = 0; i < kDma; ++i) issue_one(t + 2, nbase, i);
-              }
-              if (wait_next) {
-                if (t + 2 < kn) wait_vm<kDma>();
-                else wait_vm<0>();
-              }
-              wg_barrier();  // tile t + 1 is in LDS for every wave
-              if (next) {
-                const int un = u + 1;
-                convert(un >> 1, un & 1, nv_of(un >> 1), nxt);
-              }
+              for (int i = 0; i < kDma; ++i) issue_one(h + 3, nbase, i);
             }
-          }
-        } else {
-          // ---- bf16: halves of a page, three ahead, straight into the
-          // layout the operands are read in: load i of wave w fills group i,
-          // rows 8 w .. 8 w + 7 (1 KB of LDS), each lane one chunk, reading
-          // 128 bytes of each of 8 rows of the page
-          const int nh = 2 * kn;
-          auto half_base = [&](int h) __attribute__((always_inline)) {
-            return page_base(h >> 1) + (h & 1) * kHalf16;
-          };
-          auto issue_one = [&](int h, const uint8_t* base, int i) __attribute__((always_inline)) {
-            dma16(lds0 + (h % kSlots16) * kHalf16 + 1024 * wave + kGroup16 * i, dma_off, base + 128 * i);
-          };
-          auto issue = [&](int h) __attribute__((always_inline)) {
-            const uint8_t* base = half_base(h);
-#pragma unroll
-            for (int i = 0; i < kDma; ++i) issue_one(h, base, i);
-          };
-          for (int h = 0; h < 3 && h < nh; ++h) issue(h);
-          int pv_cur = page_ahead(0);  // page ids of tiles h / 2 and (h + 3) / 2
-          int pv_far = page_ahead(1);
-          for (int h = 0; h < nh; ++h) {
-            const int later = min(2, nh - 1 - h);  // halves loading behind half h
-            if (later == 2) wait_vm<2 * kDma>();
-            else if (later == 1) wait_vm<kDma>();
-            else wait_vm<0>();
-            wg_barrier();  // half h is in LDS; every wave is done with half h - 1 and pbuf
-            const int page = __builtin_amdgcn_readfirstlane(pv_cur);
-            const int page_far = __builtin_amdgcn_readfirstlane(pv_far);
-            pv_cur = page_ahead((h + 1) >> 1);
-            pv_far = page_ahead((h + 4) >> 1);
-            // half h + 3 goes to the slot of half h - 1, during half h's QK^T
-            const bool more = h + 3 < nh;
-            const uint8_t* nbase = more ? base_of(page_far) + ((h + 3) & 1) * kHalf16 : nullptr;
-            const int t = h >> 1, xh = h & 1;
-            const int nv = nv_of(t);
-            if (!(page >= 0 && page < p.num_pages && 32 * xh < nv)) {
-              if (more) {
-#pragma unroll
-                for (int i = 0; i < kDma; ++i) issue_one(h + 3, nbase, i);
+          } else {
+            uint8_t* buf = lds + (h % kSlots16) * kHalf16;
+            if (nv < 32 * xh + 32) {
+              // rows past the context hold stale bytes; V must be finite there
+              const int r0 = nv - 32 * xh;
+              const int per_group = (32 - r0) * 8;  // chunks of those rows in a group
+              for (int i = tid; i < 9 * per_group; i += 256) {
+                const int g = i / per_group, rem = i - g * per_group;
+                *reinterpret_cast<uint4*>(buf + g * kGroup16 + (r0 + (rem >> 3)) * 128 + 16 * (rem & 7)) =
+                    make_uint4(0u, 0u, 0u, 0u);
               }
-            } else {
-              uint8_t* buf = lds + (h % kSlots16) * kHalf16;
-              if (nv < 32 * xh + 32) {
-                // rows past the context hold stale bytes; V must be finite there
-                const int r0 = nv - 32 * xh;
-                const int per_group = (32 - r0) * 8;  // chunks of those rows in a group
-                for (int i = tid; i < 9 * per_group; i += 256) {
-                  const int g = i / per_group, rem = i - g * per_group;
-                  *reinterpret_cast<uint4*>(buf + g * kGroup16 + (r0 + (rem >> 3)) * 128 + 16 * (rem & 7)) =
-                      make_uint4(0u, 0u, 0u, 0u);
-                }
-                wg_barrier();
-              }
-              half(buf, xh, nv, [&](int ks) __attribute__((always_inline)) {
-                if (more && (ks & 3) == 3) issue_one(h + 3, nbase, ks >> 2);
-              });
+              wg_barrier();
             }
+            half(buf, xh, nv, [&](int ks) __attribute__((always_inline)) {
+              if (more && (ks & 3) == 3) issue_one(h + 3, nbase, ks >> 2);
+            });
           }
         }
         wg_barrier();  // every wave is done with the slots and the page ids
@@ -1036,12 +900,540 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
       for (int i = 0; i < 16; ++i) {
         const int hl = 32 * hb + 8 * (i >> 2) + hq + (i & 3);
         const float lh = l_all[hl];
-        const float f = lh > 0.0f ? o_scale / lh : 0.0f;
+        const float f = lh > 0.0f ? 1.0f / lh : 0.0f;
         float* dst = dst0 + hl * head_stride;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) dst[32 * nb] = O[hb][nb][i] * f;
       }
     wg_barrier();  // l_all is read before the next segment writes it
+  }
+}
+
+// ---------------------------------------------------------------------------
+// e4m3 cache on fp8 MFMA. The cache codes are e4m3 values and gfx950's
+// scaled MFMA 32x32x64 (v_mfma_scale_f32_32x32x64_f8f6f4) multiplies e4m3
+// operands directly, each 32-value block of an operand row times a power of
+// two given per lane, with fp32 accumulation. So neither contraction needs
+// the codes converted:
+//  - QK^T: S^T = K Q^T with K the codes read straight from the tile in LDS
+//    (scale 1) and q split once per segment into two e4m3 parts, q = hi 2^e
+//    + lo 2^(e - 4) with e per head from the head's largest |q|. hi keeps
+//    four significant bits and lo the next four, so the pair holds every
+//    bf16 q exactly (apart from values below 2^(e - 13), far under the
+//    head's largest). Two MFMAs (hi, lo) per k-step of 64 dims cost the
+//    time of one bf16 MFMA of the same size.
+//  - P V: the numerators of a head and half tile are scaled by 2^-e, e =
+//    floor of the half's largest exponent, so they lie in [0, 2), and split
+//    the same way into hi and lo parts (eight significant bits in all, as a
+//    bf16 numerator has); V is the codes read with ds_read_b64_tr_b8.
+// The scaled MFMA adds the products of each run of eight k-values aligned to
+// the run's largest, keeping about 13 bits below it (measured: a product
+// under 2^-13 of its run's largest is dropped), then adds runs in fp32; the
+// score error this adds is at most about 2^-10 of the sum of |q_d k_d| and
+// measured near 2e-5 of it on normal data.
+//
+// MFMA 32x32x64 operand layout (measured): lane l supplies row (A) or
+// column (B) l % 32 and 32 bytes; byte j < 16 of lane l is k-value 16 (l /
+// 32) + j, byte j >= 16 is k-value 32 + 16 (l / 32) + j - 16; the scale of
+// lane l % 32 multiplies k-values 0..31, that of lane l % 32 + 32 k-values
+// 32..63. D as for the bf16 MFMA: lane l, element i is row 8 (i / 4) + 4 (l
+// / 32) + i % 4, column l % 32. Only the pairing of A's and B's bytes
+// matters, so each side assigns its own data to bytes the same way:
+//  - QK^T (M = 32 tokens, N = 32 heads, 9 k-steps of 64 dims): byte j of
+//    lane l is dim 64 ks + 32 (l / 32) + j of the lane's token or head;
+//  - P V (M = 32 heads, N = 32 dims, K = the 64 tokens of a tile): byte j of
+//    lane l is token 8 (j' / 4) + 4 (l / 32) + j' % 4 of the tile's first
+//    half for j < 16 (j' = j) and of its second half for j >= 16 (j' = j -
+//    16) -- exactly the tokens whose scores QK^T leaves in lane l's
+//    accumulators (element i = j'), so the numerators go from the QK^T
+//    accumulators to the A operand without leaving the lane, and the scale
+//    of lane l % 32 (first half) and of lane l % 32 + 32 (second half) are
+//    the two halves' own.
+//
+// Work split as in the bf16 wide kernel (one workgroup per compute unit and
+// 128-head group, balanced ranges of whole splits), but every wave owns 32
+// heads end to end: their q, scores, numerators and all 512 dims of their
+// output rows (256 accumulation registers). Waves share only the code tiles:
+// a ring of four 36 KB tiles, three loading while one is used, and one
+// barrier per 64-token tile.
+//
+// Code tile layout in LDS (64 rows, one per token): dims 0..511 in four 8 KB
+// groups, group G holding 16-byte chunks 8 G .. 8 G + 7 of every row, row r
+// at 128 r, chunk c at position (c % 8) ^ f8swz(r); the 64 rope dims in a 4
+// KB group after them, row r at 64 r, chunk c at (c - 32) ^ f8swz4(r). K
+// operand reads (16 rows, one chunk per pass) and the transposing V reads
+// (8 rows, two chunks per pass) hit distinct banks (checked exhaustively).
+// A direct-to-LDS load fills 1 KB of one group (8 rows, or 16 rope rows) and
+// each lane fetches the global chunk its LDS position holds.
+constexpr int kF8Slots = 3;             // code tiles in the ring
+constexpr int kF8Ahead = kF8Slots - 1;  // tiles loading while one is used
+constexpr int kQLds = 1;                // trailing k-steps whose q codes live in LDS
+constexpr int kQReg = 9 - kQLds;        // k-steps whose q codes live in registers
+constexpr int kF8Group = 8192;   // 64 rows x 128 bytes
+constexpr int kF8Rope = 32768;   // the rope group: 64 rows x 64 bytes
+constexpr float kF8MinExp = -100.0f;  // lowest numerator scale exponent
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+// compile-time choice between two straight-line bodies
+template <bool B>
+struct FullTag {
+  static constexpr bool value = B;
+};
+
+__device__ __forceinline__ int f8swz(int r) {
+  return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2) | ((r >> 2) & 1);
+}
+__device__ __forceinline__ int f8swz4(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ floatx16_t mfma_f8(const v8i_t& a, const v8i_t& b, const floatx16_t& c,
+                                              int scale_a, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+}
+
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float(static_cast<uint32_t>(127 + e) << 23); }
+
+// Four floats x (already times 2^-e) -> their e4m3 codes hi (one word) and
+// the codes lo of the remainders times 16 (one word).
+__device__ __forceinline__ void split4(float x0, float x1, float x2, float x3, uint32_t& hi, uint32_t& lo) {
+  int h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  h = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, h, true);
+  const auto d0 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+  const auto d1 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+  int o = __builtin_amdgcn_cvt_pk_fp8_f32((x0 - d0[0]) * 16.0f, (x1 - d0[1]) * 16.0f, 0, false);
+  o = __builtin_amdgcn_cvt_pk_fp8_f32((x2 - d1[0]) * 16.0f, (x3 - d1[1]) * 16.0f, o, true);
+  hi = static_cast<uint32_t>(h);
+  lo = static_cast<uint32_t>(o);
+}
+
+__global__ void __launch_bounds__(256, 1) decode_mla_f8_kernel(DecodeParams p, int head_groups,
+                                                               int n_ranges) {
+  // code tiles, then per wave the q codes of the last kQLds k-steps (4 KB
+  // each: hi words 0-3, hi 4-7, lo 0-3, lo 4-7, each 64 lanes x 16 bytes)
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kF8Slots * kTile8 + 4 * kQLds * 4096];
+  __shared__ int32_t pages[kMaxUnitTiles];
+  __shared__ int vote[4];
+
+  const int hg = static_cast<int>(blockIdx.x) % head_groups;
+  const int ri = static_cast<int>(blockIdx.x) / head_groups;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5;   // which 32-byte half of a k-step (QK), which token quads (P V)
+  const int col = lane & 31;  // head (QK^T, A of P V) or dim (B and D of P V)
+  const int tps = p.split_tokens / kTile;
+
+  const int64_t total = launch_tiles(p);
+  const int64_t s0 = snap(p, ri * total / n_ranges, total, tps);
+  const int64_t s1 = snap(p, (ri + 1) * total / n_ranges, total, tps);
+  if (s0 >= s1) return;
+
+  const float qk_scale = p.k_scale[0] * p.sm_scale_log2;
+  const float o_scale = p.v_scale[0];
+  const uint8_t* kpool = static_cast<const uint8_t*>(p.k_pool);
+  const uint32_t lds0 = lds_addr(lds);
+  const int h_base = hg * 128 + wave * 32;
+
+  // Per-lane LDS offsets in a tile (the swizzles depend on the row modulo
+  // 16, so a row 16 or 32 further is a plain add):
+  // K of k-step ks < 8, 16-byte half x: row col (+ 32 for the second token
+  // half), chunk 4 ks + 2 hh + x, in group ks / 2 at position (4 (ks % 2) +
+  // 2 hh + x) ^ f8swz(col); the rope k-step: chunks 32 + 2 hh + x.
+  uint32_t koff[2][2], kro[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      koff[j][x] = static_cast<uint32_t>(128 * col + 16 * ((4 * j + 2 * hh + x) ^ f8swz(col)));
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+    kro[x] = static_cast<uint32_t>(kF8Rope + 64 * col + 16 * ((2 * hh + x) ^ f8swz4(col)));
+  // V of dim block nb (dims 32 nb + col), read x (bytes 8 x .. 8 x + 7 of the
+  // operand): the lane pair 2 e, 2 e + 1 of each 16-lane group addresses row
+  // 32 (x / 2) + 16 (x % 2) + rv, rv = 8 (e / 4) + 4 hh + e % 4, at chunk 2 nb
+  // + a (a = the group's parity: its 16 dims), byte 8 (lane % 2).
+  uint32_t voff[4];
+  {
+    const int e = (lane & 15) >> 1, a = (lane >> 4) & 1;
+    const int rv = 8 * (e >> 2) + 4 * hh + (e & 3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      voff[j] = static_cast<uint32_t>(128 * rv + 16 * ((2 * j + a) ^ f8swz(rv)) + 8 * (lane & 1));
+  }
+  // Cache loads: wave w fills blocks w + 4 i of a tile, i < 8 the 1 KB
+  // block (i % 2) (rows 8 (w + 4 (i % 2)) ..) of group i / 2, i = 8 the rope
+  // block w (rows 16 w ..); each lane fetches the chunk its LDS position holds.
+  uint32_t goff, groff;
+  {
+    const int r8 = 8 * (wave & 1) + (lane >> 3);  // the row modulo 16 of a block's lane
+    goff = static_cast<uint32_t>((lane >> 3) * kDk + 16 * ((lane & 7) ^ f8swz(r8)));
+    groff = static_cast<uint32_t>((16 * wave + (lane >> 2)) * kDk + 16 * (32 + ((lane & 3) ^ ((lane >> 4) & 3))));
+  }
+
+  int64_t x = s0;
+  while (x < s1) {
+    int b, nt;
+    int64_t start;
+    locate(p, x, b, start, nt);
+    const int j0 = static_cast<int>(x - start);
+    const int j1 = static_cast<int>(min<int64_t>(nt, s1 - start));
+    x = start + j1;
+    const int L = p.seq_lens[b];
+    const int t_begin = j0 * kTile;
+    const int t_end = min(L, j1 * kTile);
+    const int n_tiles = j1 - j0;
+    const int c0 = j0 / tps;
+
+    // ---- q of this lane's head (dims 64 ks + 32 hh .. + 31 of each k-step),
+    // loaded with the first chunk's page ids, so that one wait covers both;
+    // it is split into B operands (below) while the first tiles load
+    const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_pages;
+    uint4 qraw[36];
+    {
+      const int qi = b * p.num_q_heads + h_base + col;  // < 2^31 (checked on the host)
+      const uint16_t* qrow = p.q + static_cast<int64_t>(qi) * kDk + 32 * hh;
+#pragma unroll
+      for (int ks = 0; ks < 9; ++ks)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qraw[4 * ks + c] = *reinterpret_cast<const uint4*>(qrow + 64 * ks + 8 * c);
+    }
+    auto base_of = [&](int page) __attribute__((always_inline)) {
+      if (page < 0 || page >= p.num_pages) page = 0;  // loaded but never used
+      return kpool + static_cast<int64_t>(page) * kTile8;
+    };
+    // the cache loads of tile t (slot t % 4) of `page`: this wave's nine
+    auto issue = [&](int t, int page) __attribute__((always_inline)) {
+      const uint8_t* base = base_of(page);
+      const uint32_t slot = lds0 + (t % kF8Slots) * kTile8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int kb = wave + 4 * (i & 1);  // block of the group: rows 8 kb ..
+        dma16(slot + kF8Group * (i >> 1) + 1024 * kb, goff, base + 8 * kb * kDk + 128 * (i >> 1));
+      }
+      dma16(slot + kF8Rope + 1024 * wave, groff, base);
+    };
+    // page ids of a chunk of at most kMaxUnitTiles tiles into LDS, then its
+    // first three tiles' loads (every earlier load, q's included, has
+    // landed when they are issued, so the waits below count tile loads only)
+    auto open_chunk = [&](int k0, int kn) __attribute__((always_inline)) {
+      for (int j = tid; j < kn; j += 256) pages[j] = bt[j0 + k0 + j];
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : : : "memory");
+      for (int t = 0; t < kF8Ahead && t < kn; ++t) issue(t, __builtin_amdgcn_readfirstlane(pages[t]));
+    };
+    open_chunk(0, min(kMaxUnitTiles, n_tiles));
+
+    // q as B operands: per k-step, hi and lo codes; e per head from its
+    // largest |q| (both lanes of the head take the same)
+    v8i_t qh[kQReg], ql[kQReg];
+    uint8_t* const qlds = lds + kF8Slots * kTile8 + wave * kQLds * 4096 + 16 * lane;
+    int sqh, sql;
+    {
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 36; ++j) {
+        const uint32_t u[4] = {qraw[j].x, qraw[j].y, qraw[j].z, qraw[j].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(u[k] << 16)),
+                                   fabsf(__uint_as_float(u[k] & 0xFFFF0000u))));
+      }
+      amax = max_across_halves(amax);
+      // 2^e with amax 2^-e in [128, 256): hi codes stay below 448
+      const int ex = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFFu);
+      int e = amax > 0.0f ? ex - 127 - 7 : 0;
+      e = min(max(e, -120), 120);
+      const float inv_hi = pow2f(-e), p_hi = pow2f(e);
+      const float inv_lo = 16.0f * inv_hi;
+      sqh = amax <= 3.0e38f ? 127 + e : 255;  // an infinite q makes every score NaN
+      sql = amax <= 3.0e38f ? 127 + e - 4 : 255;
+#pragma unroll
+      for (int ks = 0; ks < 9; ++ks) {
+        uint32_t hw[8], lw[8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint4 w = qraw[4 * ks + c];
+          const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const float a0 = __uint_as_float(u[2 * k] << 16), a1 = __uint_as_float(u[2 * k] & 0xFFFF0000u);
+            const float a2 = __uint_as_float(u[2 * k + 1] << 16),
+                        a3 = __uint_as_float(u[2 * k + 1] & 0xFFFF0000u);
+            int h = __builtin_amdgcn_cvt_pk_fp8_f32(a0 * inv_hi, a1 * inv_hi, 0, false);
+            h = __builtin_amdgcn_cvt_pk_fp8_f32(a2 * inv_hi, a3 * inv_hi, h, true);
+            const auto d0 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+            const auto d1 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+            // the remainder is exact (a difference of close values), then
+            // times 2^(4 - e)
+            int o = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fmaf(-d0[0], p_hi, a0) * inv_lo,
+                                                    __builtin_fmaf(-d0[1], p_hi, a1) * inv_lo, 0, false);
+            o = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fmaf(-d1[0], p_hi, a2) * inv_lo,
+                                                __builtin_fmaf(-d1[1], p_hi, a3) * inv_lo, o, true);
+            hw[2 * c + k] = h;
+            lw[2 * c + k] = o;
+          }
+        }
+        if (ks < kQReg) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            qh[ks][j] = static_cast<int>(hw[j]);
+            ql[ks][j] = static_cast<int>(lw[j]);
+          }
+        } else {
+          // read back only by this lane, after the wave's own writes
+          uint8_t* qd = qlds + (ks - kQReg) * 4096;
+          *reinterpret_cast<uint4*>(qd) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+          *reinterpret_cast<uint4*>(qd + 1024) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+          *reinterpret_cast<uint4*>(qd + 2048) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+          *reinterpret_cast<uint4*>(qd + 3072) = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+        }
+      }
+    }
+
+    // O[nb]: rows = this wave's 32 heads (D layout), columns = dims 32 nb + ..
+    floatx16_t O[16];
+#pragma unroll
+    for (int nb = 0; nb < 16; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) O[nb][i] = 0.f;
+    // reference max (log2 domain) as in the bf16 wide kernel: set by the
+    // segment's first scores, raised (with a redo of the segment) only by a
+    // score more than kWideTau above it
+    float m = kMInit;
+    float l = 0.f;
+    bool jump = false;
+
+    bool done = false;
+    bool opened = true;  // the first chunk of the first pass is open
+    while (!done) {
+      for (int k0 = 0; k0 < n_tiles; k0 += kMaxUnitTiles) {
+        const int kn = min(kMaxUnitTiles, n_tiles - k0);
+        if (!opened) open_chunk(k0, kn);
+        opened = false;
+        auto page_ahead = [&](int t) __attribute__((always_inline)) { return pages[min(t, kn - 1)]; };
+        auto nv_of = [&](int t) __attribute__((always_inline)) {
+          return min(kTile, t_end - (t_begin + kTile * (k0 + t)));
+        };
+        int pv_cur = page_ahead(0);
+        int pv_far = page_ahead(kF8Ahead);
+        for (int t = 0; t < kn; ++t) {
+          const int later = min(kF8Ahead - 1, kn - 1 - t);  // tiles loading behind tile t
+          if (later == 2) wait_vm<2 * kDma>();
+          else if (later == 1) wait_vm<kDma>();
+          else wait_vm<0>();
+          const int page = __builtin_amdgcn_readfirstlane(pv_cur);
+          const int page_far = __builtin_amdgcn_readfirstlane(pv_far);
+          pv_cur = page_ahead(t + 1);
+          pv_far = page_ahead(t + 1 + kF8Ahead);
+          const int nv = nv_of(t);
+          const bool valid = page >= 0 && page < p.num_pages;
+          uint8_t* const buf = lds + (t % kF8Slots) * kTile8;
+          if (valid && nv < kTile) {
+            // rows past the context hold stale codes; V must be finite there
+            wg_barrier();
+            for (int i = tid; i < 32 * (kTile - nv); i += 256) {
+              const int g = i & 3, rem = i >> 2;
+              *reinterpret_cast<uint4*>(buf + kF8Group * g + (nv + (rem >> 3)) * 128 + 16 * (rem & 7)) =
+                  make_uint4(0u, 0u, 0u, 0u);
+            }
+          }
+          wg_barrier();  // tile t is in LDS; every wave is done with tile t - 1
+          if (t + kF8Ahead < kn) issue(t + kF8Ahead, page_far);
+          if (!valid) continue;
+
+          // ---- QK^T of token half mb: S = scores of tokens 32 mb .. 32 mb + 31
+          auto qk = [&](int mb) __attribute__((always_inline)) {
+            floatx16_t S;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) S[i] = 0.f;
+            // K of k-step ks (32 bytes: two 16-byte reads), two k-steps ahead
+            auto kread = [&](int ks) __attribute__((always_inline)) {
+              uint4 k0v, k1v;
+              if (ks < 8) {
+                const uint8_t* gp = buf + kF8Group * (ks >> 1) + 4096 * mb;
+                k0v = *reinterpret_cast<const uint4*>(gp + koff[ks & 1][0]);
+                k1v = *reinterpret_cast<const uint4*>(gp + koff[ks & 1][1]);
+              } else {
+                const uint8_t* gp = buf + 2048 * mb;
+                k0v = *reinterpret_cast<const uint4*>(gp + kro[0]);
+                k1v = *reinterpret_cast<const uint4*>(gp + kro[1]);
+              }
+              return v8i_t{static_cast<int>(k0v.x), static_cast<int>(k0v.y), static_cast<int>(k0v.z),
+                           static_cast<int>(k0v.w), static_cast<int>(k1v.x), static_cast<int>(k1v.y),
+                           static_cast<int>(k1v.z), static_cast<int>(k1v.w)};
+            };
+            v8i_t kq[2] = {kread(0), kread(1)};
+#pragma unroll
+            for (int ks = 0; ks < 9; ++ks) {
+              const v8i_t ka = kq[ks & 1];
+              if (ks + 2 < 9) kq[ks & 1] = kread(ks + 2);
+              if (ks < kQReg) {
+                S = mfma_f8(ka, qh[ks], S, 127, sqh);
+                S = mfma_f8(ka, ql[ks], S, 127, sql);
+              } else {
+                const uint8_t* qd = qlds + (ks - kQReg) * 4096;
+                const uint4 h0 = *reinterpret_cast<const uint4*>(qd);
+                const uint4 h1 = *reinterpret_cast<const uint4*>(qd + 1024);
+                const uint4 o0 = *reinterpret_cast<const uint4*>(qd + 2048);
+                const uint4 o1 = *reinterpret_cast<const uint4*>(qd + 3072);
+                const v8i_t bh = {static_cast<int>(h0.x), static_cast<int>(h0.y), static_cast<int>(h0.z),
+                                  static_cast<int>(h0.w), static_cast<int>(h1.x), static_cast<int>(h1.y),
+                                  static_cast<int>(h1.z), static_cast<int>(h1.w)};
+                const v8i_t bl = {static_cast<int>(o0.x), static_cast<int>(o0.y), static_cast<int>(o0.z),
+                                  static_cast<int>(o0.w), static_cast<int>(o1.x), static_cast<int>(o1.y),
+                                  static_cast<int>(o1.z), static_cast<int>(o1.w)};
+                S = mfma_f8(ka, bh, S, 127, sqh);
+                S = mfma_f8(ka, bl, S, 127, sql);
+              }
+            }
+            // order: the first two k-steps' K reads and the LDS q reads,
+            // then per k-step its two MFMAs followed by the K reads of the
+            // k-step two ahead
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 + 4 * kQLds, 0);
+#pragma unroll
+            for (int ks = 0; ks < 9; ++ks) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+              if (ks + 2 < 9) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            return S;
+          };
+
+          // ---- numerators of token half mb: 2^(s - m) = p 2^e with p in [0,
+          // 2), split into hi and lo codes (words 4 mb .. 4 mb + 3 of the A
+          // operands of P V); l += the p times 2^e. Straight-line code (the
+          // masking is compiled in or out), so it can interleave with the
+          // MFMAs of the other half.
+          v8i_t pa_hi, pa_lo;
+          int e_half[2];
+          auto numerators = [&](floatx16_t S, int mb, auto full_tag) __attribute__((always_inline)) {
+            constexpr bool kFull = decltype(full_tag)::value;
+            float lm;
+            if constexpr (kFull) {
+              // the largest scaled score, from the largest (or, for a negative
+              // scale, smallest) raw one: rounding is monotonic
+              float hi = -INFINITY, lo = INFINITY;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                hi = fmaxf(hi, S[i]);
+                lo = fminf(lo, S[i]);
+              }
+              lm = (qk_scale >= 0.0f ? hi : lo) * qk_scale;
+            } else {
+              lm = -INFINITY;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const float v = S[i] * qk_scale;
+                S[i] = (32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3) < nv) ? v : -INFINITY;
+                lm = fmaxf(lm, S[i]);
+              }
+            }
+            lm = max_across_halves(lm);
+            const bool first = m == kMInit;
+            const bool raise = !first && lm > m + kWideTau;
+            jump = jump || raise;
+            const float m_first = lm > -INFINITY ? lm : kMInit;
+            const float m_next = raise ? lm : m;
+            m = first ? m_first : m_next;
+            const int e = static_cast<int>(floorf(fmaxf(lm - m, kF8MinExp)));
+            e_half[mb] = e;
+            const float mm = m + static_cast<float>(e);
+            float pr[16];
+            float ps = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              pr[i] = __builtin_amdgcn_exp2f(kFull ? __builtin_fmaf(S[i], qk_scale, -mm) : S[i] - mm);
+              ps += pr[i];
+            }
+            l = __builtin_fmaf(ps, pow2f(e), l);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              uint32_t h, o;
+              split4(pr[4 * w], pr[4 * w + 1], pr[4 * w + 2], pr[4 * w + 3], h, o);
+              pa_hi[4 * mb + w] = static_cast<int>(h);
+              pa_lo[4 * mb + w] = static_cast<int>(o);
+            }
+          };
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            const floatx16_t S = qk(mb);
+            if (nv >= kTile) numerators(S, mb, FullTag<true>{});
+            else numerators(S, mb, FullTag<false>{});
+          }
+          // lane col supplies the first half's scale, lane col + 32 the second's
+          const int e_mine = hh ? e_half[1] : e_half[0];
+          const int sph = 127 + e_mine, spl = 127 + e_mine - 4;
+
+          // ---- O += P V over the tile's 64 tokens, 16 blocks of 32 dims
+          auto vread = [&](int nb) __attribute__((always_inline)) {
+            const uint8_t* vp = buf + kF8Group * (nb >> 2) + voff[nb & 3];
+            v8i_t vb;
+#pragma unroll
+            for (int xr = 0; xr < 4; ++xr) {
+              const v2i_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                  (lds_v2i_t*)(vp + 128 * (32 * (xr >> 1) + 16 * (xr & 1))));
+              vb[2 * xr] = r[0];
+              vb[2 * xr + 1] = r[1];
+            }
+            return vb;
+          };
+          v8i_t vq[2] = {vread(0), vread(1)};
+#pragma unroll
+          for (int nb = 0; nb < 16; ++nb) {
+            const v8i_t vb = vq[nb & 1];
+            if (nb + 2 < 16) vq[nb & 1] = vread(nb + 2);
+            O[nb] = mfma_f8(pa_hi, vb, O[nb], sph, 127);
+            O[nb] = mfma_f8(pa_lo, vb, O[nb], spl, 127);
+          }
+          // order: the first two blocks' V reads, then per block its two
+          // MFMAs followed by the reads of the block two ahead
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+          for (int nb = 0; nb < 16; ++nb) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if (nb + 2 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          }
+        }
+        wg_barrier();  // every wave is done with the slots and the page ids
+      }
+      const bool wave_jump = __builtin_amdgcn_ballot_w64(jump) != 0;
+      if (lane == 0) vote[wave] = wave_jump ? 1 : 0;
+      wg_barrier();
+      done = (vote[0] | vote[1] | vote[2] | vote[3]) == 0;
+      if (!done) {
+        jump = false;
+        l = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) O[nb][i] = 0.f;
+      }
+      wg_barrier();  // the vote has been read before it is written again
+    }
+
+    // ---- the segment's partial in split c0's row (its other splits' rows
+    // get lse = -inf): head col's denominator is the sum of lanes col and
+    // col + 32; lane (dim col, hh) holds output rows 8 (i / 4) + 4 hh + i % 4
+    l += __shfl_xor(l, 32);
+    const int64_t bh0 = static_cast<int64_t>(b) * p.num_q_heads + h_base;
+    if (hh == 0) {
+      const int64_t row = (bh0 + col) * p.max_splits;
+      p.lse_part[row + c0] = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+      const int c_last = (j1 - 1) / tps;
+      for (int cx = c0 + 1; cx <= c_last; ++cx) p.lse_part[row + cx] = -INFINITY;
+    }
+    int64_t head_stride = static_cast<int64_t>(p.max_splits) * kDv;
+    asm volatile("" : "+s"(head_stride));
+    float* dst0 = p.o_part + (bh0 * p.max_splits + c0) * kDv + col;
+    int hq = 4 * hh;
+    asm volatile("" : "+v"(hq));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int hl = 8 * (i >> 2) + hq + (i & 3);
+      const float lh = __shfl(l, hl);
+      const float f = lh > 0.0f ? o_scale / lh : 0.0f;
+      float* dst = dst0 + hl * head_stride;
+#pragma unroll
+      for (int nb = 0; nb < 16; ++nb) dst[32 * nb] = O[nb][i] * f;
+    }
   }
 }
 
@@ -1076,9 +1468,9 @@ int launch_decode_mla(const DecodeParams& p, bool e4m3, int n_split_blocks, int 
     const int n_ranges = std::max(1, cu_count() / head_groups);
     const dim3 grid(n_ranges * head_groups);
     if (e4m3) {
-      decode_mla_wide_kernel<true><<<grid, 256, 0, stream>>>(p, head_groups, n_ranges);
+      decode_mla_f8_kernel<<<grid, 256, 0, stream>>>(p, head_groups, n_ranges);
     } else {
-      decode_mla_wide_kernel<false><<<grid, 256, 0, stream>>>(p, head_groups, n_ranges);
+      decode_mla_wide_kernel<<<grid, 256, 0, stream>>>(p, head_groups, n_ranges);
     }
     return pkv::launch_status();
   }
