@@ -47,7 +47,7 @@ FLUSH_BYTES = 1 << 30    # written, then read, before every timed step: 4x the 2
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 TRAFFIC_KIB = {
     ("sweep_b64", 2048, "decode_gqa_mfma.hip", "4ff6d973bc5c8cf6"): (1197040.7, 20025.8),
-    ("mla_b64", 256, "decode_mla.hip", "d16884b292f3cabb"): (196187.0, 84068.0),
+    ("mla_b64", 256, "decode_mla.hip", "7f88329023165644"): (195596.2, 81508.0),
 }
 
 
@@ -577,9 +577,9 @@ def step_record(t: dict, nbytes: int, batch: int) -> dict:
 
 DTYPE = ("e4m3 KV cache; QK^T bf16 x bf16 and P.V f16 x f16 on MFMA (codes convert exactly, "
          "numerators rounded to f16), f32 accumulation and softmax")
-LATENT_DTYPE = ("e4m3 latent cache; QK^T and P.V on scaled fp8 MFMA with the cache codes as read "
-                "and q and the numerators each split into two e4m3 parts (eight significant bits "
-                "in all), f32 accumulation and softmax")
+LATENT_DTYPE = ("e4m3 latent cache; QK^T bf16 x bf16 on MFMA (codes convert exactly in "
+                "registers), P.V on scaled fp8 MFMA with V's codes as read and the numerators "
+                "split into two e4m3 parts (eight significant bits), f32 accumulation and softmax")
 
 
 def main():
@@ -655,9 +655,9 @@ def main():
         rec["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK,
                            "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK, 4),
                            "traffic": measured_traffic(w, split),
-                           "kernel": "pkv_decode_attn (latent, e4m3 MFMA: two e4m3 products per "
-                                     "multiply-add at the 5.0 PFLOP/s fp8 rate, so the dense bf16 "
-                                     "2.5 PFLOP/s is the ceiling for the algorithmic flops)",
+                           "kernel": "pkv_decode_attn (latent e4m3: QK^T on bf16 MFMA, P.V on "
+                                     "fp8 MFMA with two e4m3 products per multiply-add at the 5.0 "
+                                     "PFLOP/s fp8 rate, so 2.5 PFLOP/s bounds both)",
                            "avg_ms": round(dec_ms, 5), "hbm_gbs": round(dec_gbs, 2),
                            "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4)}
     else:

@@ -910,27 +910,29 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
 }
 
 // ---------------------------------------------------------------------------
-// e4m3 cache on fp8 MFMA. The cache codes are e4m3 values and gfx950's
-// scaled MFMA 32x32x64 (v_mfma_scale_f32_32x32x64_f8f6f4) multiplies e4m3
-// operands directly, each 32-value block of an operand row times a power of
-// two given per lane, with fp32 accumulation. So neither contraction needs
-// the codes converted:
-//  - QK^T: S^T = K Q^T with K the codes read straight from the tile in LDS
-//    (scale 1) and q split once per segment into two e4m3 parts, q = hi 2^e
-//    + lo 2^(e - 4) with e per head from the head's largest |q|. hi keeps
-//    four significant bits and lo the next four, so the pair holds every
-//    bf16 q exactly (apart from values below 2^(e - 13), far under the
-//    head's largest). Two MFMAs (hi, lo) per k-step of 64 dims cost the
-//    time of one bf16 MFMA of the same size.
-//  - P V: the numerators of a head and half tile are scaled by 2^-e, e =
-//    floor of the half's largest exponent, so they lie in [0, 2), and split
-//    the same way into hi and lo parts (eight significant bits in all, as a
-//    bf16 numerator has); V is the codes read with ds_read_b64_tr_b8.
-// The scaled MFMA adds the products of each run of eight k-values aligned to
-// the run's largest, keeping about 13 bits below it (measured: a product
-// under 2^-13 of its run's largest is dropped), then adds runs in fp32; the
-// score error this adds is at most about 2^-10 of the sum of |q_d k_d| and
-// measured near 2e-5 of it on normal data.
+// e4m3 cache, 128-head groups. Every wave owns 32 heads end to end: their q,
+// scores, numerators and all 512 dims of their output rows (256
+// accumulation registers), so scores never leave the lane that computed
+// them. The waves share only the code tiles: a ring of three 36 KB tiles,
+// two loading while one is used, and one barrier per 64-token tile. The
+// work split is the bf16 wide kernel's (one workgroup per compute unit and
+// 128-head group, balanced ranges of whole splits).
+//  - QK^T: S^T = K Q^T on the bf16 MFMA 32x32x16, K's codes converted
+//    (exactly) in registers as each wave reads them, q bf16: exact products
+//    and fp32 accumulation. A 64-dim step reads a lane's 32 codes (dims 64 s
+//    + 32 (l / 32) .. + 31 of its token) and runs four k-steps of 16; k-step
+//    (s, j) pairs A's and B's dims 64 s + 32 (l / 32) + 8 j .. + 7.
+//  - P V on gfx950's scaled fp8 MFMA 32x32x64
+//    (v_mfma_scale_f32_32x32x64_f8f6f4: e4m3 operands, each 32-value block
+//    of a row or column times a power of two given per lane, fp32
+//    accumulation), V being the codes read with ds_read_b64_tr_b8. A head's
+//    numerators over a 32-token half are scaled by 2^-e, e = the floor of the
+//    half's largest exponent, so they lie in [0, 2), and split into two e4m3
+//    parts, hi and lo = the remainder times 16 (eight significant bits in
+//    all, as a bf16 numerator has); two MFMAs per 32 dims. The MFMA's adder
+//    sums each run of eight k-values aligned to the run's largest product,
+//    keeping about 13 bits below it (measured), so a weight's error stays
+//    within the bf16 rounding the other kernels give it.
 //
 // MFMA 32x32x64 operand layout (measured): lane l supplies row (A) or
 // column (B) l % 32 and 32 bytes; byte j < 16 of lane l is k-value 16 (l /
@@ -938,24 +940,14 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
 // lane l % 32 multiplies k-values 0..31, that of lane l % 32 + 32 k-values
 // 32..63. D as for the bf16 MFMA: lane l, element i is row 8 (i / 4) + 4 (l
 // / 32) + i % 4, column l % 32. Only the pairing of A's and B's bytes
-// matters, so each side assigns its own data to bytes the same way:
-//  - QK^T (M = 32 tokens, N = 32 heads, 9 k-steps of 64 dims): byte j of
-//    lane l is dim 64 ks + 32 (l / 32) + j of the lane's token or head;
-//  - P V (M = 32 heads, N = 32 dims, K = the 64 tokens of a tile): byte j of
-//    lane l is token 8 (j' / 4) + 4 (l / 32) + j' % 4 of the tile's first
-//    half for j < 16 (j' = j) and of its second half for j >= 16 (j' = j -
-//    16) -- exactly the tokens whose scores QK^T leaves in lane l's
-//    accumulators (element i = j'), so the numerators go from the QK^T
-//    accumulators to the A operand without leaving the lane, and the scale
-//    of lane l % 32 (first half) and of lane l % 32 + 32 (second half) are
-//    the two halves' own.
-//
-// Work split as in the bf16 wide kernel (one workgroup per compute unit and
-// 128-head group, balanced ranges of whole splits), but every wave owns 32
-// heads end to end: their q, scores, numerators and all 512 dims of their
-// output rows (256 accumulation registers). Waves share only the code tiles:
-// a ring of four 36 KB tiles, three loading while one is used, and one
-// barrier per 64-token tile.
+// matters: in P V (M = 32 heads, N = 32 dims, K = the 64 tokens of a tile)
+// byte j of lane l is token 8 (j' / 4) + 4 (l / 32) + j' % 4 of the tile's
+// first half for j < 16 (j' = j) and of its second half for j >= 16 (j' = j
+// - 16) -- exactly the tokens whose scores QK^T leaves in lane l's
+// accumulators (element i = j'), so the numerators go from the QK^T
+// accumulators to the A operand without leaving the lane, and the scales of
+// lane l % 32 (first half) and of lane l % 32 + 32 (second half) are the two
+// halves' own.
 //
 // Code tile layout in LDS (64 rows, one per token): dims 0..511 in four 8 KB
 // groups, group G holding 16-byte chunks 8 G .. 8 G + 7 of every row, row r
@@ -967,8 +959,8 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
 // each lane fetches the global chunk its LDS position holds.
 constexpr int kF8Slots = 3;             // code tiles in the ring
 constexpr int kF8Ahead = kF8Slots - 1;  // tiles loading while one is used
-constexpr int kQLds = 1;                // trailing k-steps whose q codes live in LDS
-constexpr int kQReg = 9 - kQLds;        // k-steps whose q codes live in registers
+constexpr int kQLds = 1;                // trailing 64-dim steps whose q lives in LDS
+constexpr int kQReg = 9 - kQLds;        // 64-dim steps whose q lives in registers
 constexpr int kF8Group = 8192;   // 64 rows x 128 bytes
 constexpr int kF8Rope = 32768;   // the rope group: 64 rows x 64 bytes
 constexpr float kF8MinExp = -100.0f;  // lowest numerator scale exponent
@@ -1008,8 +1000,8 @@ __device__ __forceinline__ void split4(float x0, float x1, float x2, float x3, u
 
 __global__ void __launch_bounds__(256, 1) decode_mla_f8_kernel(DecodeParams p, int head_groups,
                                                                int n_ranges) {
-  // code tiles, then per wave the q codes of the last kQLds k-steps (4 KB
-  // each: hi words 0-3, hi 4-7, lo 0-3, lo 4-7, each 64 lanes x 16 bytes)
+  // code tiles, then per wave q of the last kQLds 64-dim steps (4 KB each:
+  // its four 8-dim k-steps, each 64 lanes x 16 bytes)
   __shared__ __attribute__((aligned(16))) uint8_t lds[kF8Slots * kTile8 + 4 * kQLds * 4096];
   __shared__ int32_t pages[kMaxUnitTiles];
   __shared__ int vote[4];
@@ -1122,72 +1114,16 @@ __global__ void __launch_bounds__(256, 1) decode_mla_f8_kernel(DecodeParams p, i
     };
     open_chunk(0, min(kMaxUnitTiles, n_tiles));
 
-    // q as B operands: per k-step, hi and lo codes; e per head from its
-    // largest |q| (both lanes of the head take the same)
-    v8i_t qh[kQReg], ql[kQReg];
+    // q as B operands of the bf16 MFMA: k-step (s, j) takes dims 64 s + 32 hh
+    // + 8 j .. + 7, which is qraw[4 s + j]; the last kQLds 64-dim steps go to
+    // this lane's slots in LDS (read back only by this lane, after the
+    // wave's own writes)
     uint8_t* const qlds = lds + kF8Slots * kTile8 + wave * kQLds * 4096 + 16 * lane;
-    int sqh, sql;
-    {
-      float amax = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 36; ++j) {
-        const uint32_t u[4] = {qraw[j].x, qraw[j].y, qraw[j].z, qraw[j].w};
+    for (int s = kQReg; s < 9; ++s)
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(u[k] << 16)),
-                                   fabsf(__uint_as_float(u[k] & 0xFFFF0000u))));
-      }
-      amax = max_across_halves(amax);
-      // 2^e with amax 2^-e in [128, 256): hi codes stay below 448
-      const int ex = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFFu);
-      int e = amax > 0.0f ? ex - 127 - 7 : 0;
-      e = min(max(e, -120), 120);
-      const float inv_hi = pow2f(-e), p_hi = pow2f(e);
-      const float inv_lo = 16.0f * inv_hi;
-      sqh = amax <= 3.0e38f ? 127 + e : 255;  // an infinite q makes every score NaN
-      sql = amax <= 3.0e38f ? 127 + e - 4 : 255;
-#pragma unroll
-      for (int ks = 0; ks < 9; ++ks) {
-        uint32_t hw[8], lw[8];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint4 w = qraw[4 * ks + c];
-          const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const float a0 = __uint_as_float(u[2 * k] << 16), a1 = __uint_as_float(u[2 * k] & 0xFFFF0000u);
-            const float a2 = __uint_as_float(u[2 * k + 1] << 16),
-                        a3 = __uint_as_float(u[2 * k + 1] & 0xFFFF0000u);
-            int h = __builtin_amdgcn_cvt_pk_fp8_f32(a0 * inv_hi, a1 * inv_hi, 0, false);
-            h = __builtin_amdgcn_cvt_pk_fp8_f32(a2 * inv_hi, a3 * inv_hi, h, true);
-            const auto d0 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
-            const auto d1 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
-            // the remainder is exact (a difference of close values), then
-            // times 2^(4 - e)
-            int o = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fmaf(-d0[0], p_hi, a0) * inv_lo,
-                                                    __builtin_fmaf(-d0[1], p_hi, a1) * inv_lo, 0, false);
-            o = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fmaf(-d1[0], p_hi, a2) * inv_lo,
-                                                __builtin_fmaf(-d1[1], p_hi, a3) * inv_lo, o, true);
-            hw[2 * c + k] = h;
-            lw[2 * c + k] = o;
-          }
-        }
-        if (ks < kQReg) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            qh[ks][j] = static_cast<int>(hw[j]);
-            ql[ks][j] = static_cast<int>(lw[j]);
-          }
-        } else {
-          // read back only by this lane, after the wave's own writes
-          uint8_t* qd = qlds + (ks - kQReg) * 4096;
-          *reinterpret_cast<uint4*>(qd) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-          *reinterpret_cast<uint4*>(qd + 1024) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-          *reinterpret_cast<uint4*>(qd + 2048) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-          *reinterpret_cast<uint4*>(qd + 3072) = make_uint4(lw[4], lw[5], lw[6], lw[7]);
-        }
-      }
-    }
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint4*>(qlds + (s - kQReg) * 4096 + 1024 * j) = qraw[4 * s + j];
 
     // O[nb]: rows = this wave's 32 heads (D layout), columns = dims 32 nb + ..
     floatx16_t O[16];
@@ -1240,18 +1176,20 @@ __global__ void __launch_bounds__(256, 1) decode_mla_f8_kernel(DecodeParams p, i
           if (t + kF8Ahead < kn) issue(t + kF8Ahead, page_far);
           if (!valid) continue;
 
-          // ---- QK^T of token half mb: S = scores of tokens 32 mb .. 32 mb + 31
+          // ---- QK^T of token half mb: S = scores of tokens 32 mb .. 32 mb + 31,
+          // on the bf16 MFMA with the codes converted (exactly) in registers
+          // as they are read: 64-dim step s reads the lane's 32 codes (dims
+          // 64 s + 32 hh .. + 31 of its token) and runs four k-steps of 16
           auto qk = [&](int mb) __attribute__((always_inline)) {
             floatx16_t S;
 #pragma unroll
             for (int i = 0; i < 16; ++i) S[i] = 0.f;
-            // K of k-step ks (32 bytes: two 16-byte reads), two k-steps ahead
-            auto kread = [&](int ks) __attribute__((always_inline)) {
+            auto kread = [&](int s) __attribute__((always_inline)) {
               uint4 k0v, k1v;
-              if (ks < 8) {
-                const uint8_t* gp = buf + kF8Group * (ks >> 1) + 4096 * mb;
-                k0v = *reinterpret_cast<const uint4*>(gp + koff[ks & 1][0]);
-                k1v = *reinterpret_cast<const uint4*>(gp + koff[ks & 1][1]);
+              if (s < 8) {
+                const uint8_t* gp = buf + kF8Group * (s >> 1) + 4096 * mb;
+                k0v = *reinterpret_cast<const uint4*>(gp + koff[s & 1][0]);
+                k1v = *reinterpret_cast<const uint4*>(gp + koff[s & 1][1]);
               } else {
                 const uint8_t* gp = buf + 2048 * mb;
                 k0v = *reinterpret_cast<const uint4*>(gp + kro[0]);
@@ -1263,36 +1201,26 @@ __global__ void __launch_bounds__(256, 1) decode_mla_f8_kernel(DecodeParams p, i
             };
             v8i_t kq[2] = {kread(0), kread(1)};
 #pragma unroll
-            for (int ks = 0; ks < 9; ++ks) {
-              const v8i_t ka = kq[ks & 1];
-              if (ks + 2 < 9) kq[ks & 1] = kread(ks + 2);
-              if (ks < kQReg) {
-                S = mfma_f8(ka, qh[ks], S, 127, sqh);
-                S = mfma_f8(ka, ql[ks], S, 127, sql);
-              } else {
-                const uint8_t* qd = qlds + (ks - kQReg) * 4096;
-                const uint4 h0 = *reinterpret_cast<const uint4*>(qd);
-                const uint4 h1 = *reinterpret_cast<const uint4*>(qd + 1024);
-                const uint4 o0 = *reinterpret_cast<const uint4*>(qd + 2048);
-                const uint4 o1 = *reinterpret_cast<const uint4*>(qd + 3072);
-                const v8i_t bh = {static_cast<int>(h0.x), static_cast<int>(h0.y), static_cast<int>(h0.z),
-                                  static_cast<int>(h0.w), static_cast<int>(h1.x), static_cast<int>(h1.y),
-                                  static_cast<int>(h1.z), static_cast<int>(h1.w)};
-                const v8i_t bl = {static_cast<int>(o0.x), static_cast<int>(o0.y), static_cast<int>(o0.z),
-                                  static_cast<int>(o0.w), static_cast<int>(o1.x), static_cast<int>(o1.y),
-                                  static_cast<int>(o1.z), static_cast<int>(o1.w)};
-                S = mfma_f8(ka, bh, S, 127, sqh);
-                S = mfma_f8(ka, bl, S, 127, sql);
+            for (int s = 0; s < 9; ++s) {
+              const v8i_t ka = kq[s & 1];
+              if (s + 2 < 9) kq[s & 1] = kread(s + 2);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const bf16x8_t kb = fp8x8_to_bf16(static_cast<uint32_t>(ka[2 * j]),
+                                                  static_cast<uint32_t>(ka[2 * j + 1]));
+                const uint4 qw = s < kQReg ? qraw[4 * s + j]
+                                           : *reinterpret_cast<const uint4*>(qlds + (s - kQReg) * 4096 + 1024 * j);
+                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, as_bf16x8(qw.x, qw.y, qw.z, qw.w), S, 0, 0, 0);
               }
             }
-            // order: the first two k-steps' K reads and the LDS q reads,
-            // then per k-step its two MFMAs followed by the K reads of the
-            // k-step two ahead
+            // order: the first two steps' code reads and the LDS q reads, then
+            // per step its four MFMAs followed by the code reads of the step
+            // two ahead
             __builtin_amdgcn_sched_group_barrier(0x100, 4 + 4 * kQLds, 0);
 #pragma unroll
-            for (int ks = 0; ks < 9; ++ks) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-              if (ks + 2 < 9) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            for (int s = 0; s < 9; ++s) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+              if (s + 2 < 9) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
             return S;
           };

@@ -435,6 +435,50 @@ def test_mla_score_jump_single_tokens(kv, jumps, head):
     assert np.allclose(ds.lse.cpu().numpy()[0], lse_ref, rtol=0, atol=1e-3)
 
 
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+def test_mla_query_magnitudes(kv):
+    """Queries whose size differs per head (2^-24 .. 2^10 times N(0,1)),
+    within a head (magnitudes spread over 2^-8 .. 2^2, random signs), an
+    all-zero head, a head of bf16 subnormals and a head with one 32x dim:
+    the e4m3 kernel splits q per head into two e4m3 parts scaled by the
+    head's largest value, so every such shape must still match the oracle.
+    Ragged: 300 tokens, the last page holds 44."""
+    from oracle import attention
+    hq, dk, dv, P, L = 128, 576, 512, 64, 300
+    n_pages = -(-L // P)
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((hq, dk))
+    q *= np.exp2(rng.integers(-24, 11, size=(hq, 1)))                  # per-head size
+    q[5:40] *= np.exp2(rng.uniform(-8, 2, size=(35, dk)))               # spread inside a head
+    q[0] = 0.0                                                          # all zero
+    q[1] = rng.choice([-1.0, 0.0, 1.0], size=dk) * rng.integers(1, 128, size=dk) * 2.0**-133  # subnormal
+    q[2] = rng.standard_normal(dk)
+    q[2, 17] = 32.0 * np.abs(q[2]).max()                                # one large dim
+    qb = torch.from_numpy(q.astype(np.float32)).to(torch.bfloat16).view(1, hq, dk)
+    vals = rng.standard_normal((n_pages * P, dk)).astype(np.float32)
+    cache = pkv.allocate_cache(n_pages, 1, P, dk, dv, kv, latent=True, device=dev)
+    if kv == "fp8":
+        scale = np.float32(np.abs(vals).max() / 448.0)
+        codes = e4m3.encode((vals / scale).astype(np.float32))
+        k_hat = e4m3.DECODE[codes] * np.float64(scale)
+        cache.k_pool[:, 0] = torch.from_numpy(codes.reshape(n_pages, P, dk)).to(dev)
+        cache.k_scale.fill_(float(scale))
+        cache.v_scale = cache.k_scale
+    else:
+        kb = torch.from_numpy(vals).to(torch.bfloat16)
+        k_hat = kb.double().numpy()
+        cache.k_pool[:, 0] = kb.view(n_pages, P, dk).to(dev)
+    k_hat = k_hat[:L]
+    bt = torch.arange(n_pages, dtype=torch.int32, device=dev).view(1, n_pages)
+    lens = torch.tensor([L], dtype=torch.int32, device=dev)
+    sm = 1 / math.sqrt(dk)
+    ds = pkv.DecodeStep(cache, hq, 1, L, 128, verify=False)
+    out = ds.attend(qb.to(dev), bt, lens, sm, None).float().cpu().numpy()[0]
+    ref, lse_ref = attention.attend(qb[0].double().numpy(), k_hat[:, None, :], k_hat[:, None, :dv], sm)
+    assert_close(out, ref, f"mla query magnitudes {kv}")
+    assert_lse_close(ds.lse.cpu().numpy()[0], lse_ref, f"mla query magnitudes {kv} lse")
+
+
 def _gqa_direct_case(kv, vals_k, vals_v, bt_pages, L, hq, P, split, num_pages, seed=11):
     """Write K/V rows straight into a pool (token t of the request lives in
     page bt_pages[t // P]) and decode one request without the tag check."""
