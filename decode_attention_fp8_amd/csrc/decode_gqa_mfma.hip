@@ -50,7 +50,6 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
   constexpr int kSlotBytes = (kBf16 ? bf16c::kTileBytes : kTileBytes) + (kRowScales ? 512 : 0);
   constexpr int kLoads = kBf16 ? 16 : (kRowScales ? 10 : 8);  // loads per tile
   __shared__ __attribute__((aligned(16))) uint8_t ring[kSlots * kSlotBytes];
-  __shared__ float rowbuf[kRows];
   const int lane = threadIdx.x;
   const int col = lane & 15, qg = lane >> 4;
   int b, g, c, L;
@@ -181,14 +180,14 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
     const bool g1_ok = tile0 + 16 < t_end && page_ok(((2 * t + 1) << 4) >> log2P);
     uint8_t* buf = ring + (t % kSlots) * kSlotBytes;
     if constexpr (kBf16) {
-      bf16c::tile_math(buf, lo, qf, qk_scale, g0_ok, g1_ok, min(kTile, t_end - tile0), rowbuf, a);
+      bf16c::tile_math(buf, lo, qf, qk_scale, g0_ok, g1_ok, min(kTile, t_end - tile0), a);
     } else {
       tile_math<kRowScales>(buf, lo, qf, qk_scale, g0_ok, g1_ok, min(kTile, t_end - tile0),
-                            rowbuf, a, reinterpret_cast<const float*>(buf + kTileBytes));
+                            a, reinterpret_cast<const float*>(buf + kTileBytes));
     }
   }
   // scales set at append: O is relative to the unit's V reference scale
-  finish(p, b, g, c, G, kRowScales ? a.vref : o_scale, rowbuf, a);
+  finish(p, b, g, c, G, kRowScales ? a.vref : o_scale, a);
 }
 
 }  // namespace

@@ -140,7 +140,7 @@ __device__ __forceinline__ float pow2_at_or_above(float x) {
 
 // QK^T, softmax and PV of the tile in buf. Group x of the tile holds valid
 // rows only if gx_ok (its page is in the pool); of the tile's 32 rows the
-// first nv are in the unit. rowbuf: 16 floats of LDS. kRowScales: the tile's
+// first nv are in the unit. kRowScales: the tile's
 // rows carry their own scales (set at append), in LDS at rs[t] (K) and
 // rs[64 + t] (V) for tile row t; a score is multiplied by its row's K scale
 // and a numerator by its row's V scale over the unit's V reference a.vref
@@ -149,7 +149,7 @@ __device__ __forceinline__ float pow2_at_or_above(float x) {
 template <bool kRowScales>
 __device__ __forceinline__ void tile_math(uint8_t* buf, const LaneOffsets& o,
                                           const bf16x8_t (&qf)[4], float qk_scale, bool g0_ok,
-                                          bool g1_ok, int nv, float* rowbuf, Acc& a,
+                                          bool g1_ok, int nv, Acc& a,
                                           const float* rs = nullptr) {
   const int lane = threadIdx.x;
   const int col = lane & 15, qg = lane >> 4;
@@ -218,15 +218,14 @@ __device__ __forceinline__ void tile_math(uint8_t* buf, const LaneOffsets& o,
     const float al = __builtin_amdgcn_exp2f(a.m - mn);
     a.m = mn;
     a.l *= al;
-    if (qg == 0) rowbuf[col] = al;
-    __builtin_amdgcn_wave_barrier();
+    // the four lanes of a head hold the same factor; lane h (< 16) holds
+    // head h's
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float f = rowbuf[4 * qg + i];
+      const float f = __shfl(al, 4 * qg + i);
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) a.O[nb][i] *= f;
     }
-    __builtin_amdgcn_wave_barrier();
   }
 
   float vinv = 1.0f;
@@ -363,7 +362,7 @@ __device__ __forceinline__ void dma_group(uint32_t slot, int x, const LaneOffset
 // denominator sums, so the weights are normalised exactly as used.
 __device__ __forceinline__ void tile_math(uint8_t* buf, const LaneOffsets& o,
                                           const bf16x8_t (&qf)[4], float qk_scale, bool g0_ok,
-                                          bool g1_ok, int nv, float* rowbuf, Acc& a) {
+                                          bool g1_ok, int nv, Acc& a) {
   const int lane = threadIdx.x;
   const int col = lane & 15, qg = lane >> 4;
   const bool full = g0_ok && g1_ok && nv == kTile;
@@ -414,15 +413,14 @@ __device__ __forceinline__ void tile_math(uint8_t* buf, const LaneOffsets& o,
     const float al = __builtin_amdgcn_exp2f(a.m - mn);
     a.m = mn;
     a.l *= al;
-    if (qg == 0) rowbuf[col] = al;
-    __builtin_amdgcn_wave_barrier();
+    // the four lanes of a head hold the same factor; lane h (< 16) holds
+    // head h's
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float f = rowbuf[4 * qg + i];
+      const float f = __shfl(al, 4 * qg + i);
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) a.O[nb][i] *= f;
     }
-    __builtin_amdgcn_wave_barrier();
   }
 
   bf16x8_t pf;
@@ -449,14 +447,12 @@ __device__ __forceinline__ void tile_math(uint8_t* buf, const LaneOffsets& o,
 // o = v_scale O / l and lse = (m + log2 l) ln 2 (o = 0, lse = -inf where no
 // token was valid).
 __device__ __forceinline__ void finish(const DecodeParams& p, int b, int g, int c, int G,
-                                       float o_scale, float* rowbuf, Acc& a) {
+                                       float o_scale, Acc& a) {
   const int lane = threadIdx.x;
   const int col = lane & 15, qg = lane >> 4;
   float l = a.l;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  if (qg == 0) rowbuf[col] = l;
-  __builtin_amdgcn_wave_barrier();
   const int64_t head0 = static_cast<int64_t>(b) * p.num_q_heads + g * G;
   if (qg == 0 && col < G)
     p.lse_part[(head0 + col) * p.max_splits + c] =
@@ -464,8 +460,8 @@ __device__ __forceinline__ void finish(const DecodeParams& p, int b, int g, int 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = 4 * qg + i;
+    const float lr = __shfl(l, h);  // lane h (< 16) holds head h's
     if (h >= G) continue;
-    const float lr = rowbuf[h];
     const float f = lr > 0.0f ? o_scale / lr : 0.0f;
     float* dst = p.o_part + ((head0 + h) * p.max_splits + c) * kD + col;
 #pragma unroll
