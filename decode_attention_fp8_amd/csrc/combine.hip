@@ -56,6 +56,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   const float4* op = reinterpret_cast<const float4*>(o_part + bh * max_splits * DV);
 
   __shared__ float red[4];
+  __shared__ int any_s[4];
   __shared__ int cnt_s[4];
   __shared__ int idx_s[256];
   __shared__ float w_s[256];
@@ -77,16 +78,24 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
       vr[j] = r < max_splits ? op[static_cast<int64_t>(r) * kC + ch] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float mx = -INFINITY;
+    bool any = false;
 #pragma unroll
     for (int j = 0; j < kRows; ++j) {
       if (sg + kP * j >= n) lr[j] = -INFINITY;  // past the request's length
       mx = fmaxf(mx, lr[j]);
+      any = any || lr[j] != -INFINITY;
     }
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if (lane == 0) red[wave] = mx;
+    const bool wave_any = __ballot(any) != 0;
+    if (lane == 0) {
+      red[wave] = mx;
+      any_s[wave] = wave_any;
+    }
     __syncthreads();
     M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    empty = (M == -INFINITY);
+    // empty: no row holds a partial (a NaN lse is a partial: it makes the
+    // output NaN, which fmaxf alone would hide)
+    empty = (any_s[0] | any_s[1] | any_s[2] | any_s[3]) == 0;
     if (!empty) {
 #pragma unroll
       for (int j = 0; j < kRows; ++j) {
@@ -104,12 +113,21 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   // the first 256 rows' lse, kept for the listing below
   const float lse0 = t < n ? lse[t] : -INFINITY;
   float mx = lse0;
-  for (int c = t + 256; c < n; c += 256) mx = fmaxf(mx, lse[c]);
+  bool any = lse0 != -INFINITY;
+  for (int c = t + 256; c < n; c += 256) {
+    const float lc = lse[c];
+    mx = fmaxf(mx, lc);
+    any = any || lc != -INFINITY;
+  }
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if (lane == 0) red[wave] = mx;
+  const bool wave_any = __ballot(any) != 0;
+  if (lane == 0) {
+    red[wave] = mx;
+    any_s[wave] = wave_any;
+  }
   __syncthreads();
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  empty = (M == -INFINITY);
+  empty = (any_s[0] | any_s[1] | any_s[2] | any_s[3]) == 0;
 
   if (!empty) {
     for (int base = 0; base < n; base += 256) {

@@ -136,7 +136,11 @@ __global__ void __launch_bounds__(256) decode_kernel(Params p) {
   for (int idx = threadIdx.x; idx < NH * DV; idx += blockDim.x) {
     const int h = idx / DV, d = idx - h * DV;
     float M = -INFINITY;
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w][h][0]);
+    bool nan = false;  // a NaN score (fmaxf leaves it out of M) reached a wave's state
+    for (int w = 0; w < kWaves; ++w) {
+      M = fmaxf(M, sm[w][h][0]);
+      nan = nan || sm[w][h][1] != sm[w][h][1];
+    }
     float den = 0.0f, num = 0.0f;
     if (M != -INFINITY) {
       for (int w = 0; w < kWaves; ++w) {
@@ -146,9 +150,11 @@ __global__ void __launch_bounds__(256) decode_kernel(Params p) {
       }
     }
     const int64_t bh = bh0 + h;
-    p.o_part[(bh * p.max_splits + c) * DV + d] = (M != -INFINITY) ? num / den : 0.0f;
+    const bool any = M != -INFINITY || nan;
+    p.o_part[(bh * p.max_splits + c) * DV + d] = M != -INFINITY ? num / den : (nan ? NAN : 0.0f);
     if (d == 0)
-      p.lse_part[bh * p.max_splits + c] = (M != -INFINITY) ? (M + __log2f(den)) * kLn2 : -INFINITY;
+      p.lse_part[bh * p.max_splits + c] =
+          M != -INFINITY ? (M + __log2f(den)) * kLn2 : (any ? NAN : -INFINITY);
   }
 }
 

@@ -317,14 +317,14 @@ __global__ void __launch_bounds__(64 * W) decode_drafts_kernel(DecodeParams p, i
   };
   if (hl == 0 && row_ok)
     p.lse_part[out_head(r_mine) * p.max_splits + c] =
-        l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+        !(l <= 0.0f) ? (m + __log2f(l)) * kLn2 : -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int row = 8 * (i >> 2) + 4 * hl + (i & 3);
     const int r = 32 * rg + row;
     if (r >= rows) continue;
     const float lr = rowbuf[0][row];
-    const float f = lr > 0.0f ? o_scale / lr : 0.0f;
+    const float f = !(lr <= 0.0f) ? o_scale / lr : 0.0f;
     float* dst = p.o_part + (out_head(r) * p.max_splits + c) * kD + col;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) dst[32 * nb] = O[nb][i] * f;

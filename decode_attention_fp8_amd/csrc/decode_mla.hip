@@ -383,12 +383,12 @@ __global__ void __launch_bounds__(256) decode_mla_kernel(DecodeParams p, int n_s
   __builtin_amdgcn_wave_barrier();
   const int64_t bh0 = static_cast<int64_t>(b) * p.num_q_heads + h_base;
   if (G == 0)
-    p.lse_part[(bh0 + lr) * p.max_splits + c] = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+    p.lse_part[(bh0 + lr) * p.max_splits + c] = !(l <= 0.0f) ? (m + __log2f(l)) * kLn2 : -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int hl = 4 * G + r;
     const float lh = l_s[wave][hl];
-    const float f = lh > 0.0f ? o_scale / lh : 0.0f;
+    const float f = !(lh <= 0.0f) ? o_scale / lh : 0.0f;
     float* dst = p.o_part + ((bh0 + hl) * p.max_splits + c) * kDv + lr;
 #pragma unroll
     for (int dn = 0; dn < 32; ++dn) dst[16 * dn] = O[dn][r] * f;
@@ -882,7 +882,7 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
     if (hh == 0) {
       l_all[wave * kWideHeads + col] = l;
       const int64_t row = (bh0 + wave * kWideHeads + col) * p.max_splits;
-      p.lse_part[row + c0] = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+      p.lse_part[row + c0] = !(l <= 0.0f) ? (m + __log2f(l)) * kLn2 : -INFINITY;
       const int c_last = (j1 - 1) / tps;
       for (int cx = c0 + 1; cx <= c_last; ++cx) p.lse_part[row + cx] = -INFINITY;
     }
@@ -900,7 +900,7 @@ __global__ void __launch_bounds__(256, 1) decode_mla_wide_kernel(DecodeParams p,
       for (int i = 0; i < 16; ++i) {
         const int hl = 32 * hb + 8 * (i >> 2) + hq + (i & 3);
         const float lh = l_all[hl];
-        const float f = lh > 0.0f ? 1.0f / lh : 0.0f;
+        const float f = !(lh <= 0.0f) ? 1.0f / lh : 0.0f;
         float* dst = dst0 + hl * head_stride;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) dst[32 * nb] = O[hb][nb][i] * f;
@@ -1344,7 +1344,7 @@ __global__ void __launch_bounds__(256, 1) decode_mla_f8_kernel(DecodeParams p, i
     const int64_t bh0 = static_cast<int64_t>(b) * p.num_q_heads + h_base;
     if (hh == 0) {
       const int64_t row = (bh0 + col) * p.max_splits;
-      p.lse_part[row + c0] = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+      p.lse_part[row + c0] = !(l <= 0.0f) ? (m + __log2f(l)) * kLn2 : -INFINITY;
       const int c_last = (j1 - 1) / tps;
       for (int cx = c0 + 1; cx <= c_last; ++cx) p.lse_part[row + cx] = -INFINITY;
     }
@@ -1357,7 +1357,7 @@ __global__ void __launch_bounds__(256, 1) decode_mla_f8_kernel(DecodeParams p, i
     for (int i = 0; i < 16; ++i) {
       const int hl = 8 * (i >> 2) + hq + (i & 3);
       const float lh = __shfl(l, hl);
-      const float f = lh > 0.0f ? o_scale / lh : 0.0f;
+      const float f = !(lh <= 0.0f) ? o_scale / lh : 0.0f;
       float* dst = dst0 + hl * head_stride;
 #pragma unroll
       for (int nb = 0; nb < 16; ++nb) dst[32 * nb] = O[nb][i] * f;

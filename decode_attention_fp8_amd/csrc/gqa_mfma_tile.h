@@ -456,13 +456,13 @@ __device__ __forceinline__ void finish(const DecodeParams& p, int b, int g, int 
   const int64_t head0 = static_cast<int64_t>(b) * p.num_q_heads + g * G;
   if (qg == 0 && col < G)
     p.lse_part[(head0 + col) * p.max_splits + c] =
-        l > 0.0f ? (a.m + __log2f(l)) * kLn2 : -INFINITY;
+        !(l <= 0.0f) ? (a.m + __log2f(l)) * kLn2 : -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = 4 * qg + i;
     const float lr = __shfl(l, h);  // lane h (< 16) holds head h's
     if (h >= G) continue;
-    const float f = lr > 0.0f ? o_scale / lr : 0.0f;
+    const float f = !(lr <= 0.0f) ? o_scale / lr : 0.0f;
     float* dst = p.o_part + ((head0 + h) * p.max_splits + c) * kD + col;
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) dst[16 * nb] = a.O[nb][i] * f;

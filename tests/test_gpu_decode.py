@@ -252,6 +252,77 @@ def test_every_e4m3_code_decodes_exactly():
     assert np.array_equal(out[ok], ref_bf16[ok])
 
 
+@pytest.mark.parametrize("kv_nan", [False, True], ids=["finite_codes", "nan_code"])
+def test_latent_every_e4m3_code_exact(kv_nan):
+    """The 128-head e4m3 latent kernel multiplies V's codes as they are (fp8
+    MFMA). Single-token requests (weight exactly 1, q = 0) whose V rows hold
+    every finite code: each output must be bf16(decode(code) * s) for every
+    head, bit for bit. With a NaN code in the row, the score (V is the row's
+    first 512 values) and every output of the request are NaN."""
+    hq, dk, dv, P = 128, 576, 512, 64
+    s = np.float32(0.375)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)  # 254 codes
+    n_req = 3
+    rows = np.full((n_req, dk), 0x38, dtype=np.uint8)
+    for i in range(n_req):
+        rows[i, :dv] = np.roll(np.resize(finite, dv), 97 * i)
+    if kv_nan:
+        rows[1, 300] = 0xFF
+    cache = pkv.allocate_cache(n_req, 1, P, dk, dv, "fp8", latent=True, device=dev)
+    cache.k_pool[:, 0, 0, :] = torch.from_numpy(rows).to(dev)
+    cache.k_scale.fill_(float(s))
+    cache.v_scale = cache.k_scale
+    bt = torch.arange(n_req, dtype=torch.int32, device=dev).view(n_req, 1)
+    lens = torch.ones(n_req, dtype=torch.int32, device=dev)
+    q = torch.zeros((n_req, hq, dk), dtype=torch.bfloat16, device=dev)
+    ds = pkv.DecodeStep(cache, hq, n_req, 1, 64, verify=False)
+    out = ds.attend(q, bt, lens, 1 / math.sqrt(dk), None).float().cpu().numpy()
+    ref = (e4m3.DECODE[rows[:, :dv]] * np.float64(s)).astype(np.float32)
+    ref_bf16 = torch.from_numpy(ref).to(torch.bfloat16).float().numpy()
+    for i in range(n_req):
+        if kv_nan and i == 1:
+            assert np.all(np.isnan(out[i])), "a NaN code makes the request's outputs NaN"
+        else:
+            assert np.array_equal(out[i], np.broadcast_to(ref_bf16[i], (hq, dv))), f"request {i}"
+
+
+@pytest.mark.parametrize("nan_tokens", [(37,), (37, 80)], ids=["one_split", "every_split"])
+def test_nan_key_code_gives_nan_rows(nan_tokens):
+    """A NaN code in a key makes that token's score NaN for every query head
+    of its kv head, and so their outputs and lse (as the oracle's max and
+    exp do), whether the NaN sits in one of the request's two splits or in
+    both; the other kv head is untouched."""
+    from oracle import attention
+    hq, hkv, D, P, L, split = 16, 2, 128, 16, 100, 64
+    n_pages = -(-L // P)
+    rng = np.random.default_rng(41)
+    vals = rng.standard_normal((2, n_pages * P, hkv, D)).astype(np.float32)
+    cache = pkv.allocate_cache(n_pages, hkv, P, D, D, "fp8", device=dev)
+    hat = []
+    for x, pool, scale in ((vals[0], cache.k_pool, cache.k_scale), (vals[1], cache.v_pool, cache.v_scale)):
+        sc = (np.abs(x).max(axis=(0, 2)) / 448.0).astype(np.float32)
+        codes = e4m3.encode((x / sc[None, :, None]).astype(np.float32))
+        if pool is cache.k_pool:
+            for t in nan_tokens:
+                codes[t, 1, 5] = 0x7F
+        hat.append(e4m3.DECODE[codes] * sc[None, :, None].astype(np.float64))
+        pool[:] = torch.from_numpy(codes.reshape(n_pages, P, hkv, D).transpose(0, 2, 1, 3).copy()).to(dev)
+        scale.copy_(torch.from_numpy(sc).to(dev))
+    q = torch.from_numpy(rng.standard_normal((1, hq, D)).astype(np.float32)).to(torch.bfloat16)
+    bt = torch.arange(n_pages, dtype=torch.int32, device=dev).view(1, n_pages)
+    lens = torch.tensor([L], dtype=torch.int32, device=dev)
+    sm = 1 / math.sqrt(D)
+    ds = pkv.DecodeStep(cache, hq, 1, L, split, verify=False)
+    out = ds.attend(q.to(dev), bt, lens, sm, None).float().cpu().numpy()[0]
+    lse = ds.lse.cpu().numpy()[0]
+    ref, lse_ref = attention.attend(q[0].double().numpy(), hat[0][:L], hat[1][:L], sm)
+    assert np.all(np.isnan(ref[8:])) and np.all(np.isnan(lse_ref[8:]))
+    assert np.all(np.isnan(out[8:])), "kv head 1's query heads must be NaN"
+    assert np.all(np.isnan(lse[8:]))
+    assert_close(out[:8], ref[:8], "kv head 0")
+    assert_lse_close(lse[:8], lse_ref[:8], "kv head 0 lse")
+
+
 def test_noop_tracker_equals_checked_path_when_nothing_aborts():
     w = W.gqa(2, 1000)
     a = State(w, "fp8", verify=True).run().clone()
