@@ -2,16 +2,19 @@
 
 A step is one pass of the whole hot path over a batch of decode requests:
     pkv_verify_append (the tag check, then one new token per request) ->
-    pkv_decode_attn -> pkv_combine
-captured once as a HIP graph. Before every timed step a 1 GiB buffer is
-written and read back (pkv_fill_u32, pkv_read_u32, outside the graph),
-which evicts the 256 MB last-level cache as the model's other layers would
-between two decode steps of one layer (the read makes the write-back of the
-dirty lines happen there, not in the step); each step is then bracketed by
-HIP events on its stream.
+    pkv_decode_attn -> pkv_combine.
+Before every timed step a 1 GiB buffer is written and read back
+(pkv_fill_u32, pkv_read_u32), which evicts the 256 MB last-level cache as
+the model's other layers would between two decode steps of one layer (the
+read makes the write-back of the dirty lines happen there, not in the
+step); the step's three launches are then bracketed by HIP events on its
+stream. The flush keeps the GPU busy far longer than the host takes to
+issue the three launches, so the figure holds no host time.
 ``ms_per_step`` is the median of those flushed steps (with a distribution-free
-95% confidence interval); warm figures (replays back to back, no flush) are
-reported beside them. A separate flushed eager pass times the decode kernel
+95% confidence interval). Beside it: the same step captured once as a HIP
+graph and replayed after each flush (a graph launch costs a fixed few
+microseconds more on this ROCm), and warm figures (graph replays back to
+back, no flush). A separate flushed eager pass times the decode kernel
 alone with events on the stream it is launched on (the roofline figure).
 Default workload: the concurrency-sweep point at batch 64 (contexts uniform
 on [2048, 32768], 64 query / 8 KV heads, head dim 128, page 16, per-head
@@ -195,9 +198,15 @@ class Runner:
 
         decode: a flushed eager pass, each step's decode launch bracketed by
           events on its stream (the kernel's own duration).
-        flushed: the captured step replayed once per flush, bracketed by
-          events; warm: replays back to back. Each list holds one time per
-          step; the headline is the flushed median."""
+        flushed: the step's three launches issued after each flush and
+          bracketed by events. The flush keeps the GPU busy for far longer
+          than the host takes to issue them, so no host time is in the
+          figure (were the host late, the gap would count against it).
+        flushed_graph: the captured step replayed once per flush (a graph
+          launch adds a fixed cost on this ROCm, reported for comparison).
+        warm: replays back to back without a flush; the graph keeps the host
+          from bounding small steps. Each list holds one time per step; the
+          headline is the flushed median."""
         torch = self.torch
         flush = flush or Flusher()
         ev = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -211,20 +220,27 @@ class Runner:
             self.one(e)
         torch.cuda.synchronize()
         dec = [a.elapsed_time(b) for a, b in evs]
+        fl = [ev() for _ in range(steps)]
+        t0 = time.perf_counter()
+        for a, b in fl:
+            flush()
+            a.record()
+            self.one()
+            b.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
         g = self.capture()
         for _ in range(warmup):
             flush()
             g.replay()
-        fl = [ev() for _ in range(steps)]
+        fg = [ev() for _ in range(steps)]
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for a, b in fl:
+        for a, b in fg:
             flush()
             a.record()
             g.replay()
             b.record()
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
         wm = [ev() for _ in range(steps)]
         for a, b in wm:
             a.record()
@@ -233,6 +249,7 @@ class Runner:
         torch.cuda.synchronize()
         del g
         return {"flushed": [a.elapsed_time(b) for a, b in fl],
+                "flushed_graph": [a.elapsed_time(b) for a, b in fg],
                 "warm": [a.elapsed_time(b) for a, b in wm],
                 "decode": dec,
                 "wall_ms_per_flushed_step": (t1 - t0) * 1e3 / steps}
@@ -274,9 +291,9 @@ def median_ci(xs):
 
 
 def summary(t: dict) -> dict:
-    """Median, 95% CI and mean of the flushed, warm and decode timings."""
+    """Median, 95% CI and mean of the flushed, graph, warm and decode timings."""
     out = {}
-    for key in ("flushed", "warm", "decode"):
+    for key in ("flushed", "flushed_graph", "warm", "decode"):
         med, lo, hi = median_ci(t[key])
         out[key] = {"median_ms": round(med, 5), "ci95_ms": [round(lo, 5), round(hi, 5)],
                     "mean_ms": round(sum(t[key]) / len(t[key]), 5)}
@@ -570,6 +587,7 @@ def step_record(t: dict, nbytes: int, batch: int) -> dict:
             "kv_gbs": round(nbytes / (med * 1e-3) / 1e9, 2),
             "hbm_frac": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "seq_steps_per_s": round(batch / (med * 1e-3), 1),
+            "graph_ms_per_step": sm["flushed_graph"]["median_ms"],
             "warm_ms_per_step": sm["warm"]["median_ms"],
             "warm_kv_gbs": round(nbytes / (sm["warm"]["median_ms"] * 1e-3) / 1e9, 2),
             "decode_ms": sm["decode"]["mean_ms"]}
@@ -638,12 +656,15 @@ def main():
                    "kv_dtype": "e4m3", "kv_bytes": fp8_bytes},
         "flushed": True,
         "timing": {"method": f"median of {args.steps} steps, each after a {FLUSH_BYTES >> 20} MiB "
-                             "write and read-back that evict the last-level cache; HIP events around each "
-                             "graph replay on its stream",
+                             "write and read-back that evict the last-level cache; HIP events on its stream "
+                             "around the step's three launches (flushed_graph: around one replay of the "
+                             "captured step; warm: replays back to back, no flush)",
                    **sm},
         "ci95_ms": sm["flushed"]["ci95_ms"],
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "seq_steps_per_s": round(w.batch / (ms * 1e-3), 1),
+        "graph": {"ms_per_step": sm["flushed_graph"]["median_ms"],
+                  "kv_gbs": round(fp8_bytes / (sm["flushed_graph"]["median_ms"] * 1e-3) / 1e9, 2)},
         "warm": {"ms_per_step": sm["warm"]["median_ms"],
                  "kv_gbs": round(fp8_bytes / (sm["warm"]["median_ms"] * 1e-3) / 1e9, 2)},
     }
