@@ -1,15 +1,18 @@
 """Throughput of the FP8 paged decode step on one MI355X.
 
 A step is one pass of the whole hot path over a batch of decode requests:
-    pkv_verify_append (the tag check, then one new token per request) ->
-    pkv_decode_attn -> pkv_combine.
+the tag check, the append of each request's new token, split-KV decode and
+the merge. Grouped-query shapes run it in two launches (pkv_step_decode, the
+decode with each split's tag check and the new token read from its values;
+pkv_step_combine, the merge with the verdicts and the append); the others in
+three (pkv_verify_append -> pkv_decode_attn -> pkv_combine).
 Before every timed step a 1 GiB buffer is written and read back
 (pkv_fill_u32, pkv_read_u32), which evicts the 256 MB last-level cache as
 the model's other layers would between two decode steps of one layer (the
 read makes the write-back of the dirty lines happen there, not in the
-step); the step's three launches are then bracketed by HIP events on its
+step); the step's launches are then bracketed by HIP events on its
 stream. The flush keeps the GPU busy far longer than the host takes to
-issue the three launches, so the figure holds no host time.
+issue the launches, so the figure holds no host time.
 ``ms_per_step`` is the median of those flushed steps (with a distribution-free
 95% confidence interval). Beside it: the same step captured once as a HIP
 graph and replayed after each flush (a graph launch costs a fixed few
@@ -156,12 +159,30 @@ class Runner:
         self.step = pkv.DecodeStep(c, w.num_q_heads, w.batch, int(w.seq_lens.max()),
                                    split or w.split_tokens, verify, dev,
                                    total_tokens=w.total_tokens)
+        # each request's new token sits at its last position, so the shapes
+        # that have it take the two-launch step
+        self.two_launch = pkv.pkv_step_launches(c, w.num_q_heads, self.step.split_tokens) == 2
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
 
     def one(self, ev=None):
         pkv, s = self.pkv, self.step
         abort = None
+        if self.two_launch:
+            # the whole step in two launches: the tag check inside the decode
+            # launch, the append inside the merge
+            if ev is not None:
+                ev[0].record()
+            exp = self.exp if s.verify else None  # None: the step without the check
+            pkv.pkv_step_decode(self.cache, self.q, self.new_k, self.new_v, self.bt, exp,
+                                self.lens, s.max_seq_len, self.w.sm_scale, s.split_tokens,
+                                s.o_part, s.lse_part, s.unit_flags, s.abort)
+            if ev is not None:
+                ev[1].record()
+            pkv.pkv_step_combine(self.cache, self.new_k, self.new_v, self.bt, exp, self.lens,
+                                 s.max_seq_len, s.split_tokens, s.o_part, s.lse_part,
+                                 s.unit_flags, s.abort, s.out, s.lse)
+            return
         if s.verify:
             # the check and the append of each request's new token, one launch
             pkv.pkv_verify_append(self.cache, self.bt, self.exp, self.lens, s.abort, self.new_k,
@@ -198,7 +219,7 @@ class Runner:
 
         decode: a flushed eager pass, each step's decode launch bracketed by
           events on its stream (the kernel's own duration).
-        flushed: the step's three launches issued after each flush and
+        flushed: the step's launches issued after each flush and
           bracketed by events. The flush keeps the GPU busy for far longer
           than the host takes to issue them, so no host time is in the
           figure (were the host late, the gap would count against it).
@@ -657,7 +678,7 @@ def main():
         "flushed": True,
         "timing": {"method": f"median of {args.steps} steps, each after a {FLUSH_BYTES >> 20} MiB "
                              "write and read-back that evict the last-level cache; HIP events on its stream "
-                             "around the step's three launches (flushed_graph: around one replay of the "
+                             "around the step's launches (flushed_graph: around one replay of the "
                              "captured step; warm: replays back to back, no flush)",
                    **sm},
         "ci95_ms": sm["flushed"]["ci95_ms"],

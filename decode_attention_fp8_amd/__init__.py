@@ -17,7 +17,7 @@ from ._binding import (EXPORTS, LIB_PATH, PKV_EHIP, PKV_EINVAL, PKV_EUNSUPPORTED
                        pkv_decode_attn_static, STATIC_SCRATCH_BYTES, pkv_int4_linear,
                        pkv_int4_linear_workspace, int4_workspace,
                        pkv_fill_u32, pkv_read_u32, pkv_requantize_pages, pkv_scales_from_amax,
-                       pkv_strerror,
+                       pkv_step_combine, pkv_step_decode, pkv_step_launches, pkv_strerror,
                        pkv_suggest_split, pkv_verify, pkv_verify_append, pkv_version)
 from .step import DecodeStep, allocate_cache
 
@@ -27,6 +27,6 @@ __all__ = ["EXPORTS", "LIB_PATH", "PKV_EHIP", "PKV_EINVAL", "PKV_EUNSUPPORTED", 
            "pkv_decode_attn_static", "STATIC_SCRATCH_BYTES", "pkv_int4_linear",
            "pkv_int4_linear_workspace", "int4_workspace",
            "pkv_fill_u32", "pkv_read_u32", "pkv_requantize_pages", "pkv_scales_from_amax",
-           "pkv_strerror",
+           "pkv_step_combine", "pkv_step_decode", "pkv_step_launches", "pkv_strerror",
            "pkv_suggest_split", "pkv_verify", "pkv_verify_append", "pkv_version", "DecodeStep",
            "allocate_cache"]

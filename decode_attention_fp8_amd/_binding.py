@@ -21,7 +21,8 @@ PKV_KV_E4M3, PKV_KV_BF16 = 1, 2
 
 EXPORTS = ("pkv_scales_from_amax", "pkv_append", "pkv_verify", "pkv_verify_append",
            "pkv_decode_attn",
-           "pkv_combine", "pkv_decode_attn_drafts", "pkv_requantize_pages", "pkv_int4_linear",
+           "pkv_combine", "pkv_step_decode", "pkv_step_combine", "pkv_step_launches",
+           "pkv_decode_attn_drafts", "pkv_requantize_pages", "pkv_int4_linear",
            "pkv_int4_linear_workspace", "pkv_fill_u32", "pkv_read_u32",
            "pkv_decode_attn_static",
            "pkv_suggest_split", "pkv_strerror", "pkv_version")
@@ -57,6 +58,11 @@ def _load() -> ctypes.CDLL:
         "pkv_verify_append": (I32, [CP, P, P, P, I32, I32, P, P, P, P, P]),
         "pkv_decode_attn": (I32, [CP, P, I32, P, P, I32, I32, I32, P, F, I32, I32, P, P, P]),
         "pkv_combine": (I32, [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P]),
+        "pkv_step_decode": (I32, [CP, P, I32, P, P, P, P, P, I32, I32, I32, F, I32, I32, P, P, P,
+                                  P, P]),
+        "pkv_step_combine": (I32, [CP, I32, P, P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P,
+                                   P, P]),
+        "pkv_step_launches": (I32, [CP, I32, I32]),
         "pkv_decode_attn_drafts": (I32, [CP, P, I32, I32, P, P, I32, I32, I32, P, F, I32, I32, P,
                                          P, P]),
         "pkv_requantize_pages": (I32, [CP, CP, P, P, P, P, I32, P]),
@@ -362,6 +368,75 @@ def pkv_combine(o_part: torch.Tensor, lse_part: torch.Tensor, seq_lens: torch.Te
     _check("pkv_combine", _lib.pkv_combine(
         _ptr(o_part), _ptr(lse_part), _ptr(seq_lens), B, Hq, Dv, int(split_tokens), max_splits,
         int(max_seq_len), _ptr(abort_flags), _ptr(out), _ptr(lse_out), _stream(stream)))
+
+
+def pkv_step_decode(cache: Cache, q: torch.Tensor, k_new: torch.Tensor,
+                    v_new: torch.Tensor | None, block_table: torch.Tensor,
+                    expected_tags: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                    sm_scale: float, split_tokens: int, o_part: torch.Tensor,
+                    lse_part: torch.Tensor, unit_flags: torch.Tensor, abort_out: torch.Tensor,
+                    stream=None) -> None:
+    """First launch of a step in two: the decode with each split's tag check
+    (none when expected_tags is None) and each request's new token (k_new[b],
+    v_new[b] at position seq_lens[b] - 1) read from its values. unit_flags
+    uint8 [B, max_splits]."""
+    _need(q, torch.bfloat16, "q")
+    _need(k_new, torch.bfloat16, "k_new")
+    if v_new is not None:
+        _need(v_new, torch.bfloat16, "v_new")
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    _need(o_part, torch.float32, "o_part")
+    _need(lse_part, torch.float32, "lse_part")
+    _need(unit_flags, torch.uint8, "unit_flags")
+    _need(abort_out, torch.uint8, "abort_out")
+    if expected_tags is not None and expected_tags.element_size() != 4:
+        raise ValueError("expected_tags are 32-bit")
+    B, Hq, _ = q.shape
+    max_splits = int(lse_part.shape[2])
+    if k_new.shape[0] != B or tuple(unit_flags.shape) != (B, max_splits):
+        raise ValueError("one new token per request; unit_flags [B, max_splits]")
+    cs = cache.struct()
+    _check("pkv_step_decode", _lib.pkv_step_decode(
+        ctypes.byref(cs), _ptr(q), Hq, _ptr(k_new), _ptr(v_new), _ptr(block_table),
+        _ptr(expected_tags), _ptr(seq_lens), B, int(block_table.shape[1]), int(max_seq_len),
+        float(sm_scale), int(split_tokens), max_splits, _ptr(o_part), _ptr(lse_part),
+        _ptr(unit_flags), _ptr(abort_out), _stream(stream)))
+
+
+def pkv_step_combine(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor | None,
+                     block_table: torch.Tensor, expected_tags: torch.Tensor,
+                     seq_lens: torch.Tensor, max_seq_len: int, split_tokens: int,
+                     o_part: torch.Tensor, lse_part: torch.Tensor, unit_flags: torch.Tensor,
+                     abort_out: torch.Tensor, out: torch.Tensor,
+                     lse_out: torch.Tensor | None = None, stream=None) -> None:
+    """Second launch of a step in two (after pkv_step_decode with the same
+    arguments): the abort flags, the append of each standing request's new
+    token, the merge into out bf16 [B, Hq, Dv] and lse_out f32 [B, Hq]."""
+    _need(out, torch.bfloat16, "out")
+    _need(unit_flags, torch.uint8, "unit_flags")
+    _need(abort_out, torch.uint8, "abort_out")
+    if expected_tags is not None and expected_tags.element_size() != 4:
+        raise ValueError("expected_tags are 32-bit")
+    B, Hq, max_splits, _ = o_part.shape
+    cs = cache.struct()
+    _check("pkv_step_combine", _lib.pkv_step_combine(
+        ctypes.byref(cs), Hq, _ptr(k_new), _ptr(v_new), _ptr(block_table), _ptr(expected_tags),
+        _ptr(seq_lens), B, int(block_table.shape[1]), int(max_seq_len), int(split_tokens),
+        max_splits, _ptr(o_part), _ptr(lse_part), _ptr(unit_flags), _ptr(abort_out), _ptr(out),
+        _ptr(lse_out), _stream(stream)))
+
+
+def pkv_step_launches(cache: Cache, num_q_heads: int, split_tokens: int) -> int:
+    """2 if this shape's step runs in two launches, 3 if in three."""
+    # only the geometry is read (as for pkv_suggest_split)
+    rows = 1 if cache.k_row_scale is not None else None
+    cs = PkvCacheStruct(1, None if cache.v_pool is None else 1, cache.dtype, cache.num_pages,
+                        cache.page_size, cache.num_kv_heads, cache.head_dim_k, cache.head_dim_v,
+                        None, None, None, rows, rows)
+    n = _lib.pkv_step_launches(ctypes.byref(cs), int(num_q_heads), int(split_tokens))
+    _check("pkv_step_launches", min(n, 0))
+    return n
 
 
 def pkv_fill_u32(dst: torch.Tensor, value: int, stream=None) -> None:

@@ -5,7 +5,17 @@
 //   M = max_c lse_c, w_c = exp(lse_c - M), o = sum w_c o_c / sum w_c
 // is a reordering of the same softmax sum. exp runs as exp2 with log2(e)
 // folded in.
+//
+// The step form (kStep, after the decode kernel's step form) also finishes
+// what that launch could not ("Smaller, faster, safer", section "Protecting
+// a shared KV cache": a request whose mapping fails the check is aborted and
+// writes nothing): it ORs the request's per-split verdicts into its abort
+// flag (a request with no units, its length past max_seq_len, is checked
+// here in full), and appends the new token of every request that stands, as
+// the append would have before the decode. Without recorded tags (no check)
+// every request stands.
 #include "common.h"
+#include "step.h"
 
 namespace {
 
@@ -30,7 +40,7 @@ constexpr int kDirectRows = 4;  // rows per thread group on the one-pass path
 // max_splits, not by the length, so every load is in the buffers, and rows
 // past the length are dropped afterwards. One memory round trip instead of
 // three (length, lse, o).
-template <int DV, bool kDirect>
+template <int DV, bool kDirect, bool kStep = false>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
                                                       const int32_t* __restrict__ seq_lens,
@@ -38,7 +48,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
                                                       int max_seq_len,
                                                       const uint8_t* __restrict__ abort_flags,
                                                       uint16_t* __restrict__ out,
-                                                      float* __restrict__ lse_out) {
+                                                      float* __restrict__ lse_out,
+                                                      StepCombineArgs sa) {
   constexpr int kC = DV / 4;     // 16-byte chunks per split row
   constexpr int kP = 256 / kC;   // split rows merged side by side
   constexpr int kRows = kDirectRows;
@@ -49,14 +60,39 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   const int sg = t / kC, ch = t % kC;
   const int64_t bh = static_cast<int64_t>(b) * heads + h;
   const int32_t L = seq_lens[b];
-  const bool aborted = abort_flags && abort_flags[b];
+  // step form: the flag is the OR of the units' verdicts, known after the
+  // first barrier (every unit of a request ran)
+  bool aborted = !kStep && abort_flags && abort_flags[b];
   const bool overflow = L > max_seq_len;
   const int n = (overflow || aborted || L <= 0) ? 0 : (L + split_tokens - 1) / split_tokens;
+  const uint8_t* uflags = kStep ? sa.unit_flags + static_cast<int64_t>(b) * max_splits : nullptr;
+  // step form: the new token's chunk this thread appends (threads 0 .. 15 of
+  // the first query head of each kv head; K chunks, then V), loaded now
+  const bool appender = kStep && t < 16 && h % sa.group == 0 && L >= 1;
+  uint4 nw0 = make_uint4(0u, 0u, 0u, 0u), nw1 = nw0;
+  if constexpr (kStep) {
+    if (appender) {
+      const uint16_t* src = (t < 8 ? sa.k_new : sa.v_new) +
+                            (static_cast<int64_t>(b) * sa.kv_heads + h / sa.group) * sa.head_dim +
+                            16 * (t & 7);
+      nw0 = *reinterpret_cast<const uint4*>(src);
+      nw1 = *reinterpret_cast<const uint4*>(src + 8);
+    }
+  }
+  // step form: the page of the request's last position (clamped into the
+  // block-table row; used only when the request stands), loaded beside the
+  // partials so the append at the end waits for nothing
+  int32_t pid = 0;
+  auto last_page = [&]() __attribute__((always_inline)) {
+    const int j = min(max(L - 1, 0) / sa.page_size, sa.max_pages - 1);
+    return sa.block_table[static_cast<int64_t>(b) * sa.max_pages + j];
+  };
   const float* lse = lse_part + bh * max_splits;
   const float4* op = reinterpret_cast<const float4*>(o_part + bh * max_splits * DV);
 
   __shared__ float red[4];
   __shared__ int any_s[4];
+  __shared__ int bad_s[4];
   __shared__ int cnt_s[4];
   __shared__ int idx_s[256];
   __shared__ float w_s[256];
@@ -77,6 +113,9 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
       lr[j] = r < max_splits ? lse[r] : -INFINITY;
       vr[j] = r < max_splits ? op[static_cast<int64_t>(r) * kC + ch] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    if constexpr (kStep) pid = last_page();
+    // step form: the units' verdicts (max_splits <= 256 here)
+    const bool ubad = kStep && sa.expected_tags && t < n && uflags[t] != 0;
     float mx = -INFINITY;
     bool any = false;
 #pragma unroll
@@ -87,16 +126,19 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     }
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     const bool wave_any = __ballot(any) != 0;
+    const bool wave_bad = __ballot(ubad) != 0;
     if (lane == 0) {
       red[wave] = mx;
       any_s[wave] = wave_any;
+      bad_s[wave] = wave_bad;
     }
     __syncthreads();
     M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if constexpr (kStep) aborted = (bad_s[0] | bad_s[1] | bad_s[2] | bad_s[3]) != 0;
     // empty: no row holds a partial (a NaN lse is a partial: it makes the
     // output NaN, which fmaxf alone would hide)
     empty = (any_s[0] | any_s[1] | any_s[2] | any_s[3]) == 0;
-    if (!empty) {
+    if (!empty && !aborted) {
 #pragma unroll
       for (int j = 0; j < kRows; ++j) {
         if (lr[j] != -INFINITY) {  // a row that holds a partial
@@ -112,24 +154,32 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   } else {
   // the first 256 rows' lse, kept for the listing below
   const float lse0 = t < n ? lse[t] : -INFINITY;
+  if constexpr (kStep) pid = last_page();
   float mx = lse0;
   bool any = lse0 != -INFINITY;
+  bool ubad = false;
   for (int c = t + 256; c < n; c += 256) {
     const float lc = lse[c];
     mx = fmaxf(mx, lc);
     any = any || lc != -INFINITY;
   }
+  if constexpr (kStep)
+    if (sa.expected_tags)
+      for (int c = t; c < n; c += 256) ubad = ubad || uflags[c] != 0;
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   const bool wave_any = __ballot(any) != 0;
+  const bool wave_bad = __ballot(ubad) != 0;
   if (lane == 0) {
     red[wave] = mx;
     any_s[wave] = wave_any;
+    bad_s[wave] = wave_bad;
   }
   __syncthreads();
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   empty = (any_s[0] | any_s[1] | any_s[2] | any_s[3]) == 0;
+  if constexpr (kStep) aborted = (bad_s[0] | bad_s[1] | bad_s[2] | bad_s[3]) != 0;
 
-  if (!empty) {
+  if (!empty && !aborted) {
     for (int base = 0; base < n; base += 256) {
       const int c = base + t;
       const float lc = base == 0 ? lse0 : (c < n ? lse[c] : -INFINITY);
@@ -163,6 +213,31 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     }
   }
   }
+  if constexpr (kStep) {
+    // a request with no units (length past max_seq_len) is checked here in
+    // full, by every workgroup of the request (the same verdict in each)
+    if (overflow && sa.expected_tags)
+      aborted = pkv::check_request(sa.page_tags, sa.num_pages, sa.page_size, sa.block_table,
+                                   sa.expected_tags, seq_lens, sa.max_pages, b) != 0;
+    if (h == 0 && t == 0) sa.abort_out[b] = aborted ? 1 : 0;
+    if (appender && !aborted) {
+      // the request stands: its new token goes to the row of position L - 1
+      // (in the pool, since the check passed), encoded as the append does
+      const int g = h / sa.group;
+      const int64_t row =
+          (static_cast<int64_t>(pid) * sa.kv_heads + g) * sa.page_size + (L - 1) % sa.page_size;
+      const int64_t dst = row * sa.head_dim + 16 * (t & 7);
+      uint8_t* pool = t < 8 ? sa.k_pool : sa.v_pool;
+      if (sa.e4m3) {
+        *reinterpret_cast<uint4*>(pool + dst) =
+            pkv::encode16(nw0, nw1, (t < 8 ? sa.k_scale : sa.v_scale)[g]);
+      } else {
+        uint4* d = reinterpret_cast<uint4*>(pool + 2 * dst);
+        d[0] = nw0;
+        d[1] = nw1;
+      }
+    }
+  }
   acc_s[sg][ch] = acc;
   if (ch == 0) den_s[sg] = den;
   __syncthreads();
@@ -187,29 +262,232 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   }
 }
 
+// When every split row of a request fits in registers (max_splits <= kMax):
+// a workgroup takes HW = 256 / (Dv / 4) consecutive query heads of one
+// request, thread (head hh, chunk ch) loads the lse values of its head's
+// rows and its 16-byte chunk of each row at once, and merges them in split
+// order by itself: no LDS and no barrier, one memory latency after the
+// request's length. Every
+// thread of a head sums the same rows in the same order, so the result is
+// the same bits on every run. The step form's flags are per request: each
+// wave ORs them with one vote.
+template <int DV, int kMax, bool kStep>
+__global__ void __launch_bounds__(256) combine_rows_kernel(const float* __restrict__ o_part,
+                                                           const float* __restrict__ lse_part,
+                                                           const int32_t* __restrict__ seq_lens,
+                                                           int heads, int split_tokens,
+                                                           int max_splits, int max_seq_len,
+                                                           const uint8_t* __restrict__ abort_flags,
+                                                           uint16_t* __restrict__ out,
+                                                           float* __restrict__ lse_out,
+                                                           StepCombineArgs sa) {
+  constexpr int kC = DV / 4;    // 16-byte chunks per split row (threads per head)
+  constexpr int HW = 256 / kC;  // heads per workgroup
+  static_assert(kC <= 256 && 256 % kC == 0, "a head's chunks tile the workgroup");
+  const int b = blockIdx.y;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int hh = t / kC, ch = t % kC;
+  const int h = blockIdx.x * HW + hh;
+  const bool head_ok = h < heads;
+  const int64_t bh = static_cast<int64_t>(b) * heads + (head_ok ? h : 0);
+  const float* lse = lse_part + bh * max_splits;
+  const float4* op = reinterpret_cast<const float4*>(o_part + bh * max_splits * DV);
+
+  // The length first (a scalar load), then every vector load is issued
+  // before any is waited for, in one memory latency: the rows the length
+  // covers (a uniform branch per row; the others are never read), the flags,
+  // the new token and the page of the last position. The empty asm
+  // statements below then take the values.
+  const int32_t L = seq_lens[b];
+  const int nl = (L > max_seq_len || L <= 0) ? 0 : min((L + split_tokens - 1) / split_tokens,
+                                                        max_splits);
+  float lr[kMax];
+  float4 vr[kMax];
+#pragma unroll
+  for (int c = 0; c < kMax; ++c) {
+    lr[c] = -INFINITY;
+    vr[c] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
+#pragma unroll
+  for (int c = 0; c < kMax; ++c) {
+    if (c < nl) {
+      lr[c] = lse[c];
+      vr[c] = op[static_cast<int64_t>(c) * kC + ch];
+    }
+  }
+  int abf = 0;
+  if (!kStep && abort_flags) abf = abort_flags[b];
+  // step form: the units' verdicts (lane c of each wave reads split c's),
+  // the new token's chunk (threads ch < 16 of the first query head of each
+  // kv head: K chunks, then V) and the page of the last position
+  const bool appender = kStep && head_ok && ch < 16 && h % sa.group == 0 && L >= 1;
+  uint4 nw0 = make_uint4(0u, 0u, 0u, 0u), nw1 = nw0;
+  uint32_t uflag = 0;
+  int32_t pid = 0;
+  if constexpr (kStep) {
+    const int j = min(max(L - 1, 0) / sa.page_size, sa.max_pages - 1);
+    pid = sa.block_table[static_cast<int64_t>(b) * sa.max_pages + j];
+    uflag = sa.unit_flags[static_cast<int64_t>(b) * max_splits + min(lane, max_splits - 1)];
+    if (appender) {
+      const uint16_t* src = (ch < 8 ? sa.k_new : sa.v_new) +
+                            (static_cast<int64_t>(b) * sa.kv_heads + h / sa.group) * sa.head_dim +
+                            16 * (ch & 7);
+      nw0 = *reinterpret_cast<const uint4*>(src);
+      nw1 = *reinterpret_cast<const uint4*>(src + 8);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < kMax; ++c)
+    asm volatile("" : : "v"(lr[c]), "v"(vr[c].x), "v"(vr[c].y), "v"(vr[c].z), "v"(vr[c].w));
+  asm volatile("" : : "v"(abf), "v"(uflag), "v"(pid));
+  asm volatile("" : : "v"(nw0.x), "v"(nw0.y), "v"(nw0.z), "v"(nw0.w));
+  asm volatile("" : : "v"(nw1.x), "v"(nw1.y), "v"(nw1.z), "v"(nw1.w));
+
+  bool aborted = abf != 0;
+  const bool overflow = L > max_seq_len;
+  const int n = (overflow || aborted || L <= 0) ? 0 : (L + split_tokens - 1) / split_tokens;
+  if constexpr (kStep) {
+    aborted = sa.expected_tags != nullptr && __any(uflag != 0 && lane < n);
+    // a request with no units (length past max_seq_len) is checked here in
+    // full, by every workgroup of the request (the same verdict in each)
+    if (overflow && sa.expected_tags)
+      aborted = pkv::check_request(sa.page_tags, sa.num_pages, sa.page_size, sa.block_table,
+                                   sa.expected_tags, seq_lens, sa.max_pages, b) != 0;
+    if (blockIdx.x == 0 && t == 0) sa.abort_out[b] = aborted ? 1 : 0;
+    if (appender && !aborted) {
+      const int g = h / sa.group;
+      const int64_t row =
+          (static_cast<int64_t>(pid) * sa.kv_heads + g) * sa.page_size + (L - 1) % sa.page_size;
+      const int64_t dst = row * sa.head_dim + 16 * (ch & 7);
+      uint8_t* pool = ch < 8 ? sa.k_pool : sa.v_pool;
+      if (sa.e4m3) {
+        *reinterpret_cast<uint4*>(pool + dst) =
+            pkv::encode16(nw0, nw1, (ch < 8 ? sa.k_scale : sa.v_scale)[g]);
+      } else {
+        uint4* d = reinterpret_cast<uint4*>(pool + 2 * dst);
+        d[0] = nw0;
+        d[1] = nw1;
+      }
+    }
+  }
+
+  // M = max lse over the rows that hold tokens; empty: no row holds a
+  // partial (a NaN lse is a partial: it makes the output NaN)
+  float M = -INFINITY;
+  bool any = false;
+#pragma unroll
+  for (int c = 0; c < kMax; ++c) {
+    if (c >= n) lr[c] = -INFINITY;
+    M = fmaxf(M, lr[c]);
+    any = any || lr[c] != -INFINITY;
+  }
+  float den = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (any && !aborted) {
+#pragma unroll
+    for (int c = 0; c < kMax; ++c) {
+      if (lr[c] != -INFINITY) {
+        const float w = exp2f((lr[c] - M) * kLog2e);
+        den += w;
+        acc.x += w * vr[c].x;
+        acc.y += w * vr[c].y;
+        acc.z += w * vr[c].z;
+        acc.w += w * vr[c].w;
+      }
+    }
+  }
+  if (!head_ok) return;
+  const bool zero = aborted || n == 0 || !any;
+  const bool nan = overflow && !aborted;
+  float x[4] = {acc.x / den, acc.y / den, acc.z / den, acc.w / den};
+  uint32_t packed[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    float a0 = x[2 * k], a1 = x[2 * k + 1];
+    if (zero) a0 = a1 = 0.0f;
+    if (nan) a0 = a1 = NAN;
+    packed[k] = static_cast<uint32_t>(pkv::f32_to_bf16_rne(a0)) |
+                (static_cast<uint32_t>(pkv::f32_to_bf16_rne(a1)) << 16);
+  }
+  *reinterpret_cast<uint2*>(out + bh * DV + 4 * ch) = make_uint2(packed[0], packed[1]);
+  if (lse_out && ch == 0) {
+    float l = M + __log2f(den) * kLn2;
+    if (zero) l = -INFINITY;
+    if (nan) l = NAN;
+    lse_out[bh] = l;
+  }
+}
+
 template <int DV>
 int launch(const float* o_part, const float* lse_part, const int32_t* seq_lens, int batch,
            int heads, int split_tokens, int max_splits, int max_seq_len,
-           const uint8_t* abort_flags, uint16_t* out, float* lse_out, hipStream_t stream) {
+           const uint8_t* abort_flags, uint16_t* out, float* lse_out, const StepCombineArgs* sa,
+           hipStream_t stream) {
   constexpr int kP = 256 / (DV / 4);
-  if (max_splits <= kP * kDirectRows)
-    combine_kernel<DV, true><<<dim3(heads, batch), 256, 0, stream>>>(
-        o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags, out,
-        lse_out);
+  const dim3 grid(heads, batch);
+  const bool direct = max_splits <= kP * kDirectRows;
+  // every row in registers: one workgroup per kP heads (up to 32 rows below
+  // head dim 512, 16 at 512; the output written 8 bytes at a time)
+  const dim3 rgrid((heads + kP - 1) / kP, batch);
+  const bool out8 = (reinterpret_cast<uintptr_t>(out) & 7u) == 0;
+  if (out8 && (max_splits <= 16 || (max_splits <= 32 && DV <= 256))) {
+    const bool r16 = max_splits <= 16;
+    if (sa) {
+      if constexpr (DV == 128) {
+        if (r16)
+          combine_rows_kernel<DV, 16, true><<<rgrid, 256, 0, stream>>>(
+              o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, nullptr,
+              out, lse_out, *sa);
+        else
+          combine_rows_kernel<DV, 32, true><<<rgrid, 256, 0, stream>>>(
+              o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, nullptr,
+              out, lse_out, *sa);
+        return pkv::launch_status();
+      }
+      return PKV_EUNSUPPORTED;
+    }
+    if (r16)
+      combine_rows_kernel<DV, 16, false><<<rgrid, 256, 0, stream>>>(
+          o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags,
+          out, lse_out, StepCombineArgs{});
+    else if constexpr (DV <= 256)
+      combine_rows_kernel<DV, 32, false><<<rgrid, 256, 0, stream>>>(
+          o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags,
+          out, lse_out, StepCombineArgs{});
+    return pkv::launch_status();
+  }
+  if (sa) {
+    if constexpr (DV == 128) {
+      if (direct)
+        combine_kernel<DV, true, true><<<grid, 256, 0, stream>>>(
+            o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, nullptr, out,
+            lse_out, *sa);
+      else
+        combine_kernel<DV, false, true><<<grid, 256, 0, stream>>>(
+            o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, nullptr, out,
+            lse_out, *sa);
+      return pkv::launch_status();
+    }
+    return PKV_EUNSUPPORTED;
+  }
+  if (direct)
+    combine_kernel<DV, true><<<grid, 256, 0, stream>>>(o_part, lse_part, seq_lens, heads,
+                                                       split_tokens, max_splits, max_seq_len,
+                                                       abort_flags, out, lse_out, StepCombineArgs{});
   else
-    combine_kernel<DV, false><<<dim3(heads, batch), 256, 0, stream>>>(
-        o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags, out,
-        lse_out);
+    combine_kernel<DV, false><<<grid, 256, 0, stream>>>(o_part, lse_part, seq_lens, heads,
+                                                        split_tokens, max_splits, max_seq_len,
+                                                        abort_flags, out, lse_out, StepCombineArgs{});
   return pkv::launch_status();
 }
 
 }  // namespace
 
-extern "C" int pkv_combine(const float* o_part, const float* lse_part, const int32_t* seq_lens,
-                           int32_t batch, int32_t num_q_heads, int32_t head_dim_v,
-                           int32_t split_tokens, int32_t max_splits, int32_t max_seq_len,
-                           const uint8_t* abort_flags, void* out, float* lse_out,
-                           hipStream_t stream) {
+int combine_impl(const float* o_part, const float* lse_part, const int32_t* seq_lens,
+                 int32_t batch, int32_t num_q_heads, int32_t head_dim_v, int32_t split_tokens,
+                 int32_t max_splits, int32_t max_seq_len, const uint8_t* abort_flags, void* out,
+                 float* lse_out, const StepCombineArgs* sa, hipStream_t stream) {
   if (!o_part || !lse_part || !seq_lens || !out || batch < 0 || num_q_heads < 1 ||
       head_dim_v < 8 || head_dim_v % 8 || split_tokens < 1 || max_splits < 1 || max_seq_len < 0)
     return PKV_EINVAL;
@@ -222,17 +500,26 @@ extern "C" int pkv_combine(const float* o_part, const float* lse_part, const int
   switch (head_dim_v) {
     case 64:
       return launch<64>(o_part, lse_part, seq_lens, batch, num_q_heads, split_tokens, max_splits,
-                       max_seq_len, abort_flags, o, lse_out, stream);
+                        max_seq_len, abort_flags, o, lse_out, sa, stream);
     case 128:
-      return launch<128>(o_part, lse_part, seq_lens, batch, num_q_heads, split_tokens, max_splits,
-                       max_seq_len, abort_flags, o, lse_out, stream);
+      return launch<128>(o_part, lse_part, seq_lens, batch, num_q_heads, split_tokens,
+                         max_splits, max_seq_len, abort_flags, o, lse_out, sa, stream);
     case 256:
-      return launch<256>(o_part, lse_part, seq_lens, batch, num_q_heads, split_tokens, max_splits,
-                       max_seq_len, abort_flags, o, lse_out, stream);
+      return launch<256>(o_part, lse_part, seq_lens, batch, num_q_heads, split_tokens,
+                         max_splits, max_seq_len, abort_flags, o, lse_out, sa, stream);
     case 512:
-      return launch<512>(o_part, lse_part, seq_lens, batch, num_q_heads, split_tokens, max_splits,
-                       max_seq_len, abort_flags, o, lse_out, stream);
+      return launch<512>(o_part, lse_part, seq_lens, batch, num_q_heads, split_tokens,
+                         max_splits, max_seq_len, abort_flags, o, lse_out, sa, stream);
     default:
       return PKV_EUNSUPPORTED;
   }
+}
+
+extern "C" int pkv_combine(const float* o_part, const float* lse_part, const int32_t* seq_lens,
+                           int32_t batch, int32_t num_q_heads, int32_t head_dim_v,
+                           int32_t split_tokens, int32_t max_splits, int32_t max_seq_len,
+                           const uint8_t* abort_flags, void* out, float* lse_out,
+                           hipStream_t stream) {
+  return combine_impl(o_part, lse_part, seq_lens, batch, num_q_heads, head_dim_v, split_tokens,
+                      max_splits, max_seq_len, abort_flags, out, lse_out, nullptr, stream);
 }

@@ -157,4 +157,51 @@ __device__ __forceinline__ uint4 encode16(const uint4& w0, const uint4& w1, floa
   return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
+// The tag check of request b by one workgroup of 256 threads ("Smaller,
+// faster, safer", section "Protecting a shared KV cache"): nonzero (the same
+// in every thread) if the request must be aborted. Each thread takes entries
+// j = j0 + 256u + tid for u < 8 of every 2048-entry round: first all eight
+// block-table entries and recorded tags, then all eight pool tags, so a
+// round costs two memory latencies whatever the request length.
+__device__ __forceinline__ int check_request(const uint32_t* __restrict__ page_tags,
+                                             int32_t num_pages, int32_t page_size,
+                                             const int32_t* __restrict__ block_table,
+                                             const uint32_t* __restrict__ expected,
+                                             const int32_t* __restrict__ seq_lens,
+                                             int32_t max_pages, int b) {
+  constexpr int kThreads = 256, kUnroll = 8;
+  const int tid = threadIdx.x;
+  const int32_t L = seq_lens[b];
+  const int64_t need = L > 0 ? (static_cast<int64_t>(L) + page_size - 1) / page_size : 0;
+  // a request needing more pages than its row holds cannot be mapped
+  int bad = need > max_pages ? 1 : 0;
+  const int64_t n = bad ? 0 : need;
+  const int32_t* row = block_table + static_cast<int64_t>(b) * max_pages;
+  const uint32_t* exp = expected + static_cast<int64_t>(b) * max_pages;
+  for (int64_t j0 = 0; j0 < n; j0 += kThreads * kUnroll) {
+    int32_t pid[kUnroll];
+    uint32_t want[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t j = j0 + u * kThreads + tid;
+      pid[u] = 0;
+      want[u] = 0;
+      if (j < n) {
+        pid[u] = row[j];
+        want[u] = exp[j];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t j = j0 + u * kThreads + tid;
+      if (j < n) {
+        const bool in_pool = pid[u] >= 0 && pid[u] < num_pages;
+        const uint32_t have = in_pool ? page_tags[pid[u]] : 0u;
+        bad |= (!in_pool || have != want[u]) ? 1 : 0;
+      }
+    }
+  }
+  return __syncthreads_or(bad);
+}
+
 }  // namespace pkv

@@ -17,6 +17,7 @@
 // softmax state, and the four states are merged through LDS at the end.
 #include "common.h"
 #include "decode_params.h"
+#include "step.h"
 
 namespace {
 
@@ -187,12 +188,12 @@ int dispatch(const Params& p, bool latent, int dk, int G, int n_split_blocks, in
 
 }  // namespace
 
-extern "C" int pkv_decode_attn(const pkv_cache* cache, const void* q, int32_t num_q_heads,
-                               const int32_t* block_table, const int32_t* seq_lens,
-                               int32_t batch, int32_t max_pages, int32_t max_seq_len,
-                               const uint8_t* abort_flags, float sm_scale, int32_t split_tokens,
-                               int32_t max_splits, float* o_part, float* lse_part,
-                               hipStream_t stream) {
+int decode_attn_impl(const pkv_cache* cache, const void* q, int32_t num_q_heads,
+                     const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                     int32_t max_pages, int32_t max_seq_len, const uint8_t* abort_flags,
+                     float sm_scale, int32_t split_tokens, int32_t max_splits, float* o_part,
+                     float* lse_part, const StepDecodeInputs* step, hipStream_t stream,
+                     bool validate_only) {
   int st = pkv::check_cache(cache);
   if (st) return st;
   if (!q || !block_table || !seq_lens || !o_part || !lse_part) return PKV_EINVAL;
@@ -250,12 +251,28 @@ extern "C" int pkv_decode_attn(const pkv_cache* cache, const void* q, int32_t nu
   p.v_row = latent ? dk : dv;
   p.sm_scale_log2 = sm_scale * kLog2e;
   const bool e4m3 = cache->dtype == PKV_KV_E4M3;
+  if (step) {
+    // step form: every request is decoded (its flag is not known yet)
+    if (validate_only) return PKV_OK;
+    if (!step_two_launch(cache, num_q_heads, split_tokens) || abort_flags ||
+        (step->expected_tags && !cache->page_tags) || !step->unit_flags || !step->k_new ||
+        !step->v_new)
+      return PKV_EINVAL;
+    p.page_tags = cache->page_tags;
+    p.expected_tags = step->expected_tags;
+    p.unit_flags = step->unit_flags;
+    p.k_new = step->k_new;
+    p.v_new = step->v_new;
+    return launch_decode_gqa_mfma_step(p, e4m3, static_cast<int>(n_split_blocks), batch, stream);
+  }
   if (cache->k_row_scale) {
     // scales set at append: the grouped-query MFMA kernel reads them
-    if (gqa_mfma_path_supported(dk, dv, G, latent, split_tokens, cache->page_size))
-      return launch_decode_gqa_mfma(p, true, static_cast<int>(n_split_blocks), batch, stream);
-    return PKV_EUNSUPPORTED;
+    if (!gqa_mfma_path_supported(dk, dv, G, latent, split_tokens, cache->page_size))
+      return PKV_EUNSUPPORTED;
+    if (validate_only) return PKV_OK;
+    return launch_decode_gqa_mfma(p, true, static_cast<int>(n_split_blocks), batch, stream);
   }
+  if (validate_only) return PKV_OK;
   if (latent && mla_fast_path_supported(dk, dv, cache->num_kv_heads, num_q_heads,
                                         cache->page_size, split_tokens))
     return launch_decode_mla(p, e4m3, static_cast<int>(n_split_blocks), batch, stream);
@@ -263,6 +280,17 @@ extern "C" int pkv_decode_attn(const pkv_cache* cache, const void* q, int32_t nu
     return launch_decode_gqa_mfma(p, e4m3, static_cast<int>(n_split_blocks), batch, stream);
   return e4m3 ? dispatch<true>(p, latent, dk, G, static_cast<int>(n_split_blocks), batch, stream)
               : dispatch<false>(p, latent, dk, G, static_cast<int>(n_split_blocks), batch, stream);
+}
+
+extern "C" int pkv_decode_attn(const pkv_cache* cache, const void* q, int32_t num_q_heads,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               int32_t batch, int32_t max_pages, int32_t max_seq_len,
+                               const uint8_t* abort_flags, float sm_scale, int32_t split_tokens,
+                               int32_t max_splits, float* o_part, float* lse_part,
+                               hipStream_t stream) {
+  return decode_attn_impl(cache, q, num_q_heads, block_table, seq_lens, batch, max_pages,
+                          max_seq_len, abort_flags, sm_scale, split_tokens, max_splits, o_part,
+                          lse_part, nullptr, stream, false);
 }
 
 extern "C" int pkv_decode_attn_drafts(const pkv_cache* cache, const void* q, int32_t num_q_heads,

@@ -23,6 +23,15 @@ struct DecodeParams {
   int q_len;            // query positions per request (drafts verified together)
   int v_row;            // elements per V row in v_pool
   float sm_scale_log2;  // sm_scale * log2(e)
+  // a step in two launches (grouped-query MFMA kernel only): the units of
+  // kv head 0 check their split's pages against the recorded tags and write
+  // unit_flags[b][c]; each request's last unit takes the new token (row L - 1)
+  // from k_new / v_new instead of the pool. NULL otherwise.
+  const uint32_t* page_tags;
+  const uint32_t* expected_tags;
+  uint8_t* unit_flags;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
 };
 
 // grouped-query kernel on MFMA for an e4m3 or bf16 cache, head dim 128, up
@@ -31,6 +40,9 @@ bool gqa_mfma_path_supported(int dk, int dv, int group, bool latent, int split_t
                              int page_size);
 int launch_decode_gqa_mfma(const DecodeParams& p, bool e4m3, int n_split_blocks, int batch,
                            hipStream_t stream);
+// the same kernel with the tag check and the new token folded in (p.unit_flags set)
+int launch_decode_gqa_mfma_step(const DecodeParams& p, bool e4m3, int n_split_blocks, int batch,
+                                hipStream_t stream);
 
 // several query positions per request (a token and its drafts), e4m3, head dim 128
 bool drafts_path_supported(int dk, int dv, bool latent, bool e4m3);

@@ -152,7 +152,7 @@ __device__ __forceinline__ void tile_math(uint8_t* buf, const LaneOffsets& o,
                                           bool g1_ok, int nv, Acc& a,
                                           const float* rs = nullptr) {
   const int lane = threadIdx.x;
-  const int col = lane & 15, qg = lane >> 4;
+  const int qg = lane >> 4;
   const bool full = g0_ok && g1_ok && nv == kTile;
   if (!full) {
     // rows past the unit or of a page outside the pool: V to zero (their
@@ -364,7 +364,7 @@ __device__ __forceinline__ void tile_math(uint8_t* buf, const LaneOffsets& o,
                                           const bf16x8_t (&qf)[4], float qk_scale, bool g0_ok,
                                           bool g1_ok, int nv, Acc& a) {
   const int lane = threadIdx.x;
-  const int col = lane & 15, qg = lane >> 4;
+  const int qg = lane >> 4;
   const bool full = g0_ok && g1_ok && nv == kTile;
   if (!full) {
     // V rows past the unit or of a page outside the pool: zero (their

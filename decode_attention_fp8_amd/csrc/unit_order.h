@@ -27,20 +27,24 @@ __device__ __forceinline__ bool find_unit(const DecodeParams& p, int u, int& b_o
                                           int& c_out, int& L_out) {
   const int lane = threadIdx.x & 63;
   const int S = p.split_tokens, H = p.num_kv_heads;
-  int L = 0;
-  auto splits = [&](int j) __attribute__((always_inline)) {
-    int n = 0;
+  // request j's length and split count (0 for no units); the length and the
+  // abort flag are loaded side by side, one memory latency
+  auto fetch = [&](int j, int& L) __attribute__((always_inline)) {
     L = 0;
+    int ab = 0;
     if (j < p.batch) {
       L = p.seq_lens[j];
-      const bool ab = p.abort_flags && p.abort_flags[j];
-      if (!ab && L > 0 && L <= p.max_seq_len) n = (L + S - 1) / S;
+      if (p.abort_flags) ab = p.abort_flags[j];
     }
-    return n;
+    return (ab == 0 && L > 0 && L <= p.max_seq_len) ? (L + S - 1) / S : 0;
   };
+  // the first 64 requests, fetched once for both passes below
+  int L0;
+  const int n0 = fetch(lane, L0);
   int base = 0;  // full units of the requests before this batch of 64
   for (int b0 = 0; b0 < p.batch; b0 += 64) {
-    const int n = splits(b0 + lane);
+    int L = L0;
+    const int n = b0 == 0 ? n0 : fetch(b0 + lane, L);
     const int full = n > 0 ? (n - 1) * H : 0;
     const int incl = wave_scan(full);
     const int total = __builtin_amdgcn_readlane(incl, 63);
@@ -57,7 +61,7 @@ __device__ __forceinline__ bool find_unit(const DecodeParams& p, int u, int& b_o
   }
   int u2 = u - base;
   if (p.batch <= 64) {
-    const int n = splits(lane);
+    const int n = n0, L = L0;
     const int psz = n > 0 ? L - (n - 1) * S : -1;
     if (u2 >= __popcll(__ballot(n > 0)) * H) return false;
     int rank = 0;
@@ -75,7 +79,8 @@ __device__ __forceinline__ bool find_unit(const DecodeParams& p, int u, int& b_o
     return true;
   }
   for (int b0 = 0; b0 < p.batch; b0 += 64) {
-    const int n = splits(b0 + lane);
+    int L = L0;
+    const int n = b0 == 0 ? n0 : fetch(b0 + lane, L);
     const int part = n > 0 ? H : 0;
     const int incl = wave_scan(part);
     const int total = __builtin_amdgcn_readlane(incl, 63);

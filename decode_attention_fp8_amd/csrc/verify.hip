@@ -15,53 +15,11 @@
 // memory latencies whatever the request length. The workgroup ORs the
 // verdicts and one thread writes the flag; no atomics, no pre-cleared output.
 #include "common.h"
+#include "step.h"
 
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;
-
-// The check of request b by one workgroup: nonzero (the same in every
-// thread) if the request must be aborted.
-__device__ __forceinline__ int check_request(const uint32_t* __restrict__ page_tags,
-                                             int32_t num_pages, int32_t page_size,
-                                             const int32_t* __restrict__ block_table,
-                                             const uint32_t* __restrict__ expected,
-                                             const int32_t* __restrict__ seq_lens,
-                                             int32_t max_pages, int b) {
-  const int tid = threadIdx.x;
-  const int32_t L = seq_lens[b];
-  const int64_t need = L > 0 ? (static_cast<int64_t>(L) + page_size - 1) / page_size : 0;
-  // a request needing more pages than its row holds cannot be mapped
-  int bad = need > max_pages ? 1 : 0;
-  const int64_t n = bad ? 0 : need;
-  const int32_t* row = block_table + static_cast<int64_t>(b) * max_pages;
-  const uint32_t* exp = expected + static_cast<int64_t>(b) * max_pages;
-  for (int64_t j0 = 0; j0 < n; j0 += kThreads * kUnroll) {
-    int32_t pid[kUnroll];
-    uint32_t want[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t j = j0 + u * kThreads + tid;
-      pid[u] = 0;
-      want[u] = 0;
-      if (j < n) {
-        pid[u] = row[j];
-        want[u] = exp[j];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t j = j0 + u * kThreads + tid;
-      if (j < n) {
-        const bool in_pool = pid[u] >= 0 && pid[u] < num_pages;
-        const uint32_t have = in_pool ? page_tags[pid[u]] : 0u;
-        bad |= (!in_pool || have != want[u]) ? 1 : 0;
-      }
-    }
-  }
-  return __syncthreads_or(bad);
-}
 
 __global__ void __launch_bounds__(kThreads) verify_kernel(const uint32_t* __restrict__ page_tags,
                                                           int32_t num_pages, int32_t page_size,
@@ -71,8 +29,8 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(const uint32_t* __rest
                                                           int32_t max_pages,
                                                           uint8_t* __restrict__ abort_out) {
   const int b = blockIdx.x;
-  const int bad = check_request(page_tags, num_pages, page_size, block_table, expected, seq_lens,
-                                max_pages, b);
+  const int bad = pkv::check_request(page_tags, num_pages, page_size, block_table, expected,
+                                     seq_lens, max_pages, b);
   if (threadIdx.x == 0) abort_out[b] = bad ? 1 : 0;
 }
 
@@ -141,7 +99,10 @@ struct Pool {
 };
 
 // pkv_verify_append: workgroup b checks request b, writes its flag and, if
-// the request stands, appends its new token (K then V rows) at slot[b].
+// the request stands, appends its new token (K then V rows) at slot[b]; with
+// slot NULL, at the row of the request's last token (position
+// seq_lens[b] - 1 of its block table), which a standing request has in the
+// pool.
 template <bool kE4M3, bool kRows>
 __global__ void __launch_bounds__(kThreads) verify_append_kernel(
     const uint32_t* __restrict__ page_tags, int32_t num_pages, int32_t page_size,
@@ -154,7 +115,7 @@ __global__ void __launch_bounds__(kThreads) verify_append_kernel(
   // the slot and, when each pool's chunks fit one pass, the new token's
   // values are loaded before the check, so their latency passes with it
   // (they are stored only if the request stands)
-  const int32_t s = slot[b];
+  int64_t s = slot ? slot[b] : -1;
   const uint16_t* ksrc = k_new + static_cast<int64_t>(b) * heads * kp.dim;
   const uint16_t* vsrc = v_new ? v_new + static_cast<int64_t>(b) * heads * vp.dim : nullptr;
   const int kch = kp.dim / 16, vch = vp.dim / 16;
@@ -163,10 +124,19 @@ __global__ void __launch_bounds__(kThreads) verify_append_kernel(
   Chunk kv{}, vv{};
   if (one_pass && i < ktot) kv = load_chunk(ksrc, kp.dim, kch, i);
   if (one_pass && i < vtot) vv = load_chunk(vsrc, vp.dim, vch, i);
-  const int bad = check_request(page_tags, num_pages, page_size, block_table, expected, seq_lens,
-                                max_pages, b);
+  // no recorded tags (the step without the check): every request stands
+  const int bad = expected ? pkv::check_request(page_tags, num_pages, page_size, block_table,
+                                                expected, seq_lens, max_pages, b)
+                           : 0;
   if (threadIdx.x == 0) abort_out[b] = bad ? 1 : 0;
-  if (bad || s < 0 || s >= n_slots) return;
+  if (bad) return;
+  if (!slot) {
+    const int32_t L = seq_lens[b];
+    if (L < 1) return;
+    const int32_t pid = block_table[static_cast<int64_t>(b) * max_pages + (L - 1) / page_size];
+    s = static_cast<int64_t>(pid) * page_size + (L - 1) % page_size;
+  }
+  if (s < 0 || s >= n_slots) return;
   const int64_t page = s / page_size;
   const int row = s - static_cast<int>(page) * page_size;
   if (one_pass) {
@@ -202,18 +172,16 @@ extern "C" int pkv_verify(const pkv_cache* cache, const int32_t* block_table,
   return pkv::launch_status();
 }
 
-extern "C" int pkv_verify_append(const pkv_cache* cache, const int32_t* block_table,
-                                 const uint32_t* expected_tags, const int32_t* seq_lens,
-                                 int32_t batch, int32_t max_pages, uint8_t* abort_out,
-                                 const void* k_new, const void* v_new, const int32_t* slot,
-                                 hipStream_t stream) {
+int verify_append_impl(const pkv_cache* cache, const int32_t* block_table,
+                       const uint32_t* expected_tags, const int32_t* seq_lens, int32_t batch,
+                       int32_t max_pages, uint8_t* abort_out, const void* k_new,
+                       const void* v_new, const int32_t* slot, hipStream_t stream) {
   int st = pkv::check_cache(cache);
   if (st) return st;
-  if (!cache->page_tags) return PKV_EINVAL;
-  if (!block_table || !expected_tags || !seq_lens || !abort_out || batch < 0 || max_pages < 1)
-    return PKV_EINVAL;
+  if (expected_tags && !cache->page_tags) return PKV_EINVAL;
+  if (!block_table || !seq_lens || !abort_out || batch < 0 || max_pages < 1) return PKV_EINVAL;
   const bool latent = cache->v_pool == nullptr;
-  if (!k_new || !slot || (latent && v_new) || (!latent && !v_new)) return PKV_EINVAL;
+  if (!k_new || (latent && v_new) || (!latent && !v_new)) return PKV_EINVAL;
   auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
   if (misaligned(k_new) || (v_new && misaligned(v_new)) || misaligned(cache->k_pool) ||
       (cache->v_pool && misaligned(cache->v_pool)))
@@ -244,4 +212,14 @@ extern "C" int pkv_verify_append(const pkv_cache* cache, const int32_t* block_ta
         abort_out, kn, vn, slot, kp, vp, cache->num_kv_heads, n_slots);
   }
   return pkv::launch_status();
+}
+
+extern "C" int pkv_verify_append(const pkv_cache* cache, const int32_t* block_table,
+                                 const uint32_t* expected_tags, const int32_t* seq_lens,
+                                 int32_t batch, int32_t max_pages, uint8_t* abort_out,
+                                 const void* k_new, const void* v_new, const int32_t* slot,
+                                 hipStream_t stream) {
+  if (!slot || !expected_tags) return PKV_EINVAL;
+  return verify_append_impl(cache, block_table, expected_tags, seq_lens, batch, max_pages,
+                            abort_out, k_new, v_new, slot, stream);
 }

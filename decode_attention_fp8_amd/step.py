@@ -6,14 +6,16 @@ the order the integrity rule needs ("Smaller, faster, safer", section
 "Protecting a shared KV cache": the mapping is checked before decode reads):
     pkv_verify -> pkv_append -> pkv_decode_attn -> pkv_combine
 with the first two as one launch (pkv_verify_append) when each request
-appends one token.
+appends one token; or, for one token per request at its last position, the
+whole step in two launches (pkv_step_decode -> pkv_step_combine: the check
+inside the decode, the append inside the merge).
 """
 from __future__ import annotations
 
 import torch
 
-from ._binding import (Cache, pkv_append, pkv_combine, pkv_decode_attn, pkv_suggest_split,
-                       pkv_verify, pkv_verify_append)
+from ._binding import (Cache, pkv_append, pkv_combine, pkv_decode_attn, pkv_step_combine,
+                       pkv_step_decode, pkv_suggest_split, pkv_verify, pkv_verify_append)
 
 E4M3_NAN = 0x7F
 BF16_NAN = 0x7FC0
@@ -73,6 +75,7 @@ class DecodeStep:
         self.lse = torch.empty((batch, num_q_heads), dtype=torch.float32, device=device)
         self.verify = verify
         self.abort = torch.zeros(batch, dtype=torch.uint8, device=device)
+        self.unit_flags = torch.zeros((batch, self.max_splits), dtype=torch.uint8, device=device)
 
     def run(self, q, block_table, expected_tags, seq_lens, sm_scale, k_new=None, v_new=None,
             slot=None, token_req=None):
@@ -99,4 +102,21 @@ class DecodeStep:
                         self.split_tokens, self.o_part, self.lse_part)
         pkv_combine(self.o_part, self.lse_part, seq_lens, self.split_tokens, self.max_seq_len,
                     abort, self.out, self.lse)
+        return self.out
+
+    def step2(self, q, block_table, expected_tags, seq_lens, sm_scale, k_new, v_new=None):
+        """One step in two launches: the tag check, the append of each
+        request's new token (k_new[b], v_new[b]) at its last position
+        (seq_lens[b] - 1), decode and merge; the same results as run() with
+        those slots. Without verify (or with expected_tags None) there is no
+        check and every request stands."""
+        c = self.cache
+        if not self.verify:
+            expected_tags = None
+        pkv_step_decode(c, q, k_new, v_new, block_table, expected_tags, seq_lens,
+                        self.max_seq_len, sm_scale, self.split_tokens, self.o_part,
+                        self.lse_part, self.unit_flags, self.abort)
+        pkv_step_combine(c, k_new, v_new, block_table, expected_tags, seq_lens, self.max_seq_len,
+                         self.split_tokens, self.o_part, self.lse_part, self.unit_flags,
+                         self.abort, self.out, self.lse)
         return self.out

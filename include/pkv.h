@@ -261,6 +261,69 @@ int pkv_combine(const float* o_part, const float* lse_part,
                 float* lse_out, hipStream_t stream);
 
 /*
+ * One decode step in two launches (sections "Protecting a shared KV cache"
+ * and "Quantizing the KV cache": the mapping is checked before anything read
+ * through it is returned, an aborted request writes nothing, the new token
+ * is stored as e4m3 under its kv head's scale and the attention kernel
+ * converts codes as it reads them). pkv_step_decode then pkv_step_combine,
+ * on one stream with the same arguments, give the abort flags, cache
+ * contents, out and lse_out of
+ *   pkv_verify_append(cache, block_table, expected_tags, seq_lens, batch,
+ *                     max_pages, abort_out, k_new, v_new, slot)
+ *   pkv_decode_attn(..., abort_flags = abort_out, ...)
+ *   pkv_combine(..., abort_flags = abort_out, out, lse_out)
+ * bit for bit, with each request's new token at the row of its last
+ * position: slot[b] = block_table[b][(L-1) / P] * P + (L-1) % P for
+ * L = seq_lens[b] >= 1 (no token when L <= 0).
+ *
+ * Two-launch form (separate K and V pools, head_dim_k == head_dim_v == 128,
+ * e4m3 with per-head scales or bf16, up to 16 query heads per kv head,
+ * split_tokens <= 128 * page_size): pkv_step_decode decodes every request;
+ * the units of kv head 0 check their split's pages and write
+ * unit_flags[b][c], and each request's last split reads the new token's row
+ * from k_new / v_new (encoded as pkv_append encodes it) instead of the pool.
+ * pkv_step_combine ORs a request's flags into abort_out[b] (checking a
+ * request with seq_lens[b] > max_seq_len, which has no units, in full),
+ * appends the new token of each request that stands, and merges. Other
+ * shapes: pkv_step_decode runs the check-and-append and the decode launches,
+ * pkv_step_combine the merge.
+ *
+ *   k_new, v_new: bf16 [batch][num_kv_heads][head_dim], 16-byte aligned;
+ *                 v_new NULL for the latent layout
+ *   expected_tags: as for pkv_verify, or NULL for the step without the
+ *                 check (no tag is read, every request stands)
+ *   unit_flags:   uint8 [batch][max_splits], scratch between the two calls
+ *   abort_out:    uint8 [batch], final after pkv_step_combine
+ *   o_part, lse_part: scratch as for pkv_decode_attn (in the two-launch form
+ *                 an aborted request's partials are computed too)
+ *   other arguments as for pkv_verify_append, pkv_decode_attn, pkv_combine.
+ * A request's new row must not lie inside another request's context in the
+ * same step (the three-launch order would show it to that request; here the
+ * other request reads the pool's previous row). Device pointers,
+ * caller-owned. Errors: those of the three calls (checked before anything is
+ * launched); EINVAL also for NULL unit_flags / abort_out, expected_tags
+ * without cache->page_tags, or misaligned k_new / v_new.
+ */
+int pkv_step_decode(const pkv_cache* cache, const void* q, int32_t num_q_heads,
+                    const void* k_new, const void* v_new, const int32_t* block_table,
+                    const uint32_t* expected_tags, const int32_t* seq_lens, int32_t batch,
+                    int32_t max_pages, int32_t max_seq_len, float sm_scale,
+                    int32_t split_tokens, int32_t max_splits, float* o_part, float* lse_part,
+                    uint8_t* unit_flags, uint8_t* abort_out, hipStream_t stream);
+int pkv_step_combine(const pkv_cache* cache, int32_t num_q_heads, const void* k_new,
+                     const void* v_new, const int32_t* block_table,
+                     const uint32_t* expected_tags, const int32_t* seq_lens, int32_t batch,
+                     int32_t max_pages, int32_t max_seq_len, int32_t split_tokens,
+                     int32_t max_splits, const float* o_part, const float* lse_part,
+                     const uint8_t* unit_flags, uint8_t* abort_out, void* out,
+                     float* lse_out, hipStream_t stream);
+/* Host only: 2 if the step of this shape runs in two launches, 3 if the two
+ * calls run the three. Reads the cache's geometry (NULL-ness of v_pool and
+ * k_row_scale, head dims, page size, kv heads); EINVAL for NULL or an
+ * invalid page size or kv head count. */
+int pkv_step_launches(const pkv_cache* cache, int32_t num_q_heads, int32_t split_tokens);
+
+/*
  * Decode attention of a token and its drafts verified together (Cloudflare's
  * post on serving extra-large models, speculative decoding section: a draft
  * model proposes a few future tokens and the target model checks them in

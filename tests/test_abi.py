@@ -61,6 +61,16 @@ def test_host_helpers():
     assert pkv.pkv_suggest_split(lat, 128, 1, 8192, 8192) == 64
     for s in (pkv.pkv_suggest_split(gqa, 64, 3, 0, 5000), pkv.pkv_suggest_split(lat, 128, 3, 0, 5000)):
         assert s > 0 and s % 16 == 0
+    # the step in two launches: grouped-query head dim 128, static scales or
+    # bf16, up to 128 pages per split
+    assert pkv.pkv_step_launches(gqa, 64, 2048) == 2
+    assert pkv.pkv_step_launches(gqa_bf16, 64, 256) == 2
+    assert pkv.pkv_step_launches(gqa, 64, 4096) == 3
+    assert pkv.pkv_step_launches(gqa, 8, 2048) == 2 and pkv.pkv_step_launches(gqa, 256, 2048) == 3
+    assert pkv.pkv_step_launches(lat, 128, 256) == 3
+    d64 = pkv.Cache(torch.empty((1, 2, 16, 64), dtype=torch.uint8),
+                    torch.empty((1, 2, 16, 64), dtype=torch.uint8))
+    assert pkv.pkv_step_launches(d64, 8, 64) == 3
     with pytest.raises(pkv.PkvError):
         pkv.pkv_suggest_split(gqa, 63, 1, 10, 10)  # query heads not a multiple of kv heads
     with pytest.raises(pkv.PkvError):
@@ -110,6 +120,23 @@ def test_invalid_arguments_rejected_on_host():
     assert lib.pkv_combine(None, P, P, 1, 1, 64, 16, 4, 64, None, P, None, None) == E
     assert lib.pkv_combine(P, P, P, 1, 1, 64, 16, 3, 64, None, P, None, None) == E
     assert lib.pkv_combine(P, P, P, 1, 1, 60, 16, 4, 64, None, P, None, None) == E
+    # the step in two calls: every argument is checked before any launch
+    sd, sc = lib.pkv_step_decode, lib.pkv_step_combine
+    g = ctypes.byref(_cache(num_kv_heads=2, head_dim_k=128, head_dim_v=128))
+    ok = (P, 8, P, P, P, P, P, 1, 4, 64, 0.1, 16, 8, P, P, P, P, None)
+    assert sd(ctypes.byref(_cache(page_tags=None)), *ok) == E
+    assert sd(g, *ok[:15], None, *ok[16:]) == E              # unit_flags
+    assert sd(g, *ok[:16], None, None) == E                  # abort_out
+    assert sd(g, P, 8, P + 2, *ok[3:]) == E                   # k_new misaligned
+    assert sd(g, P, 8, P, None, *ok[4:]) == E                 # v_new missing (separate pools)
+    assert sd(g, *ok[:11], 24, *ok[12:]) == E                 # split not a page multiple
+    assert sd(g, *ok[:12], 3, *ok[13:]) == E                  # max_splits too small
+    assert sd(g, None, *ok[1:]) == E                          # q
+    okc = (8, P, P, P, P, P, 1, 4, 64, 16, 8, P, P, P, P, P, None, None)
+    assert sc(g, *okc[:13], None, *okc[14:]) == E             # unit_flags
+    assert sc(g, *okc[:14], None, *okc[15:]) == E             # abort_out
+    assert sc(g, 8, P, P, None, *okc[4:]) == E                # block_table
+    assert sc(ctypes.byref(_cache(page_tags=None)), *okc) == E
     # INT4 linear: NULL, batch outside [1, 64], n not a multiple of 32, k not a
     # multiple of 1024, misaligned pointers (the workspace too)
     assert lib.pkv_int4_linear(None, P, P, 1, 32, 1024, P, None, None) == E
