@@ -52,8 +52,8 @@ FLUSH_BYTES = 1 << 30    # written, then read, before every timed step: 4x the 2
 # here and WRITE_SIZE in KiB. Entries stop matching once the kernel changes.
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 TRAFFIC_KIB = {
-    ("sweep_b64", 2048, "decode_gqa_mfma.hip", "9e23a98e5a8366fc"): (1197023.3, 20028.0),
-    ("mla_b64", 256, "decode_mla.hip", "5e25dd76209f2105"): (195682.4, 81508.0),
+    ("sweep_b64", 2048, "decode_gqa_mfma.hip", "335c4a7ad6adc235"): (1197483.1, 20030.8),
+    ("mla_b64", 256, "decode_mla.hip", "695033e6be803fe4"): (195725.4, 81508.0),
 }
 
 
@@ -61,7 +61,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--batch", type=int, default=64)
     ap.add_argument("--workload", default="sweep", choices=["sweep", "gqa", "long", "mla"],
                     help="sweep: concurrency-sweep point (--batch); gqa: batch 8 x 4096; "
@@ -729,7 +729,7 @@ def main():
             row = {"batch": B}
             for kv, e in (("fp8", 1), ("bf16", 2)):
                 r = Runner(ws, kv, None)
-                tr = r.time(max(20, args.steps), 5, flush)
+                tr = r.time(max(20, args.steps), args.warmup, flush)
                 nb = kv_bytes(ws, e, r.step.abort.cpu().numpy() == 0)
                 row[kv] = {**step_record(tr, nb, B), "split_tokens": r.step.split_tokens}
                 del r
@@ -742,10 +742,10 @@ def main():
         for B in (1, 2, 4, 8):
             wi = W.integrity_cost(B)
             on = Runner(wi, "fp8", None, verify=True)
-            t_on = summary(on.time(max(50, args.steps), 10, flush))
+            t_on = summary(on.time(max(50, args.steps), args.warmup, flush))
             del on
             off = Runner(wi, "fp8", None, verify=False)
-            t_off = summary(off.time(max(50, args.steps), 10, flush))
+            t_off = summary(off.time(max(50, args.steps), args.warmup, flush))
             del off
             torch.cuda.empty_cache()
             m_on, m_off = t_on["flushed"]["median_ms"], t_off["flushed"]["median_ms"]
