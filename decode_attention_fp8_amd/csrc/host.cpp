@@ -20,9 +20,8 @@ extern "C" int32_t pkv_version(void) { return 100; }  // 0.1.0
 // Split planning: a longer split writes fewer partial rows (one per query
 // head and split, read again by the merge) and repeats the per-unit set-up
 // less often; a shorter one gives more units to spread over 256 compute
-// units. Measured on MI355X: the grouped-query kernel is flat between 256 and
-// 512 at batch 64 and best at 128..256 for batch 1..8; the wide latent
-// kernel keeps gaining up to 4096-token splits at batch 64.
+// units. Measured on MI355X: see the grouped-query branch below; the wide
+// latent kernel keeps gaining up to 4096-token splits at batch 64.
 extern "C" int32_t pkv_suggest_split(const pkv_cache* cache, int32_t num_q_heads, int32_t batch,
                                      int64_t total_tokens, int32_t max_seq_len) {
   if (!cache || batch < 1 || max_seq_len < 1 || num_q_heads < 1 || cache->num_kv_heads < 1 ||
@@ -49,12 +48,16 @@ extern "C" int32_t pkv_suggest_split(const pkv_cache* cache, int32_t num_q_heads
     while (pages * 2 <= share / 8 && pages < 64) pages *= 2;
     s = pages * P;
   } else if (!latent && cache->head_dim_k == 128 && cache->head_dim_v == 128 && G <= 16) {
-    // MFMA grouped-query kernel (e4m3 or bf16): single-wave units, nine
-    // (five with bf16) per compute unit; splits of 128 .. 2048 tokens (256
-    // pages at most), the longest giving 4096 units or more: long units pay
-    // their start (three dependent memory round trips) less often
-    s = std::min<int64_t>(2048, 256 * P);
-    while (s > 128 && units(s, cache->num_kv_heads) < 4096) s /= 2;
+    // MFMA grouped-query kernel (e4m3 or bf16): single-wave units; splits of
+    // 128 .. 2048 tokens (128 pages at most, the two-launch step's limit),
+    // the longest giving 1100 units or more, enough waves to keep HBM busy:
+    // long units pay their start and their partials less often. Measured
+    // on the concurrency sweep (flushed step, e4m3): batch 16 0.111 ms at
+    // 2048 against 0.119 at 512, batch 32 0.215 at 2048 against 0.221 at
+    // 1024, batch 8 0.065 at 1024 and 0.063 at 512 against 0.067 at 256,
+    // batch 1 best at 128 (0.0192, against 0.0199 at 64 and 0.0202 at 256).
+    s = std::min<int64_t>(2048, 128 * P);
+    while (s > 128 && units(s, cache->num_kv_heads) < 1100) s /= 2;
   } else {
     constexpr int64_t kTargetUnits = 16384;
     const int64_t work = static_cast<int64_t>(batch) * cache->num_kv_heads * max_seq_len;

@@ -51,7 +51,7 @@ def test_host_helpers():
     gqa_bf16 = pkv.Cache(torch.empty((1, 8, 16, 128), dtype=torch.bfloat16),
                          torch.empty((1, 8, 16, 128), dtype=torch.bfloat16))
     assert pkv.pkv_suggest_split(gqa_bf16, 64, 64, 64 * 17000, 32768) == 2048
-    assert pkv.pkv_suggest_split(gqa, 64, 8, 8 * 17000, 32768) == 256
+    assert pkv.pkv_suggest_split(gqa, 64, 8, 8 * 17000, 32768) == 512
     assert pkv.pkv_suggest_split(gqa, 64, 1, 17000, 17000) == 128
     # never longer than the longest request (rounded up to whole pages)
     assert pkv.pkv_suggest_split(gqa, 64, 1, 10, 10) == 16
