@@ -21,38 +21,54 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kDirectRows = 4;  // rows per thread group on the one-pass path
+// The step form's own work in a merge workgroup, after the request's verdict
+// is known: the flag (workgroup `first`, thread 0) and, when the request
+// stands, the append of its new token by threads ch < 16 of the first query
+// head of each kv head (K chunks, then V), the row of position L - 1 of the
+// block-table page pid, encoded as the append encodes it.
+__device__ __forceinline__ void step_epilogue(const StepCombineArgs& sa, int b, int h, int ch,
+                                              bool first, bool appender, bool aborted, int32_t L,
+                                              int32_t pid, const uint4& nw0, const uint4& nw1) {
+  if (first && threadIdx.x == 0) sa.abort_out[b] = aborted ? 1 : 0;
+  if (!appender || aborted) return;
+  const int g = h / sa.group;
+  const int64_t row =
+      (static_cast<int64_t>(pid) * sa.kv_heads + g) * sa.page_size + (L - 1) % sa.page_size;
+  const int64_t dst = row * sa.head_dim + 16 * (ch & 7);
+  uint8_t* pool = ch < 8 ? sa.k_pool : sa.v_pool;
+  if (sa.e4m3) {
+    *reinterpret_cast<uint4*>(pool + dst) =
+        pkv::encode16(nw0, nw1, (ch < 8 ? sa.k_scale : sa.v_scale)[g]);
+  } else {
+    uint4* d = reinterpret_cast<uint4*>(pool + 2 * dst);
+    d[0] = nw0;
+    d[1] = nw1;
+  }
+}
 
-// One workgroup of 256 threads per (request, query head). The maximum lse is
-// reduced over the workgroup. Then, 256 split rows at a time, the rows that
-// hold tokens (lse > -inf; the latent kernel leaves the other rows of a run
-// of splits it merged empty) are listed in LDS in split order, with their
-// weights, and the threads split into P = 256 / (Dv / 4) groups: group sg
-// merges listed rows sg, sg + P, ... with each thread owning one 16-byte
-// chunk of the head, so a workgroup reads P whole split rows per step and
-// consecutive steps' loads are independent. The P partial sums meet in LDS.
-// The order of every sum is fixed, so the result is the same bits on every
-// run.
-//
-// When every split row of a head fits in one pass (kRows rows per thread
-// group, max_splits <= kP * kRows), the rows' lse and o chunks are all
-// loaded at the start, beside the request's length: rows are bounded by
-// max_splits, not by the length, so every load is in the buffers, and rows
-// past the length are dropped afterwards. One memory round trip instead of
-// three (length, lse, o).
-template <int DV, bool kDirect, bool kStep = false>
-__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o_part,
-                                                      const float* __restrict__ lse_part,
-                                                      const int32_t* __restrict__ seq_lens,
-                                                      int heads, int split_tokens, int max_splits,
-                                                      int max_seq_len,
-                                                      const uint8_t* __restrict__ abort_flags,
-                                                      uint16_t* __restrict__ out,
-                                                      float* __restrict__ lse_out,
-                                                      StepCombineArgs sa) {
-  constexpr int kC = DV / 4;     // 16-byte chunks per split row
-  constexpr int kP = 256 / kC;   // split rows merged side by side
-  constexpr int kRows = kDirectRows;
+// More split rows than the register-held merges below take, or rows that
+// may be empty (the latent kernel leaves most rows of a head empty: a run of
+// splits it decoded together writes its partial in its first split's row):
+// the merge lists the rows that hold a partial before reading any. One
+// workgroup of 256 threads per (request, query head) reduces the maximum lse
+// over the rows, then, 256 rows at a time, lists (in LDS, in split order)
+// the rows whose lse is not -inf, with their weights; the threads form P =
+// 256 / (Dv / 4) groups and group sg merges listed rows sg, sg + P, ...,
+// each thread owning one 16-byte chunk of the head. The P partial sums meet
+// in LDS. The order of every sum is fixed, so the result is the same bits on
+// every run.
+template <int DV, bool kStep>
+__global__ void __launch_bounds__(256) combine_list_kernel(const float* __restrict__ o_part,
+                                                           const float* __restrict__ lse_part,
+                                                           const int32_t* __restrict__ seq_lens,
+                                                           int heads, int split_tokens,
+                                                           int max_splits, int max_seq_len,
+                                                           const uint8_t* __restrict__ abort_flags,
+                                                           uint16_t* __restrict__ out,
+                                                           float* __restrict__ lse_out,
+                                                           StepCombineArgs sa) {
+  constexpr int kC = DV / 4;    // 16-byte chunks per split row
+  constexpr int kP = 256 / kC;  // split rows merged side by side
   const int b = blockIdx.y;
   const int h = blockIdx.x;
   const int t = threadIdx.x;
@@ -60,17 +76,20 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   const int sg = t / kC, ch = t % kC;
   const int64_t bh = static_cast<int64_t>(b) * heads + h;
   const int32_t L = seq_lens[b];
-  // step form: the flag is the OR of the units' verdicts, known after the
-  // first barrier (every unit of a request ran)
+  // step form: the request's flag is the OR of its units' verdicts, known
+  // after the first barrier
   bool aborted = !kStep && abort_flags && abort_flags[b];
   const bool overflow = L > max_seq_len;
   const int n = (overflow || aborted || L <= 0) ? 0 : (L + split_tokens - 1) / split_tokens;
-  const uint8_t* uflags = kStep ? sa.unit_flags + static_cast<int64_t>(b) * max_splits : nullptr;
-  // step form: the new token's chunk this thread appends (threads 0 .. 15 of
-  // the first query head of each kv head; K chunks, then V), loaded now
+  const float* lse = lse_part + bh * max_splits;
+  const float4* op = reinterpret_cast<const float4*>(o_part + bh * max_splits * DV);
   const bool appender = kStep && t < 16 && h % sa.group == 0 && L >= 1;
   uint4 nw0 = make_uint4(0u, 0u, 0u, 0u), nw1 = nw0;
+  int32_t pid = 0;
+  bool ubad = false;
   if constexpr (kStep) {
+    const int j = min(max(L - 1, 0) / sa.page_size, sa.max_pages - 1);
+    pid = sa.block_table[static_cast<int64_t>(b) * sa.max_pages + j];
     if (appender) {
       const uint16_t* src = (t < 8 ? sa.k_new : sa.v_new) +
                             (static_cast<int64_t>(b) * sa.kv_heads + h / sa.group) * sa.head_dim +
@@ -78,17 +97,10 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
       nw0 = *reinterpret_cast<const uint4*>(src);
       nw1 = *reinterpret_cast<const uint4*>(src + 8);
     }
+    if (sa.expected_tags)
+      for (int c = t; c < n; c += 256)
+        ubad = ubad || sa.unit_flags[static_cast<int64_t>(b) * max_splits + c] != 0;
   }
-  // step form: the page of the request's last position (clamped into the
-  // block-table row; used only when the request stands), loaded beside the
-  // partials so the append at the end waits for nothing
-  int32_t pid = 0;
-  auto last_page = [&]() __attribute__((always_inline)) {
-    const int j = min(max(L - 1, 0) / sa.page_size, sa.max_pages - 1);
-    return sa.block_table[static_cast<int64_t>(b) * sa.max_pages + j];
-  };
-  const float* lse = lse_part + bh * max_splits;
-  const float4* op = reinterpret_cast<const float4*>(o_part + bh * max_splits * DV);
 
   __shared__ float red[4];
   __shared__ int any_s[4];
@@ -101,71 +113,15 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float den = 0.0f;
-  float M;
-  bool empty;
-  if constexpr (kDirect) {
-    // rows sg + kP j of this thread's group, all loaded at once
-    float lr[kRows];
-    float4 vr[kRows];
-#pragma unroll
-    for (int j = 0; j < kRows; ++j) {
-      const int r = sg + kP * j;
-      lr[j] = r < max_splits ? lse[r] : -INFINITY;
-      vr[j] = r < max_splits ? op[static_cast<int64_t>(r) * kC + ch] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    if constexpr (kStep) pid = last_page();
-    // step form: the units' verdicts (max_splits <= 256 here)
-    const bool ubad = kStep && sa.expected_tags && t < n && uflags[t] != 0;
-    float mx = -INFINITY;
-    bool any = false;
-#pragma unroll
-    for (int j = 0; j < kRows; ++j) {
-      if (sg + kP * j >= n) lr[j] = -INFINITY;  // past the request's length
-      mx = fmaxf(mx, lr[j]);
-      any = any || lr[j] != -INFINITY;
-    }
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    const bool wave_any = __ballot(any) != 0;
-    const bool wave_bad = __ballot(ubad) != 0;
-    if (lane == 0) {
-      red[wave] = mx;
-      any_s[wave] = wave_any;
-      bad_s[wave] = wave_bad;
-    }
-    __syncthreads();
-    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    if constexpr (kStep) aborted = (bad_s[0] | bad_s[1] | bad_s[2] | bad_s[3]) != 0;
-    // empty: no row holds a partial (a NaN lse is a partial: it makes the
-    // output NaN, which fmaxf alone would hide)
-    empty = (any_s[0] | any_s[1] | any_s[2] | any_s[3]) == 0;
-    if (!empty && !aborted) {
-#pragma unroll
-      for (int j = 0; j < kRows; ++j) {
-        if (lr[j] != -INFINITY) {  // a row that holds a partial
-          const float w = exp2f((lr[j] - M) * kLog2e);
-          den += w;
-          acc.x += w * vr[j].x;
-          acc.y += w * vr[j].y;
-          acc.z += w * vr[j].z;
-          acc.w += w * vr[j].w;
-        }
-      }
-    }
-  } else {
   // the first 256 rows' lse, kept for the listing below
   const float lse0 = t < n ? lse[t] : -INFINITY;
-  if constexpr (kStep) pid = last_page();
   float mx = lse0;
   bool any = lse0 != -INFINITY;
-  bool ubad = false;
   for (int c = t + 256; c < n; c += 256) {
     const float lc = lse[c];
     mx = fmaxf(mx, lc);
     any = any || lc != -INFINITY;
   }
-  if constexpr (kStep)
-    if (sa.expected_tags)
-      for (int c = t; c < n; c += 256) ubad = ubad || uflags[c] != 0;
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   const bool wave_any = __ballot(any) != 0;
   const bool wave_bad = __ballot(ubad) != 0;
@@ -175,10 +131,19 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     bad_s[wave] = wave_bad;
   }
   __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  empty = (any_s[0] | any_s[1] | any_s[2] | any_s[3]) == 0;
-  if constexpr (kStep) aborted = (bad_s[0] | bad_s[1] | bad_s[2] | bad_s[3]) != 0;
-
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  // empty: no row holds a partial (a NaN lse is a partial: it makes the
+  // output NaN, which fmaxf alone would hide)
+  const bool empty = (any_s[0] | any_s[1] | any_s[2] | any_s[3]) == 0;
+  if constexpr (kStep) {
+    aborted = (bad_s[0] | bad_s[1] | bad_s[2] | bad_s[3]) != 0;
+    // a request with no units (length past max_seq_len) is checked here in
+    // full, by every workgroup of the request (the same verdict in each)
+    if (overflow && sa.expected_tags)
+      aborted = pkv::check_request(sa.page_tags, sa.num_pages, sa.page_size, sa.block_table,
+                                   sa.expected_tags, seq_lens, sa.max_pages, b) != 0;
+    step_epilogue(sa, b, h, t, h == 0, appender, aborted, L, pid, nw0, nw1);
+  }
   if (!empty && !aborted) {
     for (int base = 0; base < n; base += 256) {
       const int c = base + t;
@@ -212,32 +177,6 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
       __syncthreads();  // the list is read before the next round writes it
     }
   }
-  }
-  if constexpr (kStep) {
-    // a request with no units (length past max_seq_len) is checked here in
-    // full, by every workgroup of the request (the same verdict in each)
-    if (overflow && sa.expected_tags)
-      aborted = pkv::check_request(sa.page_tags, sa.num_pages, sa.page_size, sa.block_table,
-                                   sa.expected_tags, seq_lens, sa.max_pages, b) != 0;
-    if (h == 0 && t == 0) sa.abort_out[b] = aborted ? 1 : 0;
-    if (appender && !aborted) {
-      // the request stands: its new token goes to the row of position L - 1
-      // (in the pool, since the check passed), encoded as the append does
-      const int g = h / sa.group;
-      const int64_t row =
-          (static_cast<int64_t>(pid) * sa.kv_heads + g) * sa.page_size + (L - 1) % sa.page_size;
-      const int64_t dst = row * sa.head_dim + 16 * (t & 7);
-      uint8_t* pool = t < 8 ? sa.k_pool : sa.v_pool;
-      if (sa.e4m3) {
-        *reinterpret_cast<uint4*>(pool + dst) =
-            pkv::encode16(nw0, nw1, (t < 8 ? sa.k_scale : sa.v_scale)[g]);
-      } else {
-        uint4* d = reinterpret_cast<uint4*>(pool + 2 * dst);
-        d[0] = nw0;
-        d[1] = nw1;
-      }
-    }
-  }
   acc_s[sg][ch] = acc;
   if (ch == 0) den_s[sg] = den;
   __syncthreads();
@@ -258,6 +197,172 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     float l = M + __log2f(D) * kLn2;
     if (aborted || n == 0 || empty) l = -INFINITY;
     if (overflow && !aborted) l = NAN;
+    lse_out[bh] = l;
+  }
+}
+
+// Up to P kR split rows per head, every one holding a partial (the
+// grouped-query kernels write one per split), so nothing needs listing: one
+// 256-thread workgroup per (request, query head), the threads in P = 256 /
+// (Dv / 4) groups of one 16-byte chunk each; group sg takes rows sg, sg + P,
+// ..., every load issued before any is waited for (one memory latency after
+// the request's length), and sums them against its own maximum. The P groups
+// meet in LDS in group order, each group's sums scaled to the common maximum.
+// The order of every sum is fixed, so the result is the same bits on every
+// run.
+template <int DV, int kR, bool kStep>
+__global__ void __launch_bounds__(256) combine_groups_kernel(const float* __restrict__ o_part,
+                                                             const float* __restrict__ lse_part,
+                                                             const int32_t* __restrict__ seq_lens,
+                                                             int heads, int split_tokens,
+                                                             int max_splits, int max_seq_len,
+                                                             const uint8_t* __restrict__ abort_flags,
+                                                             uint16_t* __restrict__ out,
+                                                             float* __restrict__ lse_out,
+                                                             StepCombineArgs sa) {
+  constexpr int kC = DV / 4;    // 16-byte chunks per split row
+  constexpr int kP = 256 / kC;  // row groups
+  static_assert(kP >= 4, "the groups' meeting below takes at most 64 threads per chunk");
+  const int b = blockIdx.y;
+  const int h = blockIdx.x;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int sg = t / kC, ch = t % kC;
+  const int64_t bh = static_cast<int64_t>(b) * heads + h;
+  const float* lse = lse_part + bh * max_splits;
+  const float4* op = reinterpret_cast<const float4*>(o_part + bh * max_splits * DV);
+  const int32_t L = seq_lens[b];
+  const bool overflow = L > max_seq_len;
+  // rows the length covers (a request the flags abort is dropped at the end)
+  const int n = (overflow || L <= 0) ? 0 : min((L + split_tokens - 1) / split_tokens, max_splits);
+
+  // step form: the new token's chunk (threads 0 .. 15 of the first query
+  // head of each kv head), the page of the last position, and the verdicts
+  // of the first 256 splits (thread t reads split t's; rows past the length
+  // read the last row's and are dropped)
+  const bool appender = kStep && t < 16 && h % sa.group == 0 && L >= 1;
+  uint4 nw0 = make_uint4(0u, 0u, 0u, 0u), nw1 = nw0;
+  int32_t pid = 0;
+  uint32_t uflag = 0;
+  if constexpr (kStep) {
+    const int j = min(max(L - 1, 0) / sa.page_size, sa.max_pages - 1);
+    pid = sa.block_table[static_cast<int64_t>(b) * sa.max_pages + j];
+    if (appender) {
+      const uint16_t* src = (t < 8 ? sa.k_new : sa.v_new) +
+                            (static_cast<int64_t>(b) * sa.kv_heads + h / sa.group) * sa.head_dim +
+                            16 * (t & 7);
+      nw0 = *reinterpret_cast<const uint4*>(src);
+      nw1 = *reinterpret_cast<const uint4*>(src + 8);
+    }
+    uflag = sa.unit_flags[static_cast<int64_t>(b) * max_splits + min(t, max(n, 1) - 1)];
+  }
+  int abf = 0;  // the abort flag, loaded behind the rows
+
+  float m = -INFINITY, den = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  bool any = false;
+  // the rows: every load issued before any is waited for, the rows a group
+  // takes bounded by a workgroup-uniform count (a uniform branch per row; a
+  // row past the length reads the last row again and is dropped)
+  if (n > 0) {
+    float lr[kR];
+    float4 vr[kR];
+    const int jn = min(kR, (n + kP - 1) / kP);
+#pragma unroll
+    for (int j = 0; j < kR; ++j) {
+      lr[j] = -INFINITY;
+      vr[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int j = 0; j < kR; ++j) {
+      if (j < jn) {
+        const int c = min(sg + kP * j, n - 1);
+        lr[j] = lse[c];
+        vr[j] = op[static_cast<int64_t>(c) * kC + ch];
+      }
+    }
+    if (!kStep && abort_flags) abf = abort_flags[b];
+#pragma unroll
+    for (int j = 0; j < kR; ++j)
+      asm volatile("" : : "v"(lr[j]), "v"(vr[j].x), "v"(vr[j].y), "v"(vr[j].z), "v"(vr[j].w));
+#pragma unroll
+    for (int j = 0; j < kR; ++j) {
+      if (sg + kP * j >= n) lr[j] = -INFINITY;
+      m = fmaxf(m, lr[j]);
+      any = any || lr[j] != -INFINITY;
+    }
+#pragma unroll
+    for (int j = 0; j < kR; ++j) {
+      if (lr[j] != -INFINITY) {
+        const float w = exp2f((lr[j] - m) * kLog2e);
+        den += w;
+        acc.x += w * vr[j].x;
+        acc.y += w * vr[j].y;
+        acc.z += w * vr[j].z;
+        acc.w += w * vr[j].w;
+      }
+    }
+  }
+  bool ubad = kStep && sa.expected_tags && t < n && uflag != 0;
+  if constexpr (kStep)
+    if (sa.expected_tags)
+      for (int c = t + 256; c < n; c += 256)
+        ubad = ubad || sa.unit_flags[static_cast<int64_t>(b) * max_splits + c] != 0;
+
+  __shared__ float m_s[kP];
+  __shared__ float den_s[kP];
+  __shared__ float4 acc_s[kP][kC];
+  __shared__ int any_s[4];
+  __shared__ int bad_s[4];
+  acc_s[sg][ch] = acc;
+  if (ch == 0) {
+    m_s[sg] = m;
+    den_s[sg] = den;
+  }
+  const bool wave_any = __ballot(any) != 0;
+  const bool wave_bad = __ballot(ubad) != 0;
+  if (lane == 0) {
+    any_s[wave] = wave_any;
+    bad_s[wave] = wave_bad;
+  }
+  __syncthreads();
+  const bool empty = (any_s[0] | any_s[1] | any_s[2] | any_s[3]) == 0;
+  bool aborted = abf != 0;
+  if constexpr (kStep) {
+    aborted = (bad_s[0] | bad_s[1] | bad_s[2] | bad_s[3]) != 0;
+    // a request with no units (length past max_seq_len) is checked here in
+    // full, by every workgroup of the request (the same verdict in each)
+    if (overflow && sa.expected_tags)
+      aborted = pkv::check_request(sa.page_tags, sa.num_pages, sa.page_size, sa.block_table,
+                                   sa.expected_tags, seq_lens, sa.max_pages, b) != 0;
+    step_epilogue(sa, b, h, t, h == 0, appender, aborted, L, pid, nw0, nw1);
+  }
+  // the groups meet: M over their maxima, each group's sums scaled to it
+  float M = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < kP; ++g) M = fmaxf(M, m_s[g]);
+  float D = 0.0f;
+  float fg[kP];
+#pragma unroll
+  for (int g = 0; g < kP; ++g) {
+    fg[g] = m_s[g] == -INFINITY ? 0.0f : exp2f((m_s[g] - M) * kLog2e);
+    D += den_s[g] * fg[g];
+  }
+  const bool zero = aborted || n == 0 || empty;
+  const bool nan = overflow && !aborted;
+  for (int d = t; d < DV; d += 256) {
+    float x = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kP; ++g) x += reinterpret_cast<const float*>(acc_s[g])[d] * fg[g];
+    x /= D;
+    if (zero) x = 0.0f;
+    if (nan) x = NAN;
+    out[bh * DV + d] = pkv::f32_to_bf16_rne(x);
+  }
+  if (lse_out && t == 0) {
+    float l = M + __log2f(D) * kLn2;
+    if (zero) l = -INFINITY;
+    if (nan) l = NAN;
     lse_out[bh] = l;
   }
 }
@@ -354,22 +459,7 @@ __global__ void __launch_bounds__(256) combine_rows_kernel(const float* __restri
     if (overflow && sa.expected_tags)
       aborted = pkv::check_request(sa.page_tags, sa.num_pages, sa.page_size, sa.block_table,
                                    sa.expected_tags, seq_lens, sa.max_pages, b) != 0;
-    if (blockIdx.x == 0 && t == 0) sa.abort_out[b] = aborted ? 1 : 0;
-    if (appender && !aborted) {
-      const int g = h / sa.group;
-      const int64_t row =
-          (static_cast<int64_t>(pid) * sa.kv_heads + g) * sa.page_size + (L - 1) % sa.page_size;
-      const int64_t dst = row * sa.head_dim + 16 * (ch & 7);
-      uint8_t* pool = ch < 8 ? sa.k_pool : sa.v_pool;
-      if (sa.e4m3) {
-        *reinterpret_cast<uint4*>(pool + dst) =
-            pkv::encode16(nw0, nw1, (ch < 8 ? sa.k_scale : sa.v_scale)[g]);
-      } else {
-        uint4* d = reinterpret_cast<uint4*>(pool + 2 * dst);
-        d[0] = nw0;
-        d[1] = nw1;
-      }
-    }
+    step_epilogue(sa, b, h, ch, blockIdx.x == 0, appender, aborted, L, pid, nw0, nw1);
   }
 
   // M = max lse over the rows that hold tokens; empty: no row holds a
@@ -419,67 +509,58 @@ __global__ void __launch_bounds__(256) combine_rows_kernel(const float* __restri
   }
 }
 
+// The merge kernels for head dim DV; kStep: the step form (head dim 128).
+template <int DV, bool kStep>
+int launch_form(const float* o_part, const float* lse_part, const int32_t* seq_lens, int batch,
+                int heads, int split_tokens, int max_splits, int max_seq_len,
+                const uint8_t* abort_flags, uint16_t* out, float* lse_out,
+                const StepCombineArgs& a, hipStream_t stream) {
+  constexpr int kP = 256 / (DV / 4);
+  constexpr int kR = 24;  // rows per thread of the row-group merge
+  const dim3 grid(heads, batch);
+  // every row in registers: one workgroup per kP heads (up to 32 rows below
+  // head dim 512, 16 at 512; the output written 8 bytes at a time)
+  const dim3 rgrid((heads + kP - 1) / kP, batch);
+  const bool out8 = (reinterpret_cast<uintptr_t>(out) & 7u) == 0;
+  if (out8 && max_splits <= 16) {
+    combine_rows_kernel<DV, 16, kStep><<<rgrid, 256, 0, stream>>>(
+        o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags,
+        out, lse_out, a);
+  } else if constexpr (DV <= 256) {
+    if (out8 && max_splits <= 32)
+      combine_rows_kernel<DV, 32, kStep><<<rgrid, 256, 0, stream>>>(
+          o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags,
+          out, lse_out, a);
+    else if (max_splits <= kP * kR)
+      combine_groups_kernel<DV, kR, kStep><<<grid, 256, 0, stream>>>(
+          o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags,
+          out, lse_out, a);
+    else
+      combine_list_kernel<DV, kStep><<<grid, 256, 0, stream>>>(
+          o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags,
+          out, lse_out, a);
+  } else {
+    combine_list_kernel<DV, kStep><<<grid, 256, 0, stream>>>(
+        o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags,
+        out, lse_out, a);
+  }
+  return pkv::launch_status();
+}
+
 template <int DV>
 int launch(const float* o_part, const float* lse_part, const int32_t* seq_lens, int batch,
            int heads, int split_tokens, int max_splits, int max_seq_len,
            const uint8_t* abort_flags, uint16_t* out, float* lse_out, const StepCombineArgs* sa,
            hipStream_t stream) {
-  constexpr int kP = 256 / (DV / 4);
-  const dim3 grid(heads, batch);
-  const bool direct = max_splits <= kP * kDirectRows;
-  // every row in registers: one workgroup per kP heads (up to 32 rows below
-  // head dim 512, 16 at 512; the output written 8 bytes at a time)
-  const dim3 rgrid((heads + kP - 1) / kP, batch);
-  const bool out8 = (reinterpret_cast<uintptr_t>(out) & 7u) == 0;
-  if (out8 && (max_splits <= 16 || (max_splits <= 32 && DV <= 256))) {
-    const bool r16 = max_splits <= 16;
-    if (sa) {
-      if constexpr (DV == 128) {
-        if (r16)
-          combine_rows_kernel<DV, 16, true><<<rgrid, 256, 0, stream>>>(
-              o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, nullptr,
-              out, lse_out, *sa);
-        else
-          combine_rows_kernel<DV, 32, true><<<rgrid, 256, 0, stream>>>(
-              o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, nullptr,
-              out, lse_out, *sa);
-        return pkv::launch_status();
-      }
-      return PKV_EUNSUPPORTED;
-    }
-    if (r16)
-      combine_rows_kernel<DV, 16, false><<<rgrid, 256, 0, stream>>>(
-          o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags,
-          out, lse_out, StepCombineArgs{});
-    else if constexpr (DV <= 256)
-      combine_rows_kernel<DV, 32, false><<<rgrid, 256, 0, stream>>>(
-          o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags,
-          out, lse_out, StepCombineArgs{});
-    return pkv::launch_status();
-  }
   if (sa) {
-    if constexpr (DV == 128) {
-      if (direct)
-        combine_kernel<DV, true, true><<<grid, 256, 0, stream>>>(
-            o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, nullptr, out,
-            lse_out, *sa);
-      else
-        combine_kernel<DV, false, true><<<grid, 256, 0, stream>>>(
-            o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, nullptr, out,
-            lse_out, *sa);
-      return pkv::launch_status();
-    }
+    if constexpr (DV == 128)
+      return launch_form<DV, true>(o_part, lse_part, seq_lens, batch, heads, split_tokens,
+                                   max_splits, max_seq_len, nullptr, out, lse_out, *sa, stream);
     return PKV_EUNSUPPORTED;
   }
-  if (direct)
-    combine_kernel<DV, true><<<grid, 256, 0, stream>>>(o_part, lse_part, seq_lens, heads,
-                                                       split_tokens, max_splits, max_seq_len,
-                                                       abort_flags, out, lse_out, StepCombineArgs{});
-  else
-    combine_kernel<DV, false><<<grid, 256, 0, stream>>>(o_part, lse_part, seq_lens, heads,
-                                                        split_tokens, max_splits, max_seq_len,
-                                                        abort_flags, out, lse_out, StepCombineArgs{});
-  return pkv::launch_status();
+  return launch_form<DV, false>(o_part, lse_part, seq_lens, batch, heads, split_tokens,
+                                max_splits, max_seq_len, abort_flags, out, lse_out,
+                                StepCombineArgs{}, stream);
 }
 
 }  // namespace
