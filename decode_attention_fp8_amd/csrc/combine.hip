@@ -201,6 +201,138 @@ __global__ void __launch_bounds__(256) combine_list_kernel(const float* __restri
   }
 }
 
+// The latent merge at head dim 512: rows mostly empty (a run of splits the
+// latent kernel decoded together writes its partial in its first split's
+// row), so the rows that hold a partial are listed before any is read. A
+// 256-thread workgroup takes HW = 256 / (Dv / 4) heads (2 at 512), the
+// Dv / 4 threads of a head one 16-byte chunk each. A thread loads the lse of
+// rows ch, ch + Dv / 4, ... of its head at once, beside the request's length
+// (rows past max_splits read the last row again; rows past the length are
+// dropped after), so the lse and the length cost one memory latency; the
+// head's maximum and its list of rows holding a partial (in split order)
+// come from wave votes and LDS, and every thread then reads its chunk of the
+// listed rows. The order of every sum is fixed, so the result is the same
+// bits on every run.
+template <int DV, int kL>
+__global__ void __launch_bounds__(256) combine_sparse_kernel(const float* __restrict__ o_part,
+                                                             const float* __restrict__ lse_part,
+                                                             const int32_t* __restrict__ seq_lens,
+                                                             int heads, int split_tokens,
+                                                             int max_splits, int max_seq_len,
+                                                             const uint8_t* __restrict__ abort_flags,
+                                                             uint16_t* __restrict__ out,
+                                                             float* __restrict__ lse_out) {
+  constexpr int kC = DV / 4;    // threads per head
+  constexpr int HW = 256 / kC;  // heads per workgroup
+  constexpr int kWavesPerHead = kC / 64;
+  static_assert(kC % 64 == 0 && kC <= 256, "a head's chunks fill whole waves");
+  const int b = blockIdx.y;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int hh = t / kC, ch = t % kC;
+  const int hw = wave % kWavesPerHead;  // the wave's place within its head
+  const int h = blockIdx.x * HW + hh;
+  const bool head_ok = h < heads;
+  const int64_t bh = static_cast<int64_t>(b) * heads + (head_ok ? h : 0);
+  const float* lse = lse_part + bh * max_splits;
+  const float4* op = reinterpret_cast<const float4*>(o_part + bh * max_splits * DV);
+
+  // the lse of rows ch + kC j (kL of them cover max_splits), then the length
+  float lr[kL];
+#pragma unroll
+  for (int j = 0; j < kL; ++j) lr[j] = lse[min(ch + kC * j, max_splits - 1)];
+  const int32_t L = seq_lens[b];
+  int abf = 0;
+  if (abort_flags) abf = abort_flags[b];
+#pragma unroll
+  for (int j = 0; j < kL; ++j) asm volatile("" : : "v"(lr[j]));
+  asm volatile("" : : "v"(abf));
+  const bool aborted = abf != 0;
+  const bool overflow = L > max_seq_len;
+  const int n = (overflow || aborted || L <= 0) ? 0 : (L + split_tokens - 1) / split_tokens;
+
+  __shared__ float red_s[HW][kWavesPerHead];
+  __shared__ int any_s[HW][kWavesPerHead];
+  __shared__ int cnt_s[HW][kWavesPerHead][kL];
+  __shared__ int idx_s[HW][kL * kC];
+  float mx = -INFINITY;
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < kL; ++j) {
+    if (ch + kC * j >= n) lr[j] = -INFINITY;
+    mx = fmaxf(mx, lr[j]);
+    any = any || lr[j] != -INFINITY;
+  }
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  const bool wave_any = __ballot(any) != 0;
+  // per row block j: this wave's rows holding a partial, in lane order
+  uint64_t bal[kL];
+#pragma unroll
+  for (int j = 0; j < kL; ++j) bal[j] = __ballot(lr[j] != -INFINITY);
+  if (lane == 0) {
+    red_s[hh][hw] = mx;
+    any_s[hh][hw] = wave_any;
+#pragma unroll
+    for (int j = 0; j < kL; ++j) cnt_s[hh][hw][j] = __popcll(bal[j]);
+  }
+  __syncthreads();
+  float M = -INFINITY;
+  bool hany = false;
+#pragma unroll
+  for (int w = 0; w < kWavesPerHead; ++w) {
+    M = fmaxf(M, red_s[hh][w]);
+    hany = hany || any_s[hh][w];
+  }
+  // list position of row ch + kC j: rows of earlier blocks, then of earlier
+  // waves in this block, then of earlier lanes in this wave
+  int listed = 0;
+#pragma unroll
+  for (int j = 0; j < kL; ++j) {
+    int pos = listed;
+#pragma unroll
+    for (int w = 0; w < kWavesPerHead; ++w) pos += w < hw ? cnt_s[hh][w][j] : 0;
+    pos += __popcll(bal[j] & ((1ull << lane) - 1ull));
+    if (lr[j] != -INFINITY) idx_s[hh][pos] = ch + kC * j;
+#pragma unroll
+    for (int w = 0; w < kWavesPerHead; ++w) listed += cnt_s[hh][w][j];
+  }
+  __syncthreads();
+  float den = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (hany) {
+    for (int k = 0; k < listed; ++k) {
+      const int c = idx_s[hh][k];
+      const float w = exp2f((lse[c] - M) * kLog2e);
+      const float4 v = op[static_cast<int64_t>(c) * kC + ch];
+      den += w;
+      acc.x += w * v.x;
+      acc.y += w * v.y;
+      acc.z += w * v.z;
+      acc.w += w * v.w;
+    }
+  }
+  if (!head_ok) return;
+  const bool zero = aborted || n == 0 || !hany;
+  const bool nan = overflow && !aborted;
+  float x[4] = {acc.x / den, acc.y / den, acc.z / den, acc.w / den};
+  uint32_t packed[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    float a0 = x[2 * k], a1 = x[2 * k + 1];
+    if (zero) a0 = a1 = 0.0f;
+    if (nan) a0 = a1 = NAN;
+    packed[k] = static_cast<uint32_t>(pkv::f32_to_bf16_rne(a0)) |
+                (static_cast<uint32_t>(pkv::f32_to_bf16_rne(a1)) << 16);
+  }
+  *reinterpret_cast<uint2*>(out + bh * DV + 4 * ch) = make_uint2(packed[0], packed[1]);
+  if (lse_out && ch == 0) {
+    float l = M + __log2f(den) * kLn2;
+    if (zero) l = -INFINITY;
+    if (nan) l = NAN;
+    lse_out[bh] = l;
+  }
+}
+
 // Up to P kR split rows per head, every one holding a partial (the
 // grouped-query kernels write one per split), so nothing needs listing: one
 // 256-thread workgroup per (request, query head), the threads in P = 256 /
@@ -539,6 +671,11 @@ int launch_form(const float* o_part, const float* lse_part, const int32_t* seq_l
       combine_list_kernel<DV, kStep><<<grid, 256, 0, stream>>>(
           o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags,
           out, lse_out, a);
+  } else if (!kStep && out8 && max_splits <= 2 * (DV / 4)) {
+    // the latent merge: two heads per workgroup, rows listed per head
+    combine_sparse_kernel<DV, 2><<<rgrid, 256, 0, stream>>>(
+        o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags,
+        out, lse_out);
   } else {
     combine_list_kernel<DV, kStep><<<grid, 256, 0, stream>>>(
         o_part, lse_part, seq_lens, heads, split_tokens, max_splits, max_seq_len, abort_flags,
