@@ -66,14 +66,29 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kSlots * kSlotBytes];
   const int lane = threadIdx.x;
   const int col = lane & 15, qg = lane >> 4;
+  // The unit: with one request, unit u is split u / Hkv of kv head u % Hkv
+  // (the work-unit order reduces to that), so its q, page ids and recorded
+  // tags are loaded beside the request's length, one memory latency instead
+  // of two, and the entries past the length are dropped once it is in.
   int b, g, c, L;
-  if (!pkv::find_unit(p, static_cast<int>(blockIdx.x), b, g, c, L)) return;
+  const bool one_req = p.batch == 1;
+  if (one_req) {
+    c = static_cast<int>(blockIdx.x) / p.num_kv_heads;
+    g = static_cast<int>(blockIdx.x) - c * p.num_kv_heads;
+    b = 0;
+    L = 0;
+  } else if (!pkv::find_unit(p, static_cast<int>(blockIdx.x), b, g, c, L)) {
+    return;
+  }
   const int G = p.num_q_heads / p.num_kv_heads;
   const int t_begin = c * p.split_tokens;
-  const int t_end = min(L, t_begin + p.split_tokens);
-  const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
   const int P = p.page_size;
   const int log2P = P == 16 ? 4 : (P == 32 ? 5 : 6);
+  const int first_page = t_begin >> log2P;
+  // pages loaded: the unit's, or with one request the whole split's (within
+  // the block-table row: the launch has ceil(max_seq_len / S) splits)
+  const int load_pages = one_req ? min(p.split_tokens >> log2P, p.max_pages - first_page)
+                                 : (min(L, t_begin + p.split_tokens) - t_begin + P - 1) >> log2P;
 
   // query head col as B operands (heads G .. 15 are zero rows): k-step s,
   // slot 8 qg + j <-> dim 32 qg + 8 s + j. Every lane loads (a padding lane
@@ -97,17 +112,21 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
   // head g) in vector h < kPageVecs (named variables, so that selecting one
   // by a uniform index stays in registers)
   const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_pages;
-  const int first_page = t_begin >> log2P;
-  const int n_pages = (t_end - t_begin + P - 1) >> log2P;
   auto load_page = [&](int h) __attribute__((always_inline)) {
-    return 64 * h + lane < n_pages ? bt[first_page + 64 * h + lane] : -1;
+    return 64 * h + lane < load_pages ? bt[first_page + 64 * h + lane] : -1;
   };
-  const int pg0 = load_page(0), pg1 = load_page(1), pg2 = load_page(2), pg3 = load_page(3);
+  int pg0 = load_page(0), pg1 = load_page(1), pg2 = load_page(2), pg3 = load_page(3);
+  // with one request: its length and abort flag
+  int L1 = 0, ab1 = 0;
+  if (one_req) {
+    L1 = p.seq_lens[0];
+    if (p.abort_flags) ab1 = p.abort_flags[0];
+  }
   // step form: the recorded tags of the unit's pages (kv head 0's units),
-  // and the new token's K and V values (the request's last unit): lanes
-  // 0 .. 2 kNewChunks - 1 each hold one 16-byte chunk of a row, K first
+  // and the new token's K and V values (the request's last unit; with one
+  // request every unit loads them, 256 bytes): lanes 0 .. 2 kNewChunks - 1
+  // each hold one 16-byte chunk of a row, K first
   const bool checker = kStep && g == 0 && p.expected_tags != nullptr;
-  const bool inject = kStep && t_end == L;
   constexpr int kNewChunks = kBf16 ? 16 : 8;  // chunks of a 128-value row
   uint32_t want0 = 0, want1 = 0;  // a step-form unit has at most 128 pages
   uint4 nw0 = make_uint4(0u, 0u, 0u, 0u), nw1 = nw0;
@@ -115,11 +134,11 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
     if (checker) {
       const uint32_t* er = p.expected_tags + static_cast<int64_t>(b) * p.max_pages + first_page;
       auto load_want = [&](int h) __attribute__((always_inline)) {
-        return 64 * h + lane < n_pages ? er[64 * h + lane] : 0u;
+        return 64 * h + lane < load_pages ? er[64 * h + lane] : 0u;
       };
       want0 = load_want(0), want1 = load_want(1);
     }
-    if (inject && lane < 2 * kNewChunks) {
+    if ((one_req || min(L, t_begin + p.split_tokens) == L) && lane < 2 * kNewChunks) {
       const int ch = lane & (kNewChunks - 1);
       const uint16_t* src = (lane < kNewChunks ? p.k_new : p.v_new) +
                             (static_cast<int64_t>(b) * p.num_kv_heads + g) * kD +
@@ -132,9 +151,29 @@ __global__ void __launch_bounds__(64) decode_gqa_mfma_kernel(DecodeParams p) {
   for (int s = 0; s < 4; ++s) asm volatile("" : : "v"(qf[s]));
   asm volatile("" : : "v"(pg0), "v"(pg1), "v"(pg2), "v"(pg3));
   asm volatile("" : : "v"(qk_scale), "v"(o_scale));
+  asm volatile("" : : "v"(L1), "v"(ab1));
   // from here on the only vector memory loads in flight are the ring's
   // (and, in the step form, the pool tags issued before them)
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" : : : "memory");
+  if (one_req) {
+    // the unit exists if the request has this split (as the work-unit
+    // lookup would decide); the split's page entries past it are dropped
+    L = __builtin_amdgcn_readfirstlane(L1);
+    const int n = (__builtin_amdgcn_readfirstlane(ab1) == 0 && L > 0 && L <= p.max_seq_len)
+                      ? (L + p.split_tokens - 1) / p.split_tokens
+                      : 0;
+    if (c >= n) return;
+  }
+  const int t_end = min(L, t_begin + p.split_tokens);
+  const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
+  const int n_pages = (t_end - t_begin + P - 1) >> log2P;
+  if (one_req) {
+    auto keep = [&](int h, int v) __attribute__((always_inline)) {
+      return 64 * h + lane < n_pages ? v : -1;
+    };
+    pg0 = keep(0, pg0), pg1 = keep(1, pg1), pg2 = keep(2, pg2), pg3 = keep(3, pg3);
+  }
+  const bool inject = kStep && t_end == L;
   if (!head_ok) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)

@@ -181,6 +181,44 @@ def test_two_launch_step_page64_and_overlong_requests(kv):
     assert s >= 0 and not poisoned.any()
 
 
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+@pytest.mark.parametrize("case", ["L1", "L15", "L700", "tag", "empty", "overlong", "outside_pool"])
+def test_one_request(kv, case):
+    """One request (its units' places need no lookup, so their loads go out
+    beside its length): the two-launch step equals the three-launch one bit
+    for bit, through tiny, aborted, empty and over-long requests, and a
+    standing request matches the oracle."""
+    L = {"L1": 1, "L15": 15}.get(case, 700)
+    w = W.custom(f"one_{case}", 3500 + L, [L], hq=16, hkv=4, dk=128, dv=128, page=16,
+                 per_head=True)
+
+    def edit(st):
+        if case == "tag":
+            st.expected.view(torch.int32)[0, 20] ^= 1
+        elif case == "empty":
+            st.seq_lens[0] = 0
+        elif case == "outside_pool":
+            st.block_table[0, 3] = st.w.num_pages + 1
+
+    msl = 600 if case == "overlong" else None
+    a, b = _prepare(w, kv, 64, max_seq_len=msl, edit=edit)
+    flags, out = _run_both_and_compare(a, b)
+    assert flags[0] == (1 if case in ("tag", "outside_pool") else 0)
+    if case in ("tag", "outside_pool", "empty"):
+        assert np.all(out[0] == 0.0)
+    elif case == "overlong":
+        assert np.all(np.isnan(out[0]))
+    else:
+        _check_requests(TwoLaunchStateFrom(b), [0])
+
+
+def TwoLaunchStateFrom(st):
+    """The same device state, its step run as the two-launch form again (the
+    pool already holds the appended row; appending it again changes nothing)."""
+    st.__class__ = TwoLaunchState
+    return st
+
+
 @pytest.mark.parametrize("case", ["row_scales", "head_dim_64", "long_split", "latent"])
 def test_three_launch_fallback_shapes(case):
     """Shapes without the two-launch form run the three launches inside the
