@@ -357,11 +357,12 @@ def time_handoff(steps: int, n_pages: int = 8192):
             "kernel": "requant_kernel (bf16 pages -> e4m3, tags)"}
 
 
-def time_drafts(run, T: int, steps: int, warmup: int, read, dec_ms: float):
+def time_drafts(run, T: int, steps: int, warmup: int, read, dec_ms: float, flush):
     """pkv_decode_attn_drafts + pkv_combine over the Runner's resident cache:
     each request verifies its last T tokens together (query j sees the
     context up to L - T + j). The kernel reads the same cache bytes as a
-    one-token decode; flops grow with T (QK^T and PV for T x Hq rows)."""
+    one-token decode; flops grow with T (QK^T and PV for T x Hq rows).
+    Flushed like the step: the kernel's events after each flush."""
     import torch
 
     pkv, w, s = run.pkv, run.w, run.step
@@ -369,8 +370,8 @@ def time_drafts(run, T: int, steps: int, warmup: int, read, dec_ms: float):
     q = torch.randn((w.batch, T, w.num_q_heads, w.head_dim_k), generator=g, device="cuda")
     q = q.to(torch.bfloat16)
     L = s.max_seq_len
-    # the drafts kernel takes up to 64 pages per unit
-    split = min(s.split_tokens, 64 * w.page_size)
+    # the drafts kernel takes up to 128 pages per unit
+    split = min(s.split_tokens, 128 * w.page_size)
     n_split = -(-L // split)
     o_part = torch.empty((w.batch, T * w.num_q_heads, n_split, w.head_dim_v),
                          dtype=torch.float32, device="cuda")
@@ -391,12 +392,14 @@ def time_drafts(run, T: int, steps: int, warmup: int, read, dec_ms: float):
         pkv.pkv_combine(o_part, lse_part, run.lens, split, L, abort, out, lse)
 
     for _ in range(warmup):
+        flush()
         one()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for e in evs:
+        flush()
         one(e)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -406,7 +409,7 @@ def time_drafts(run, T: int, steps: int, warmup: int, read, dec_ms: float):
     flop = 2 * T * w.num_q_heads * (w.head_dim_k + w.head_dim_v) * tokens
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"q_len": T, "split_tokens": split, "decode_ms": round(ms, 5),
-            "eager_ms_per_step": round((t1 - t0) * 1e3 / steps, 5),
+            "wall_ms_per_flushed_step": round((t1 - t0) * 1e3 / steps, 5),
             "kv_gbs": round(gbs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
             "vs_q_len_single_token_decodes": round(T * dec_ms / ms, 3),
@@ -711,7 +714,8 @@ def main():
         if w.latent or w.head_dim_k != 128 or w.head_dim_v != 128:
             rec["drafts"] = {"error": "the drafts path takes head dim 128 without a latent cache"}
         else:
-            rec["drafts"] = time_drafts(run, args.drafts, args.steps, args.warmup, read, dec_ms)
+            rec["drafts"] = time_drafts(run, args.drafts, args.steps, args.warmup, read, dec_ms,
+                                        flush)
     del run
     torch.cuda.empty_cache()
     if not args.no_bf16:

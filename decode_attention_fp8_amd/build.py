@@ -37,8 +37,11 @@ def sources() -> list[str]:
                   glob.glob(os.path.join(HERE, "csrc", "*.cpp")))
 
 
-# per-source device code generation options
-EXTRA = {"decode_gqa_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# per-source device code generation options: MFMA results in VGPRs (with
+# them in AGPRs the compiler copies the accumulators across the register
+# files every tile: 80 copies per tile in the drafts kernel)
+EXTRA = {"decode_gqa_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "decode_drafts.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def compile_command(src: str, obj: str) -> list[str]:

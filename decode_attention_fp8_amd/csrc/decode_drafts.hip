@@ -50,7 +50,7 @@ constexpr int kTile = 32;                    // tokens per tile
 constexpr int kHalf = kTile * kD;            // K (or V) bytes of a tile
 constexpr int kTileBytes = 2 * kHalf;        // K then V: 8 KB
 constexpr int kSlots = 2;
-constexpr int kMaxUnitPages = 64;
+constexpr int kMaxUnitPages = 128;  // two vectors of page ids per lane
 
 // Tile layouts: K chunk c of token row t at c ^ ((t >> 1) & 7) (the 32 rows
 // a K read touches at one chunk land on distinct bank groups); V chunk c of
@@ -96,21 +96,19 @@ __global__ void __launch_bounds__(64 * W) decode_drafts_kernel(DecodeParams p, i
   // tokens this row may see inside the unit: [t_begin, lim)
   const int lim = row_ok ? min(t_end, L - T + j_mine + 1) : t_begin;
 
-  // query as B operands: k-step s covers dims 32(s/2) + 16h + 8(s%2) .. +7
+  // query as B operands: k-step s covers dims 32(s/2) + 16h + 8(s%2) .. +7.
+  // Every lane loads (a lane past the rows reads row 0) and those lanes'
+  // operands are zeroed once the loads are in: zeroing registers a load is
+  // still writing would make the first load complete before the others are
+  // issued.
   bf16x8_t qf[8];
   {
     const int hh = row_ok ? r_mine - j_mine * G : 0;
     const uint16_t* qrow =
         p.q + ((static_cast<int64_t>(b) * T + j_mine) * p.num_q_heads + g * G + hh) * kD;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      if (row_ok) {
-        qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * (s >> 1) + 16 * hl + 8 * (s & 1));
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[s][e] = static_cast<__bf16>(0.0f);
-      }
-    }
+    for (int s = 0; s < 8; ++s)
+      qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * (s >> 1) + 16 * hl + 8 * (s & 1));
   }
   const float qk_scale = p.k_scale[g] * p.sm_scale_log2;
   const float o_scale = p.v_scale[g];
@@ -119,18 +117,36 @@ __global__ void __launch_bounds__(64 * W) decode_drafts_kernel(DecodeParams p, i
   const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_pages;
   const int first_page = t_begin >> log2P;
   const int n_pages = (t_end - t_begin + P - 1) >> log2P;
-  int pg = -1;
+  // the unit's pages: lane j holds pages j and 64 + j
+  int pg = -1, pgh = -1;
   if (lane < n_pages) pg = bt[first_page + lane];
+  if (64 + lane < n_pages) pgh = bt[first_page + 64 + lane];
 #pragma unroll
   for (int s = 0; s < 8; ++s) asm volatile("" : : "v"(qf[s]));
-  asm volatile("" : : "v"(qk_scale), "v"(o_scale), "v"(pg));
+  asm volatile("" : : "v"(qk_scale), "v"(o_scale), "v"(pg), "v"(pgh));
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" : : : "memory");
+  if (!row_ok) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[s][e] = static_cast<__bf16>(0.0f);
+  }
   const bool pg_ok = pg >= 0 && pg < p.num_pages;
-  const uint64_t valid = __ballot(pg_ok);
-  const int64_t blk = (static_cast<int64_t>(pg_ok ? pg : 0) * p.num_kv_heads + g) *
-                      (static_cast<int64_t>(P) * kD);
+  const bool pgh_ok = pgh >= 0 && pgh < p.num_pages;
+  const uint64_t valid = __ballot(pg_ok), validh = __ballot(pgh_ok);
+  auto block_of = [&](int page, bool ok) __attribute__((always_inline)) {
+    return (static_cast<int64_t>(ok ? page : 0) * p.num_kv_heads + g) *
+           (static_cast<int64_t>(P) * kD);
+  };
+  const int64_t blk = block_of(pg, pg_ok), blkh = block_of(pgh, pgh_ok);
   const int off_lo = static_cast<int>(static_cast<uint32_t>(blk));
   const int off_hi = static_cast<int>(static_cast<uint32_t>(static_cast<uint64_t>(blk) >> 32));
+  const int offh_lo = static_cast<int>(static_cast<uint32_t>(blkh));
+  const int offh_hi = static_cast<int>(static_cast<uint32_t>(static_cast<uint64_t>(blkh) >> 32));
+  // page j of the unit is valid (j < 128; a uniform choice of vector)
+  auto page_valid = [&](int j) __attribute__((always_inline)) {
+    return (((j < 64 ? valid : validh) >> (j & 63)) & 1u) != 0;
+  };
 
   // DMA source offsets inside a 16-token group block: lane L fills LDS chunk
   // position L & 7 of group row L >> 3 (first 1 KB) and 8 + (L >> 3)
@@ -146,8 +162,10 @@ __global__ void __launch_bounds__(64 * W) decode_drafts_kernel(DecodeParams p, i
   auto group_base = [&](int gg) __attribute__((always_inline)) {
     const int j = (gg << 4) >> log2P;
     const uint64_t off =
-        (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(off_hi, j))) << 32) |
-        static_cast<uint32_t>(__builtin_amdgcn_readlane(off_lo, j));
+        (static_cast<uint64_t>(static_cast<uint32_t>(
+             __builtin_amdgcn_readlane(j < 64 ? off_hi : offh_hi, j & 63)))
+         << 32) |
+        static_cast<uint32_t>(__builtin_amdgcn_readlane(j < 64 ? off_lo : offh_lo, j & 63));
     return off + static_cast<uint32_t>(((gg << 4) & (P - 1)) * kD);
   };
   // 8 loads per tile, always: a 16-token group past the unit's end loads the
@@ -227,8 +245,8 @@ __global__ void __launch_bounds__(64 * W) decode_drafts_kernel(DecodeParams p, i
     const int tile0 = t_begin + kTile * t;
     // rows past the unit or of a page outside the pool: V to zero (their
     // scores are masked, and 0 * NaN must not reach the accumulators)
-    const bool g0_ok = ((valid >> (((2 * t) << 4) >> log2P)) & 1u) != 0;
-    const bool g1_ok = tile0 + 16 < t_end && ((valid >> (((2 * t + 1) << 4) >> log2P)) & 1u) != 0;
+    const bool g0_ok = page_valid(((2 * t) << 4) >> log2P);
+    const bool g1_ok = tile0 + 16 < t_end && page_valid(((2 * t + 1) << 4) >> log2P);
     const int nv = min(kTile, t_end - tile0);
     if (!g0_ok || !g1_ok || nv < kTile) {
       for (int q = static_cast<int>(threadIdx.x); q < kTile * (kD / 16); q += 64 * W) {

@@ -82,10 +82,12 @@ def test_drafts_many_row_groups_share_tiles(T, hq, hkv):
 
 
 @pytest.mark.parametrize("lens,P,split", [([1, 2, 3, 4], 16, 16), ([33, 31, 32, 47], 16, 32),
-                                          ([129, 64, 65], 64, 64), ([4096 + 3], 32, 512)])
+                                          ([129, 64, 65], 64, 64), ([4096 + 3], 32, 512),
+                                          ([5000, 2049, 1100], 16, 2048)])
 def test_drafts_ragged_lengths_splits_and_short_requests(lens, P, split):
     """Queries that see nothing (L < q_len), split boundaries inside the
-    drafts (empty trailing splits for the first queries), page sizes."""
+    drafts (empty trailing splits for the first queries), page sizes, and
+    128-page units (the second vector of page ids)."""
     w = W.custom(f"drr{len(lens)}_{P}", 93, lens, hq=16, hkv=2, dk=128, dv=128, page=P)
     _check(w, 4, split)
 
