@@ -64,9 +64,12 @@ __device__ __forceinline__ uint32_t vswz(uint32_t t) {
 // W waves per workgroup, one group of 32 query rows each, share every tile:
 // each wave issues 8 / W of the tile's loads, one barrier per tile makes the
 // whole tile visible and frees the slot two tiles ahead (three slots). With
-// W = 1 the wave runs its own two-slot ring without barriers.
+// W = 1 the wave runs its own two-slot ring without barriers. Up to two
+// waves a workgroup the registers are held to 168, three waves per SIMD
+// (they fit without spilling; four and eight waves would spill).
 template <int W>
-__global__ void __launch_bounds__(64 * W) decode_drafts_kernel(DecodeParams p, int row_groups) {
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W <= 2 ? 3 : 1)))
+decode_drafts_kernel(DecodeParams p, int row_groups) {
   constexpr int kRing = W == 1 ? kSlots : 3;
   constexpr int kMine = 8 / W;  // loads per tile issued by each wave
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kTileBytes];
