@@ -25,12 +25,16 @@ constexpr float kLn2 = 0.6931471805599453f;
 // is known: the flag (workgroup `first`, thread 0) and, when the request
 // stands, the append of its new token by threads ch < 16 of the first query
 // head of each kv head (K chunks, then V), the row of position L - 1 of the
-// block-table page pid, encoded as the append encodes it.
+// block-table page pid, encoded as the append encodes it. A position past
+// the block-table row, or a page outside the pool (both possible only
+// without the check), appends nothing, as the append does not.
 __device__ __forceinline__ void step_epilogue(const StepCombineArgs& sa, int b, int h, int ch,
                                               bool first, bool appender, bool aborted, int32_t L,
                                               int32_t pid, const uint4& nw0, const uint4& nw1) {
   if (first && threadIdx.x == 0) sa.abort_out[b] = aborted ? 1 : 0;
-  if (!appender || aborted) return;
+  if (!appender || aborted || (L - 1) / sa.page_size >= sa.max_pages || pid < 0 ||
+      pid >= sa.num_pages)
+    return;
   const int g = h / sa.group;
   const int64_t row =
       (static_cast<int64_t>(pid) * sa.kv_heads + g) * sa.page_size + (L - 1) % sa.page_size;

@@ -132,7 +132,8 @@ __global__ void __launch_bounds__(kThreads) verify_append_kernel(
   if (bad) return;
   if (!slot) {
     const int32_t L = seq_lens[b];
-    if (L < 1) return;
+    // no position (or one past the block-table row): nothing to append
+    if (L < 1 || (L - 1) / page_size >= max_pages) return;
     const int32_t pid = block_table[static_cast<int64_t>(b) * max_pages + (L - 1) / page_size];
     s = static_cast<int64_t>(pid) * page_size + (L - 1) % page_size;
   }

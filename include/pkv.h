@@ -274,7 +274,9 @@ int pkv_combine(const float* o_part, const float* lse_part,
  *   pkv_combine(..., abort_flags = abort_out, out, lse_out)
  * bit for bit, with each request's new token at the row of its last
  * position: slot[b] = block_table[b][(L-1) / P] * P + (L-1) % P for
- * L = seq_lens[b] >= 1 (no token when L <= 0).
+ * L = seq_lens[b] >= 1 (no token when L <= 0, when (L-1) / P >= max_pages,
+ * or when that page lies outside the pool: cases only a step without the
+ * check can reach, since the check aborts such a request).
  *
  * Two-launch form (separate K and V pools, head_dim_k == head_dim_v == 128,
  * e4m3 with per-head scales or bf16, up to 16 query heads per kv head,

@@ -252,6 +252,33 @@ def test_three_launch_fallback_shapes(case):
     assert ok.size and np.all(np.isfinite(out[ok]))
 
 
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+def test_no_check_append_stays_inside_the_pool_and_the_row(kv):
+    """Without the check a request may still reach the step with a length
+    past its block-table row, or with the page of its last position outside
+    the pool. Neither launch form may append then (no read past the row, no
+    write past the pool); both give the same flags, outputs and pools."""
+    w = W.custom("step_bounds", 3160, [300, 450, 200, 100], hq=16, hkv=4, dk=128, dv=128,
+                 page=16, per_head=True)
+
+    def edit(st):
+        P, mp = st.w.page_size, st.block_table.shape[1]
+        st.block_table[1, (450 - 1) // P] = st.w.num_pages + 3  # last page outside the pool
+        st.seq_lens[3] = mp * P + 5                             # past the last request's row
+
+    a, b = _prepare(w, kv, 64, max_seq_len=450, edit=edit, verify=False)
+    before = _pool_bytes(b.cache.k_pool).clone()
+    flags, out = _run_both_and_compare(a, b)
+    assert not flags.any()
+    assert np.all(np.isnan(out[3]))
+    # only requests 0 and 2 appended: every other row is as before
+    after = _pool_bytes(b.cache.k_pool)
+    changed = torch.nonzero((after != before).reshape(after.shape[0], after.shape[1],
+                                                      after.shape[2], -1).any(-1).any(1))
+    rows = {int(p) * w.page_size + int(r) for p, r in changed.tolist()}
+    assert rows <= {int(a.last_slot[0]), int(a.last_slot[2])}, rows
+
+
 def test_sweep_b64_full_size_sampled_against_oracle():
     """The measured workload through the two-launch step, sampled requests
     against the float64 oracle (the new token's row comes from its values)."""
