@@ -295,6 +295,17 @@ def test_sweep_b64_full_size_sampled_against_oracle():
     assert torch.equal(lse2.view(torch.int32), st.step.lse.view(torch.int32))
 
 
+def test_long_context_full_size_sampled_against_oracle():
+    """The long-context workload (4 x 131,072 tokens, page 64, 256-token
+    chunks) as bench.py times it, through the two-launch step: two requests
+    against the float64 oracle (all 512 chunks of each merged), their new
+    tokens' rows poisoned in the pool beforehand."""
+    st = TwoLaunchState(W.long_context(), "fp8")
+    assert pkv.pkv_step_launches(st.cache, st.w.num_q_heads, st.step.split_tokens) == 2
+    _poison_rows(st, _last_slots(st, st.seq_lens.cpu().numpy()))
+    _check_requests(st, [0, 3], kv_heads=[5])
+
+
 @pytest.mark.parametrize("kv", ["fp8", "bf16"])
 @pytest.mark.parametrize("make", [lambda: W.sweep(64), W.long_context],
                          ids=["sweep_b64", "long_b4"])
