@@ -347,7 +347,8 @@ int pkv_step_launches(const pkv_cache* cache, int32_t num_q_heads, int32_t split
  * out bf16 [batch][q_len][num_q_heads][head_dim_v].
  * Other arguments and errors as for pkv_decode_attn; also EINVAL for
  * q_len outside [1, 64]. EUNSUPPORTED unless the cache is e4m3 with
- * separate K and V pools and head_dim_k == head_dim_v == 128.
+ * separate K and V pools and head_dim_k == head_dim_v == 128, and for
+ * split_tokens > 128 * page_size (a split's page ids are held in registers).
  */
 int pkv_decode_attn_drafts(const pkv_cache* cache, const void* q, int32_t num_q_heads,
                            int32_t q_len, const int32_t* block_table, const int32_t* seq_lens,

@@ -58,6 +58,18 @@ def _check(w, T, split, seed=0, requests=None, aborted=()):
         assert np.allclose(lse[b][fin], lse_ref[fin], atol=1e-3, rtol=1e-4)
 
 
+def test_drafts_split_past_128_pages_is_unsupported():
+    """A split's page ids are held in registers, 128 per unit: a 4096-token
+    split at page 16 (256 pages) is refused before anything is launched."""
+    w = W.custom("dr_long", 90, [5000, 300], hq=64, hkv=8, dk=128, dv=128, page=16)
+    st = State(w, "fp8")
+    q = torch.zeros((w.batch, 2, w.num_q_heads, w.head_dim_k), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(pkv.PkvError) as e:
+        _run_drafts(st, q, 4096)
+    assert e.value.status == pkv.PKV_EUNSUPPORTED
+    _check(w, 2, 2048, requests=[0, 1])  # 128 pages: the limit itself runs
+
+
 @pytest.mark.parametrize("T", [1, 2, 4])
 def test_drafts_production_heads(T):
     """64 query / 8 kv heads: T x 8 <= 32 query rows per kv head."""
