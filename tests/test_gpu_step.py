@@ -129,7 +129,8 @@ def _edits(st):
 
 
 @pytest.mark.parametrize("kv", ["fp8", "bf16"])
-@pytest.mark.parametrize("heads", [(16, 4), (16, 1), (8, 8)], ids=["G4", "G16", "G1"])
+@pytest.mark.parametrize("heads", [(16, 4), (16, 1), (8, 8), (16, 8), (64, 8)],
+                         ids=["G4", "G16", "G1", "G2", "G8"])
 @pytest.mark.parametrize("split", [64, 16], ids=["direct_merge", "looped_merge"])
 def test_two_launch_step_equals_three_launches(kv, heads, split):
     hq, hkv = heads
@@ -143,6 +144,27 @@ def test_two_launch_step_equals_three_launches(kv, heads, split):
     assert np.all(out[8] == 0.0)
     ok = [i for i in range(w.batch) if not flags[i] and i != 8]
     assert ok and np.all(np.isfinite(out[ok])), "a standing request has non-finite output"
+
+
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+def test_two_launch_step_page32(kv):
+    """Page 32, 128-token splits (four pages a split), the same edits."""
+    w = W.custom("step_p32", 3170, LENS, hq=64, hkv=8, dk=128, dv=128, page=32, per_head=True,
+                 n_realloc=2)
+
+    def edit(st):
+        e = st.expected.view(torch.int32)
+        e[9, 0] ^= 1
+        st.block_table[10, 6] = st.w.num_pages + 7
+        e[11, (int(st.seq_lens[11]) - 1) // 32] ^= 1
+        st.seq_lens[8] = 0
+
+    a, b = _prepare(w, kv, 128, edit=edit)
+    assert pkv.pkv_step_launches(b.cache, 64, 128) == 2
+    flags, out = _run_both_and_compare(a, b)
+    want = ostep.flags(w).astype(np.uint8)
+    want[8], want[9], want[10], want[11] = 0, 1, 1, 1
+    assert np.array_equal(flags, want), (flags, want)
 
 
 @pytest.mark.parametrize("kv", ["fp8", "bf16"])
