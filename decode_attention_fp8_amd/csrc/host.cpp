@@ -56,8 +56,13 @@ extern "C" int32_t pkv_suggest_split(const pkv_cache* cache, int32_t num_q_heads
     // 2048 against 0.119 at 512, batch 32 0.215 at 2048 against 0.221 at
     // 1024, batch 8 0.065 at 1024 and 0.063 at 512 against 0.067 at 256,
     // batch 1 best at 128 (0.0192, against 0.0199 at 64 and 0.0202 at 256).
+    // Splits of 128 tokens are kept for launches that 256-token ones would
+    // leave with fewer than 1024 units (four per CU): at 32 KB a unit's start
+    // and its partial row cost more than the extra waves gain (batch 8 x
+    // 4096: 0.0253 ms per step at 256, 1064 units, against 0.0279 at 128).
     s = std::min<int64_t>(2048, 128 * P);
     while (s > 128 && units(s, cache->num_kv_heads) < 1100) s /= 2;
+    if (s == 128 && 128 * P >= 256 && units(256, cache->num_kv_heads) >= 1024) s = 256;
   } else {
     constexpr int64_t kTargetUnits = 16384;
     const int64_t work = static_cast<int64_t>(batch) * cache->num_kv_heads * max_seq_len;

@@ -53,6 +53,8 @@ def test_host_helpers():
     assert pkv.pkv_suggest_split(gqa_bf16, 64, 64, 64 * 17000, 32768) == 2048
     assert pkv.pkv_suggest_split(gqa, 64, 8, 8 * 17000, 32768) == 512
     assert pkv.pkv_suggest_split(gqa, 64, 1, 17000, 17000) == 128
+    # batch 8 x 4096: 256-token splits still give 1064 units, so not 128
+    assert pkv.pkv_suggest_split(gqa, 64, 8, 8 * 4096, 4096) == 256
     # never longer than the longest request (rounded up to whole pages)
     assert pkv.pkv_suggest_split(gqa, 64, 1, 10, 10) == 16
     lat = pkv.Cache(torch.empty((1, 1, 64, 576), dtype=torch.uint8), None, latent_dim_v=512)
