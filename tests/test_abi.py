@@ -59,7 +59,7 @@ def test_host_helpers():
     assert pkv.pkv_suggest_split(gqa, 64, 1, 10, 10) == 16
     lat = pkv.Cache(torch.empty((1, 1, 64, 576), dtype=torch.uint8), None, latent_dim_v=512)
     # latent: about an eighth of an equal per-compute-unit share of the pages
-    assert pkv.pkv_suggest_split(lat, 128, 64, 907520, 65536) == 256
+    assert pkv.pkv_suggest_split(lat, 128, 64, 907520, 65536) == 128
     assert pkv.pkv_suggest_split(lat, 128, 1, 8192, 8192) == 64
     for s in (pkv.pkv_suggest_split(gqa, 64, 3, 0, 5000), pkv.pkv_suggest_split(lat, 128, 3, 0, 5000)):
         assert s > 0 and s % 16 == 0
